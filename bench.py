@@ -1,0 +1,249 @@
+"""Benchmark: draft + verify cycles/s and tokens/s of the one-pass block-
+diffusion drafter on one MI355X.
+
+A step is one full cycle (inject_kv -> block_draft -> lm_head_argmax ->
+verify) over the batch of the workload, on synthetic inputs already resident
+in HBM.  Default workload: the 8B-shaped drafter (5 layers, hidden 4096,
+32/8 heads x 128, MLP 12288, vocabulary 151936) at batch 32 with ragged
+contexts U[1024, 8192], block 16, temperature-1 rejection-sampling verify
+with bf16 target logits N(0, 3) and Philox uniforms.
+
+Prints ONE JSON line (see the keys at the end of main()).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def _algorithmic(cfg, rows, n_inj):
+    """Algorithmic bytes / flops of each library call for one cycle (weights
+    and context K/V read once, activations, logits only where stored)."""
+    d, V, L = cfg["hidden"], cfg["vocab"], cfg["n_layers"]
+    hq, hkv, dh, m = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["mlp"]
+    F = cfg["feat_dim"]
+    eb = 2 if cfg["dtype"] == "bf16" else 4
+    bs, C, B, g = cfg["bs"], cfg["n_copies"], cfg["block"], cfg["gamma"]
+    R = bs * C * B
+    layer_params = (hq + 2 * hkv) * dh * d + d * hq * dh + 2 * m * d + d * m
+    ctx = cfg["ctx_lens"]
+    attn_bytes = L * sum((S + B * C) * hkv * dh * 2 * eb for S in ctx)
+    attn_flops = L * sum(C * 4 * B * hq * dh * (S + B) for S in ctx)
+    head_logits = 4 * rows * V if cfg["verify"] == "rs" else 0
+    head_bytes = eb * V * d + rows * (eb * d + 16) + head_logits
+    head_flops = 2 * rows * V * d
+    inj_params = d * F + 2 * hkv * dh * d * L
+    inj_bytes = eb * inj_params + n_inj * (F * eb + L * 2 * hkv * dh * eb)
+    inj_flops = 2 * n_inj * inj_params
+    tsz = 2 if cfg.get("target_dtype") == "bf16" else 4
+    ver_bytes = bs * (g + 1) * V * tsz + (bs * V * 4 if cfg["verify"] == "rs" else 0)
+    if cfg["verify"] == "none":
+        ver_bytes = 0
+    draft_bytes = eb * L * layer_params + attn_bytes
+    draft_flops = 2 * R * L * layer_params + attn_flops
+    return dict(
+        inject=dict(bytes=inj_bytes, flops=inj_flops),
+        draft=dict(bytes=draft_bytes, flops=draft_flops, attn_bytes=attn_bytes,
+                   attn_flops=attn_flops, gemm_bytes=eb * L * layer_params,
+                   gemm_flops=2 * R * L * layer_params),
+        head=dict(bytes=head_bytes, flops=head_flops),
+        verify=dict(bytes=ver_bytes, flops=0),
+    )
+
+
+def _cpu_baseline(cfg, cyc, budget_s):
+    """Time the CPU oracle on a bounded sample of the same workload: whole
+    cycles for as many sequences as fit in ~budget_s, scaled to the batch."""
+    import numpy as np
+
+    from oracle.drafter import Drafter as OracleDrafter, lm_head
+    from oracle import philox
+    from oracle.verify import verify_batch
+
+    def host(t):
+        return t.detach().cpu().double().numpy()
+
+    w = {k: (host(v) if not isinstance(v, list) else
+             [{a: host(b) for a, b in l.items()} for l in v]) for k, v in cyc.w.items()}
+    od = OracleDrafter(cfg, w)
+    feats = host(cyc.feats)
+    tokens = cyc.tokens.cpu().numpy()
+    target = host(cyc.target) if cyc.verify_mode is not None else None
+    n_new, g, V = cyc.n_new, cfg["gamma"], cfg["vocab"]
+    T = float(cfg.get("temperature", 1.0))
+    done, t_total = 0, 0.0
+    for b, S in enumerate(cfg["ctx_lens"]):
+        ck = [host(k[b]) for k in cyc.kv.k]
+        cv = [host(v[b]) for v in cyc.kv.v]
+        t0 = time.perf_counter()
+        ks, vs = od.inject_rows(feats[b * n_new:(b + 1) * n_new], np.arange(S - n_new, S))
+        for l in range(cfg["n_layers"]):
+            ck[l][:, S - n_new:S] = ks[l].transpose(1, 0, 2)
+            cv[l][:, S - n_new:S] = vs[l].transpose(1, 0, 2)
+        hid = od.draft(ck, cv, tokens[b], S)
+        if cyc.mode == 0:
+            out = lm_head(w["lm_head"], hid[0, 1:], keep_logits=True)
+        else:
+            gm = np.stack([philox.gumbel_row(cyc.seed, 0, b, k, 0, V) for k in range(g)])
+            out = lm_head(w["lm_head"], hid[0, 1:], temperature=T, gumbel=gm, keep_logits=True)
+        if target is not None:
+            mode = "rs" if cfg["verify"] == "rs" else "greedy"
+            verify_batch(mode, target[b:b + 1], out["ids"][None, :],
+                         zd=out["logits"][None, :], temperature=T, seed=cyc.seed, cycle=0)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    per_seq = t_total / done
+    cycles_per_s = 1.0 / (per_seq * cfg["bs"])
+    return dict(value=cycles_per_s, unit="cycles/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle",
+                sample=f"{done} of {cfg['bs']} sequences, one full cycle each "
+                       f"({t_total:.1f} s), scaled linearly to the batch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="q8b_bs32_rs")
+    ap.add_argument("--n-new", type=int, default=8)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path shards "
+              "over sequences with no per-cycle exchange, and multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_speculative_kv_amd import _lib
+    from block_diffusion_speculative_kv_amd.cycle import Cycle
+    from synth import configs
+
+    _lib.load()
+    cfg = configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {args.workload}: setting up (weights, prefill inject)", file=sys.stderr,
+          flush=True)
+    cyc = Cycle(cfg, device=dev, n_new=args.n_new)
+    st = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        cyc.step(cycle=i)
+    torch.cuda.synchronize()
+
+    # whole-cycle timing
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    taus = []
+    ev0.record(st)
+    for i in range(args.steps):
+        cyc.step(cycle=args.warmup + i)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    if cyc.verify_mode is not None:
+        taus = cyc.tau.cpu().numpy().tolist()
+
+    # per-call timing (same stream, events around each library call)
+    names = ["inject", "draft", "head", "verify"]
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for n in names}
+    tau_hist = []
+    for i in range(args.steps):
+        c = args.warmup + args.steps + i
+        for n, fn in (("inject", cyc.inject), ("draft", cyc.draft),
+                      ("head", lambda: cyc.head(c)), ("verify", lambda: cyc.verify(c))):
+            evs[n][i][0].record(st)
+            fn()
+            evs[n][i][1].record(st)
+        if cyc.verify_mode is not None and i < 8:
+            tau_hist.append(cyc.tau.clone())
+    torch.cuda.synchronize()
+    per_call = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) for n in names}
+    if tau_hist:
+        taus = torch.cat(tau_hist).cpu().numpy().tolist()
+    tau_mean = float(np.mean(taus)) if taus else None
+
+    n_inj = cfg["bs"] * cyc.n_new
+    alg = _algorithmic(cfg, cyc.rows, n_inj)
+    cycles_per_s = 1000.0 / ms_step
+    bs = cfg["bs"]
+    tokens_per_s = cycles_per_s * bs * tau_mean if tau_mean else None
+    total_bytes = sum(v["bytes"] for v in alg.values())
+    hbm_gbs = total_bytes / (ms_step * 1e-3) / 1e9
+
+    # roofline of the LM-head call (one main kernel plus a small merge)
+    head_s = per_call["head"] * 1e-3
+    head_bound = "mfma" if alg["head"]["flops"] / alg["head"]["bytes"] > \
+        MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    if head_bound == "mfma":
+        ach = alg["head"]["flops"] / head_s / 1e12
+        roof = dict(kernel="lm_head_kernel (+lm_combine)", bound="mfma", achieved=round(ach, 2),
+                    peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    traffic=None, avg_us=round(per_call["head"] * 1e3, 2))
+    else:
+        ach = alg["head"]["bytes"] / head_s / 1e9
+        roof = dict(kernel="lm_head_kernel (+lm_combine)", bound="hbm", achieved=round(ach, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                    traffic=None, avg_us=round(per_call["head"] * 1e3, 2))
+
+    stages = {}
+    for n in names:
+        t = per_call[n] * 1e-3
+        b, f = alg[n]["bytes"], alg[n]["flops"]
+        stages[n] = dict(ms=round(per_call[n], 4), gbs=round(b / t / 1e9, 1) if t else None,
+                         tflops=round(f / t / 1e12, 2) if t else None)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(cfg, cyc, args.cpu_budget)
+
+    out = {
+        "metric": "draft+verify cycles/s (bs=32, 8B-shaped drafter)",
+        "value": round(cycles_per_s, 3),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bs, "block": cfg["block"],
+                   "gamma": cfg["gamma"], "ctx": cfg["ctx"] if isinstance(cfg["ctx"], str)
+                   else cfg["ctx_lens"], "verify": cfg["verify"], "head": cfg["lm_mode"],
+                   "n_new_per_cycle": cyc.n_new},
+        "tokens_per_s": round(tokens_per_s, 1) if tokens_per_s else None,
+        "tau_mean": tau_mean,
+        "hbm_gbs": round(hbm_gbs, 1),
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+// Dense projections on the matrix cores: out[split][m][n] = sum over the
+// split's k-range of X[m][k] * W[n][k].  W is a weight in [out, in] layout, X
+// an activation block; both are k-contiguous, so each MFMA operand fragment
+// is one 16-byte load per lane straight from global memory.  The weight is
+// the MFMA A operand (16 output features per tile) and the activation rows
+// the B operand, so a lane ends up with 4 consecutive output features of one
+// row and stores them as one 16-byte vector.  Partial sums over k-splits are
+// summed in a fixed order by the consumer (the fused epilogue kernels), which
+// keeps results deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dstill {
+
+template <typename T, int NTW, int MTW>
+__global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, long ldx,
+                                                       const T *__restrict__ W, long ldw,
+                                                       float *__restrict__ out, int M, int N,
+                                                       int nks, int ks_per_split) {
+  typedef typename Mma<T>::frag F;
+  constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int nbase = (blockIdx.x * 4 + wave) * (NTW * 16);
+  const int mbase = blockIdx.y * (MTW * 16);
+  if (nbase >= N) return;
+  const int ks0 = blockIdx.z * ks_per_split;
+  const int ks1 = min(ks0 + ks_per_split, nks);
+
+  const T *wp[NTW];
+  const T *xp[MTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int n = min(nbase + 16 * t + r16, N - 1);
+    wp[t] = W + (long)n * ldw + g * VEC + (long)ks0 * KW;
+  }
+#pragma unroll
+  for (int t = 0; t < MTW; ++t) {
+    const int m = min(mbase + 16 * t + r16, M - 1);
+    xp[t] = X + (long)m * ldx + g * VEC + (long)ks0 * KW;
+  }
+
+  f32x4 acc[NTW][MTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  F a[NTW], b[MTW];
+  if (ks0 < ks1) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) a[t] = load_frag<T>(wp[t]);
+#pragma unroll
+    for (int t = 0; t < MTW; ++t) b[t] = load_frag<T>(xp[t]);
+  }
+  for (int ks = ks0; ks < ks1; ++ks) {
+    F an[NTW], bn[MTW];
+    const long off = (long)(ks + 1 - ks0) * KW;
+    if (ks + 1 < ks1) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) an[t] = load_frag<T>(wp[t] + off);
+#pragma unroll
+      for (int t = 0; t < MTW; ++t) bn[t] = load_frag<T>(xp[t] + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) acc[i][j] = Mma<T>::run(a[i], b[j], acc[i][j]);
+    if (ks + 1 < ks1) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) a[t] = an[t];
+#pragma unroll
+      for (int t = 0; t < MTW; ++t) b[t] = bn[t];
+    }
+  }
+
+  float *o = out + (long)blockIdx.z * M * N;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int n = nbase + 16 * i + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const int m = mbase + 16 * j + r16;
+      if (m < M) *reinterpret_cast<f32x4 *>(o + (long)m * N + n) = acc[i][j];
+    }
+  }
+}
+
+// Host-side plan: wave tile of NTW x MTW 16x16 tiles, 4 waves along N, and a
+// k-split that gives the launch at least ~2 workgroups per compute unit.
+template <typename T, int NTW, int MTW>
+static void launch_tile(const GemmArgs &a, hipStream_t st) {
+  constexpr int KW = Mma<T>::KW;
+  const int nks = a.K / KW;
+  const int bn = 4 * NTW * 16, bm = MTW * 16;
+  const int tiles_n = (a.N + bn - 1) / bn, tiles_m = (a.M + bm - 1) / bm;
+  const int splits = a.splits;
+  const int per = (nks + splits - 1) / splits;
+  dim3 grid(tiles_n, tiles_m, splits);
+  hipLaunchKernelGGL((gemm_nt_partial<T, NTW, MTW>), grid, dim3(256), 0, st,
+                     (const T *)a.X, a.ldx, (const T *)a.W, a.ldw, a.out, a.M, a.N, nks, per);
+}
+
+// Chooses the wave tile from M and the number of k-splits; returns the split
+// count the output buffer must hold.
+int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
+  const int KW = dtype == 1 ? 32 : 16;
+  const int nks = K / KW;
+  int ntw, mtw;
+  gemm_pick_tile(M, &ntw, &mtw);
+  const int bn = 4 * ntw * 16, bm = mtw * 16;
+  const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+  const long target = 2L * num_cu;
+  int splits = (int)((target + tiles - 1) / tiles);
+  // at least 8 k-steps per split, so each wave keeps enough loads in flight
+  splits = max(1, min(splits, nks / 8));
+  const int per = (nks + splits - 1) / splits;
+  splits = (nks + per - 1) / per;  // no empty split
+  return splits;
+}
+
+void gemm_pick_tile(int M, int *ntw, int *mtw) {
+  if (M <= 16) { *ntw = 2; *mtw = 1; }
+  else if (M <= 32) { *ntw = 2; *mtw = 2; }
+  else if (M <= 48) { *ntw = 2; *mtw = 3; }
+  else if (M <= 64) { *ntw = 2; *mtw = 4; }
+  else { *ntw = 4; *mtw = 4; }
+}
+
+template <typename T>
+static void launch_typed(const GemmArgs &a, hipStream_t st) {
+  int ntw, mtw;
+  gemm_pick_tile(a.M, &ntw, &mtw);
+  if (ntw == 2 && mtw == 1) launch_tile<T, 2, 1>(a, st);
+  else if (ntw == 2 && mtw == 2) launch_tile<T, 2, 2>(a, st);
+  else if (ntw == 2 && mtw == 3) launch_tile<T, 2, 3>(a, st);
+  else if (ntw == 2 && mtw == 4) launch_tile<T, 2, 4>(a, st);
+  else launch_tile<T, 4, 4>(a, st);
+}
+
+void launch_gemm(const GemmArgs &a, hipStream_t st) {
+  if (a.dtype == 1) launch_typed<bf16>(a, st);
+  else launch_typed<float>(a, st);
+}
+
+}  // namespace dstill

@@ -1,0 +1,105 @@
+// Internal launch interface between the host dispatcher (api.cpp) and the
+// kernels.  Every launcher only enqueues work on the given stream; argument
+// validation happens before any of them is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dstill {
+
+// ---- dense projections (gemm.hip) -----------------------------------------
+struct GemmArgs {
+  const void *X;  // [M, K] activations, row stride ldx (elements)
+  long ldx;
+  const void *W;  // [N, K] weight rows, row stride ldw (elements)
+  long ldw;
+  float *out;     // [splits][M][N] fp32 partial sums
+  int M, N, K, splits, dtype;
+};
+void gemm_pick_tile(int M, int *ntw, int *mtw);
+int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu);
+void launch_gemm(const GemmArgs &a, hipStream_t st);
+
+// ---- per-row and element-wise stages (layer_ops.hip) ------------------------
+void launch_draft_prep(const int32_t *tokens, const int32_t *ctx_len, int bs, int per_seq,
+                       int vocab, int ctx_limit, int32_t *eff_ctx, int32_t *tok_clamped,
+                       uint32_t *flags, hipStream_t st);
+void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d, float *h,
+                  hipStream_t st);
+// out = RMSNorm(x) * gain with x = sum of `nsplit` partial planes (+ resid);
+// the new residual is written back when write_resid is set.
+void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
+                      int write_resid, const void *gain, float eps, void *out, long out_stride,
+                      hipStream_t st);
+void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, int hkv, int dh,
+                     const int32_t *eff_ctx, int rows_per_seq, int block, const void *q_norm,
+                     const void *k_norm, int qk_norm, float eps, float theta, void *q, void *kb,
+                     void *vb, hipStream_t st);
+void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, void *act,
+                   hipStream_t st);
+void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
+                        const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
+                        float eps, float theta, void *kc, void *vc, int max_batch, int cap,
+                        hipStream_t st);
+
+// ---- block attention over injected context (attn.hip) --------------------
+struct AttnArgs {
+  int dtype;
+  const void *q;       // [bs*C*B, hq*dh]
+  const void *kb;      // [bs*C*B, hkv*dh] block keys
+  const void *vb;      // [bs*C*B, hkv*dh] block values
+  const void *kc;      // cache K of this layer [max_batch][hkv][cap][dh]
+  const void *vc;
+  const int32_t *eff_ctx;  // [bs] clamped context lengths
+  int bs, C, B, hq, hkv, dh, cap;
+  int split;           // context keys per split (multiple of 64)
+  int nsplit;          // splits planned for the longest context
+  float scale;         // 1/sqrt(dh)
+  float *opart;        // [bs*C][hq][nsplit][B][dh]
+  float *mlpart;       // [bs*C][hq][nsplit][B][2]  (running max in log2 units, sum)
+  void *out;           // [bs*C*B, hq*dh]
+};
+void launch_attention(const AttnArgs &a, hipStream_t st);
+
+// ---- LM head with fused vocabulary reduction (lm_head.hip) -----------------
+struct HeadPartial {
+  float best, second, zbest, zmax, m, s;  // m: max z/T in block, s: sum exp(z/T - m)
+  int idx, pad;
+};
+struct HeadArgs {
+  int dtype;
+  const void *hidden;
+  int rows, rows_per_seq, seq_stride, d, vocab;
+  const void *w;       // [vocab, d]
+  int mode;
+  float temperature;
+  uint64_t seed, cycle;
+  HeadPartial *part;   // [rows][nvb]
+  int nvb;             // vocabulary blocks
+  float *logits;       // optional [rows][vocab]
+  int32_t *ids;
+  float *zmax, *lse, *zsel, *gap;
+};
+int head_vocab_block();
+void launch_lm_head(const HeadArgs &a, hipStream_t st);
+
+// ---- verification (verify.hip) ------------------------------------------
+struct VerifyArgs {
+  int mode, bs, gamma, vocab, tdtype;
+  float temperature;
+  uint64_t seed, cycle;
+  const int32_t *draft_ids;
+  const float *draft_lse;
+  const float *draft_logits;
+  const void *target;
+  int32_t *tokens, *tau;
+  uint32_t *flags;
+  void *ws;
+  int nsplit;          // vocabulary splits per row
+};
+int verify_plan_splits(int vocab);
+size_t verify_ws_bytes(int bs, int gamma, int nsplit);
+void launch_verify(const VerifyArgs &a, hipStream_t st);
+
+}  // namespace dstill

@@ -1,0 +1,307 @@
+// Per-row and element-wise stages of the drafter, each fused onto the output
+// of a projection: summing the k-split partial planes, RMSNorm with its gain,
+// per-head q/k RMSNorm with the rotary embedding, the SwiGLU gate, and the
+// scatter of injected K/V into the cache.
+//
+// Readings of the drafter (DStill appendix drafter table: "Qwen3-style"
+// layers; DFlash review, Method / Inference for the injection):
+//   RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g, in fp32;
+//   rotary embedding on q and k: the pair (i, i + dh/2) turns by the angle
+//   pos * theta^(-2i/dh), computed in fp64 so that positions up to 2^20 keep
+//   full fp32 accuracy;
+//   SwiGLU: silu(gate) * up, silu(x) = x / (1 + exp(-x)).
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dstill {
+
+// ---- context clamp, token check ----------------------------------------------
+__global__ __launch_bounds__(64) void draft_prep_kernel(const int32_t *__restrict__ tokens,
+                                                        const int32_t *__restrict__ ctx_len,
+                                                        int per_seq, int vocab, int ctx_limit,
+                                                        int32_t *__restrict__ eff_ctx,
+                                                        int32_t *__restrict__ tok_clamped,
+                                                        uint32_t *__restrict__ flags) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  uint32_t f = 0;
+  for (int i = lane; i < per_seq; i += WAVE) {
+    int t = tokens[(long)b * per_seq + i];
+    if (t < 0 || t >= vocab) {
+      f |= 16u;  // DSTILL_FLAG_BAD_INPUT
+      t = t < 0 ? 0 : vocab - 1;
+    }
+    tok_clamped[(long)b * per_seq + i] = t;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, WAVE);
+  if (lane == 0) {
+    int c = ctx_len[b];
+    if (c < 0 || c > ctx_limit) {
+      f |= 32u;  // DSTILL_FLAG_CTX_CLAMPED
+      c = c < 0 ? 0 : ctx_limit;
+    }
+    eff_ctx[b] = c;
+    if (flags) flags[b] = f;
+  }
+}
+
+void launch_draft_prep(const int32_t *tokens, const int32_t *ctx_len, int bs, int per_seq,
+                       int vocab, int ctx_limit, int32_t *eff_ctx, int32_t *tok_clamped,
+                       uint32_t *flags, hipStream_t st) {
+  hipLaunchKernelGGL(draft_prep_kernel, dim3(bs), dim3(64), 0, st, tokens, ctx_len, per_seq, vocab,
+                     ctx_limit, eff_ctx, tok_clamped, flags);
+}
+
+// ---- embedding gather into the fp32 residual stream --------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T *__restrict__ embed,
+                                                    const int32_t *__restrict__ tok, int d,
+                                                    float *__restrict__ h) {
+  const int r = blockIdx.x;
+  const T *src = embed + (long)tok[r] * d;
+  float *dst = h + (long)r * d;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) dst[j] = to_f32(src[j]);
+}
+
+void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d, float *h,
+                  hipStream_t st) {
+  if (R == 0) return;
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(R), dim3(256), 0, st, (const bf16 *)embed, tok, d, h);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(R), dim3(256), 0, st, (const float *)embed, tok, d, h);
+}
+
+// ---- RMSNorm over rows, fused with the split-sum and the residual add --------
+constexpr int NORM_MAX_PER_THREAD = 32;  // hidden <= 8192 with 256 threads
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_rows_kernel(const float *__restrict__ parts,
+                                                        int nsplit, int M, int d,
+                                                        float *__restrict__ resid,
+                                                        int write_resid,
+                                                        const T *__restrict__ gain, float eps,
+                                                        T *__restrict__ out, long out_stride) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  float x[NORM_MAX_PER_THREAD];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NORM_MAX_PER_THREAD; ++i) {
+    const int j = threadIdx.x + i * 256;
+    float v = 0.f;
+    if (j < d) {
+      for (int s = 0; s < nsplit; ++s) v += parts[((long)s * M + r) * d + j];
+      if (resid) {
+        v += resid[(long)r * d + j];
+        if (write_resid) resid[(long)r * d + j] = v;
+      }
+    }
+    x[i] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < NORM_MAX_PER_THREAD; ++i) {
+    const int j = threadIdx.x + i * 256;
+    if (j < d) out[(long)r * out_stride + j] = from_f32<T>(x[i] * rs * to_f32(gain[j]));
+  }
+}
+
+void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
+                      int write_resid, const void *gain, float eps, void *out, long out_stride,
+                      hipStream_t st) {
+  if (M == 0) return;
+  if (dtype == 1)
+    hipLaunchKernelGGL(norm_rows_kernel<bf16>, dim3(M), dim3(256), 0, st, parts, nsplit, M, d,
+                       resid, write_resid, (const bf16 *)gain, eps, (bf16 *)out, out_stride);
+  else
+    hipLaunchKernelGGL(norm_rows_kernel<float>, dim3(M), dim3(256), 0, st, parts, nsplit, M, d,
+                       resid, write_resid, (const float *)gain, eps, (float *)out, out_stride);
+}
+
+// ---- per-head RMSNorm + rotary embedding -------------------------------------
+// One wave handles one (row, head); lane p owns the rotary pairs
+// (p, p + dh/2) and (p + 64, p + 64 + dh/2) (dh <= 256).
+__device__ __forceinline__ void rope_pair(float &x1, float &x2, int p, int dh, int pos,
+                                          float theta) {
+  const double inv = exp(-2.0 * (double)p / (double)dh * log((double)theta));
+  double sn, cs;
+  sincos((double)pos * inv, &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  const float y1 = x1 * c - x2 * s;
+  const float y2 = x2 * c + x1 * s;
+  x1 = y1;
+  x2 = y2;
+}
+
+template <typename T>
+__device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh, bool norm,
+                                               const T *g, float eps, bool rope, int pos,
+                                               float theta) {
+  const int lane = threadIdx.x & 63, half = dh / 2;
+  if (norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)dh + eps);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = lane + 64 * i;
+      if (p < half) {
+        x1[i] = x1[i] * rs * to_f32(g[p]);
+        x2[i] = x2[i] * rs * to_f32(g[p + half]);
+      }
+    }
+  }
+  if (rope) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = lane + 64 * i;
+      if (p < half) rope_pair(x1[i], x2[i], p, dh, pos, theta);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void qkv_post_kernel(
+    const float *__restrict__ parts, int nsplit, int R, int hq, int hkv, int dh,
+    const int32_t *__restrict__ eff_ctx, int rows_per_seq, int block,
+    const T *__restrict__ q_norm, const T *__restrict__ k_norm, int qk_norm, float eps,
+    float theta, T *__restrict__ q, T *__restrict__ kb, T *__restrict__ vb) {
+  const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
+  const int half = dh / 2, ncol = (hq + 2 * hkv) * dh;
+  const int pos = eff_ctx[r / rows_per_seq] + r % block;
+  const bool is_q = head < hq, is_k = !is_q && head < hq + hkv;
+  float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) {
+      const float *src = parts + (long)r * ncol + head * dh + p;
+      for (int s = 0; s < nsplit; ++s) {
+        x1[i] += src[(long)s * R * ncol];
+        x2[i] += src[(long)s * R * ncol + half];
+      }
+    }
+  }
+  T *dst;
+  if (is_q) dst = q + (long)r * hq * dh + head * dh;
+  else if (is_k) dst = kb + (long)r * hkv * dh + (head - hq) * dh;
+  else dst = vb + (long)r * hkv * dh + (head - hq - hkv) * dh;
+  if (is_q || is_k)
+    head_norm_rope<T>(x1, x2, dh, qk_norm != 0, is_q ? q_norm : k_norm, eps, true, pos, theta);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) {
+      dst[p] = from_f32<T>(x1[i]);
+      dst[p + half] = from_f32<T>(x2[i]);
+    }
+  }
+}
+
+void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, int hkv, int dh,
+                     const int32_t *eff_ctx, int rows_per_seq, int block, const void *q_norm,
+                     const void *k_norm, int qk_norm, float eps, float theta, void *q, void *kb,
+                     void *vb, hipStream_t st) {
+  if (R == 0) return;
+  dim3 grid(R, hq + 2 * hkv);
+  if (dtype == 1)
+    hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
+                       eff_ctx, rows_per_seq, block, (const bf16 *)q_norm, (const bf16 *)k_norm,
+                       qk_norm, eps, theta, (bf16 *)q, (bf16 *)kb, (bf16 *)vb);
+  else
+    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
+                       eff_ctx, rows_per_seq, block, (const float *)q_norm, (const float *)k_norm,
+                       qk_norm, eps, theta, (float *)q, (float *)kb, (float *)vb);
+}
+
+// ---- SwiGLU gate ------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const float *__restrict__ parts, int nsplit,
+                                                     int R, int mlp, T *__restrict__ act) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)R * mlp) return;
+  const long r = i / mlp, j = i % mlp;
+  const long plane = (long)R * 2 * mlp;
+  float g = 0.f, u = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    g += parts[s * plane + r * 2 * mlp + j];
+    u += parts[s * plane + r * 2 * mlp + mlp + j];
+  }
+  const float silu = g / (1.0f + expf(-g));
+  act[i] = from_f32<T>(silu * u);
+}
+
+void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, void *act,
+                   hipStream_t st) {
+  const long n = (long)R * mlp;
+  if (n == 0) return;
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(swiglu_kernel<bf16>, dim3(blocks), dim3(256), 0, st, parts, nsplit, R, mlp,
+                       (bf16 *)act);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<float>, dim3(blocks), dim3(256), 0, st, parts, nsplit, R, mlp,
+                       (float *)act);
+}
+
+// ---- injected K/V: k-norm + rotary embedding, scatter into the cache --------
+template <typename T>
+__global__ __launch_bounds__(64) void inject_post_kernel(
+    const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
+    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos,
+    const T *__restrict__ k_norm, int qk_norm, float eps, float theta, T *__restrict__ kc,
+    T *__restrict__ vc, int max_batch, int cap) {
+  const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
+  const int sq = seq[r], ps = pos[r];
+  if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
+  const int half = dh / 2, ncol = 2 * hkv * dh;
+  const bool is_k = head < hkv;
+  const int h = is_k ? head : head - hkv;
+  float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) {
+      const float *src = parts + (long)r * ncol + head * dh + p;
+      for (int s = 0; s < nsplit; ++s) {
+        x1[i] += src[(long)s * n * ncol];
+        x2[i] += src[(long)s * n * ncol + half];
+      }
+    }
+  }
+  if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, true, ps, theta);
+  T *dst = (is_k ? kc : vc) + (((long)sq * hkv + h) * cap + ps) * dh;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) {
+      dst[p] = from_f32<T>(x1[i]);
+      dst[p + half] = from_f32<T>(x2[i]);
+    }
+  }
+}
+
+void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
+                        const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
+                        float eps, float theta, void *kc, void *vc, int max_batch, int cap,
+                        hipStream_t st) {
+  if (n == 0) return;
+  dim3 grid(n, 2 * hkv);
+  if (dtype == 1)
+    hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
+                       seq, pos, (const bf16 *)k_norm, qk_norm, eps, theta, (bf16 *)kc,
+                       (bf16 *)vc, max_batch, cap);
+  else
+    hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
+                       seq, pos, (const float *)k_norm, qk_norm, eps, theta, (float *)kc,
+                       (float *)vc, max_batch, cap);
+}
+
+}  // namespace dstill

@@ -1,0 +1,304 @@
+// Shared LM head with a fused vocabulary-wide reduction (DStill, Experimental
+// Setup and DFlash review, Training: the drafter reuses the target's frozen
+// LM head; DStill, Inference: greedy top-1 or a sampled proposal per
+// position; SPOT, Method: one Gumbel table shared per block slot).
+//
+// z = hidden . W^T is computed tile by tile on the matrix cores and reduced
+// on the spot: per row and vocabulary block the kernel keeps the best score
+// (z, or z/T + g for Gumbel-max sampling), its id (lowest id on ties), the
+// runner-up score, z at the best id, max z, and the softmax mass at
+// temperature T relative to the block's max.  The logits themselves are
+// written only when the caller asks for them (rejection sampling needs the
+// draft rows).  A second kernel merges the per-block records of each row in
+// a fixed order, so results are deterministic.
+//
+// Layout: the weight is the MFMA A operand (16 vocabulary rows per tile) and
+// the hidden rows the B operand.  Vocabulary rows inside each pair of tiles
+// are permuted so that lane group g of a wave holds the 8 consecutive ids
+// 8g .. 8g+7 of a 32-id span: exactly one Philox4x64-10 block.
+//
+// Launch: the row blocks of one vocabulary block are placed on the same XCD
+// (workgroup i runs on XCD i mod 8) and next to each other in dispatch order,
+// so when there are several row blocks they read the weight tile through the
+// same L2 at about the same time instead of fetching it again from HBM.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dstill {
+
+constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup (64 per wave)
+constexpr int NXCD = 8;
+
+int head_vocab_block() { return HEAD_VB; }
+
+struct RowStat {
+  ArgTop2 arg;
+  float zbest, zmax, m, s;
+};
+
+__device__ __forceinline__ void ms_merge(float &m, float &s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) { m = m2; s = s2; return; }
+  const float M = fmaxf(m, m2);
+  s = s * expf(m - M) + s2 * expf(m2 - M);
+  m = M;
+}
+
+__device__ __forceinline__ RowStat rowstat_merge(RowStat a, const RowStat &b) {
+  const bool bw = b.arg.best > a.arg.best || (b.arg.best == a.arg.best && b.arg.idx < a.arg.idx);
+  const float zb = bw ? b.zbest : a.zbest;
+  a.arg = top2_merge(a.arg, b.arg);
+  a.zbest = zb;
+  a.zmax = fmaxf(a.zmax, b.zmax);
+  ms_merge(a.m, a.s, b.m, b.s);
+  return a;
+}
+
+__device__ __forceinline__ RowStat rowstat_shfl_xor(const RowStat &a, int o) {
+  RowStat b;
+  b.arg.best = __shfl_xor(a.arg.best, o, WAVE);
+  b.arg.second = __shfl_xor(a.arg.second, o, WAVE);
+  b.arg.idx = __shfl_xor(a.arg.idx, o, WAVE);
+  b.zbest = __shfl_xor(a.zbest, o, WAVE);
+  b.zmax = __shfl_xor(a.zmax, o, WAVE);
+  b.m = __shfl_xor(a.m, o, WAVE);
+  b.s = __shfl_xor(a.s, o, WAVE);
+  return rowstat_merge(a, b);
+}
+
+template <typename T, int MTW>
+__global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
+  typedef typename Mma<T>::frag F;
+  constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
+  __shared__ RowStat red[4][MTW * 16];
+
+  // XCD-aware mapping of the linear workgroup id to (vocab block, row block).
+  const int L = blockIdx.x;
+  const int xcd = L % NXCD, slot = L / NXCD;
+  const int vb = (slot / nrb) * NXCD + xcd, rb = slot % nrb;
+  if (vb >= a.nvb) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int vw = vb * HEAD_VB + wave * 64;
+  const int rbase = rb * MTW * 16;
+  const int V = a.vocab, d = a.d;
+
+  const T *wp[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int v = vw + 32 * (t >> 1) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3);
+    wp[t] = (const T *)a.w + (long)min(v, V - 1) * d + g * VEC;
+  }
+  const T *xp[MTW];
+#pragma unroll
+  for (int t = 0; t < MTW; ++t) {
+    const int r = min(rbase + 16 * t + r16, a.rows - 1);
+    const long hrow = (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq;
+    xp[t] = (const T *)a.hidden + hrow * d + g * VEC;
+  }
+
+  f32x4 acc[4][MTW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = d / KW;
+  F fa[4], fb[MTW];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fa[t] = load_frag<T>(wp[t]);
+#pragma unroll
+  for (int t = 0; t < MTW; ++t) fb[t] = load_frag<T>(xp[t]);
+  for (int ks = 0; ks < nks; ++ks) {
+    F na[4], nb[MTW];
+    const long off = (long)(ks + 1) * KW;
+    if (ks + 1 < nks) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) na[t] = load_frag<T>(wp[t] + off);
+#pragma unroll
+      for (int t = 0; t < MTW; ++t) nb[t] = load_frag<T>(xp[t] + off);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) acc[i][j] = Mma<T>::run(fa[i], fb[j], acc[i][j]);
+    if (ks + 1 < nks) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fa[t] = na[t];
+#pragma unroll
+      for (int t = 0; t < MTW; ++t) fb[t] = nb[t];
+    }
+  }
+
+  const float invT = 1.0f / a.temperature;
+  const bool gumbel = a.mode != 0;
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt) {
+    const int r = rbase + 16 * mt + r16;
+    const bool rvalid = r < a.rows;
+    const int seq = r / a.rows_per_seq, slot = r % a.rows_per_seq;
+    RowStat st;
+    st.arg.best = -INFINITY;
+    st.arg.second = -INFINITY;
+    st.arg.idx = 0x7fffffff;
+    st.zbest = 0.f;
+    st.zmax = -INFINITY;
+    st.m = -INFINITY;
+    st.s = 0.f;
+    float zz[2][8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][mt][e & 3];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int v0 = vw + 32 * p + 8 * g;
+      float gn[8];
+      if (gumbel && rvalid && v0 < V) {
+        uint32_t raw[8];
+        if (a.mode == 2)
+          philox_block8(a.seed, 3u, 0, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
+        else
+          philox_block8(a.seed, 0u, (uint64_t)seq, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gn[e] = gumbel_of(raw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gn[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = v0 + e;
+        if (v < V) {
+          const float z = zz[p][e];
+          const float sc = gumbel ? z * invT + gn[e] : z;
+          const bool win = sc > st.arg.best || (sc == st.arg.best && v < st.arg.idx);
+          if (win) st.zbest = z;
+          top2_push(st.arg, sc, v);
+          st.zmax = fmaxf(st.zmax, z);
+          st.m = fmaxf(st.m, z * invT);
+        }
+      }
+      if (a.logits && rvalid) {
+        float *lp = a.logits + (long)r * V + v0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (v0 + e < V) lp[e] = zz[p][e];
+      }
+    }
+    if (st.m != -INFINITY) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (vw + 32 * p + 8 * g + e < V) st.s += expf(zz[p][e] * invT - st.m);
+    }
+    st = rowstat_shfl_xor(st, 16);
+    st = rowstat_shfl_xor(st, 32);
+    if (g == 0) red[wave][16 * mt + r16] = st;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < MTW * 16; i += blockDim.x) {
+    const int r = rbase + i;
+    if (r >= a.rows) continue;
+    RowStat st = red[0][i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) st = rowstat_merge(st, red[w][i]);
+    HeadPartial hp;
+    hp.best = st.arg.best;
+    hp.second = st.arg.second;
+    hp.idx = st.arg.idx;
+    hp.zbest = st.zbest;
+    hp.zmax = st.zmax;
+    hp.m = st.m;
+    hp.s = st.s;
+    hp.pad = 0;
+    a.part[(long)r * a.nvb + vb] = hp;
+  }
+}
+
+// One wave per row merges the row's vocabulary-block records.
+__global__ __launch_bounds__(64) void lm_combine_kernel(HeadArgs a) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  ArgTop2 arg;
+  arg.best = -INFINITY;
+  arg.second = -INFINITY;
+  arg.idx = 0x7fffffff;
+  float zbest = 0.f, zmax = -INFINITY, m = -INFINITY;
+  double s = 0.0;
+  const HeadPartial *p = a.part + (long)r * a.nvb;
+  for (int i = lane; i < a.nvb; i += WAVE) {
+    const HeadPartial h = p[i];
+    ArgTop2 o;
+    o.best = h.best;
+    o.second = h.second;
+    o.idx = h.idx;
+    const bool bw = o.best > arg.best || (o.best == arg.best && o.idx < arg.idx);
+    if (bw) zbest = h.zbest;
+    arg = top2_merge(arg, o);
+    zmax = fmaxf(zmax, h.zmax);
+    if (h.m != -INFINITY) {
+      if (m == -INFINITY) { m = h.m; s = h.s; }
+      else {
+        const float M = fmaxf(m, h.m);
+        s = s * exp((double)m - M) + (double)h.s * exp((double)h.m - M);
+        m = M;
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    ArgTop2 b;
+    b.best = __shfl_xor(arg.best, o, WAVE);
+    b.second = __shfl_xor(arg.second, o, WAVE);
+    b.idx = __shfl_xor(arg.idx, o, WAVE);
+    const float zb2 = __shfl_xor(zbest, o, WAVE);
+    const bool bw = b.best > arg.best || (b.best == arg.best && b.idx < arg.idx);
+    if (bw) zbest = zb2;
+    arg = top2_merge(arg, b);
+    zmax = fmaxf(zmax, __shfl_xor(zmax, o, WAVE));
+    const float m2 = __shfl_xor(m, o, WAVE);
+    const double s2 = __shfl_xor(s, o, WAVE);
+    if (m2 != -INFINITY) {
+      if (m == -INFINITY) { m = m2; s = s2; }
+      else {
+        const float M = fmaxf(m, m2);
+        s = s * exp((double)m - M) + s2 * exp((double)m2 - M);
+        m = M;
+      }
+    }
+  }
+  if (lane == 0) {
+    a.ids[r] = arg.idx;
+    if (a.zmax) a.zmax[r] = zmax;
+    if (a.lse) a.lse[r] = (float)((double)m + log(s));
+    if (a.zsel) a.zsel[r] = zbest;
+    if (a.gap) a.gap[r] = arg.best - arg.second;
+  }
+}
+
+template <typename T, int MTW>
+static void launch_typed(const HeadArgs &a, hipStream_t st) {
+  const int nrb = (a.rows + MTW * 16 - 1) / (MTW * 16);
+  const int nvb8 = (a.nvb + NXCD - 1) / NXCD * NXCD;
+  hipLaunchKernelGGL((lm_head_kernel<T, MTW>), dim3(nvb8 * nrb), dim3(256), 0, st, a, nrb);
+}
+
+template <typename T>
+static void launch_rows(const HeadArgs &a, hipStream_t st) {
+  if (a.rows <= 16) launch_typed<T, 1>(a, st);
+  else if (a.rows <= 32) launch_typed<T, 2>(a, st);
+  else if (a.rows <= 48) launch_typed<T, 3>(a, st);
+  else launch_typed<T, 4>(a, st);
+}
+
+void launch_lm_head(const HeadArgs &a, hipStream_t st) {
+  if (a.rows == 0) return;
+  if (a.dtype == 1) launch_rows<bf16>(a, st);
+  else launch_rows<float>(a, st);
+  hipLaunchKernelGGL(lm_combine_kernel, dim3(a.rows), dim3(64), 0, st, a);
+}
+
+}  // namespace dstill

@@ -1,0 +1,385 @@
+// Verification of a drafted block against the target's logits (DStill,
+// Inference: greedy verification and the standard rejection-sampling
+// verifier, a correction token after a rejection and a bonus token after
+// full acceptance; DFlash review, Preliminary: tau = accepted + 1 in
+// [1, gamma+1]).  The acceptance test and the residual are the textbook ones
+// of speculative sampling (Leviathan et al.; Chen et al., both cited there):
+// accept y ~ q_k while u_k < p_k(y) / q_k(y); at the first rejection draw from
+// norm(max(0, p_k - q_k)); after gamma acceptances draw from p_gamma.  Draws
+// use Gumbel-max over log-weights with counter-based Philox noise.
+//
+// Four kernels, all streaming:
+//   vrow     per (target row, vocab split): max, argmax (lowest id), runner-
+//            up, and the softmax mass at temperature T (fp64 accumulation)
+//   vdecide  per sequence: merge the splits, then the greedy prefix match or
+//            the accept scan (one lane per block slot, first failure by
+//            ballot); writes the accepted prefix, tau and the flags
+//   vsample  (rejection sampling) per (sequence, vocab split): Gumbel-max
+//            over log max(0, p - q) of the rejected row, or over log p of
+//            the bonus row, in fp64
+//   vfinish  per sequence: merge and write the final token
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dstill {
+
+struct VRowPart {
+  float best, second;
+  int idx, bad;
+  float m, pad;
+  double s;  // sum exp(z/T - m)
+};
+
+struct D2 {
+  double best, second;
+  int idx;
+};
+__device__ __forceinline__ void d2_push(D2 &a, double s, int i) {
+  if (s > a.best || (s == a.best && i < a.idx)) {
+    a.second = fmax(a.second, a.best);
+    a.best = s;
+    a.idx = i;
+  } else {
+    a.second = fmax(a.second, s);
+  }
+}
+__device__ __forceinline__ D2 d2_merge(D2 a, D2 b) {
+  if (b.best > a.best || (b.best == a.best && b.idx < a.idx)) {
+    D2 t = a; a = b; b = t;
+  }
+  a.second = fmax(a.second, b.best);
+  return a;
+}
+
+struct VSampPart {
+  double best_r, second_r, best_p, second_p;
+  int idx_r, idx_p, any_r, bad;
+};
+
+struct VerifyWs {
+  VRowPart *rowpart;   // [bs*(gamma+1)][nsplit]
+  double *lse_t;       // [bs*(gamma+1)]
+  int *kstar;          // [bs]
+  VSampPart *samp;     // [bs][nsplit]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline VerifyWs carve(void *ws, int bs, int gamma, int nsplit) {
+  char *p = (char *)ws;
+  VerifyWs w;
+  const size_t rows = (size_t)bs * (gamma + 1);
+  w.rowpart = (VRowPart *)p;
+  p += align256(rows * nsplit * sizeof(VRowPart));
+  w.lse_t = (double *)p;
+  p += align256(rows * sizeof(double));
+  w.kstar = (int *)p;
+  p += align256((size_t)bs * sizeof(int));
+  w.samp = (VSampPart *)p;
+  return w;
+}
+
+size_t verify_ws_bytes(int bs, int gamma, int nsplit) {
+  const size_t rows = (size_t)bs * (gamma + 1);
+  return align256(rows * nsplit * sizeof(VRowPart)) + align256(rows * sizeof(double)) +
+         align256((size_t)bs * sizeof(int)) + align256((size_t)bs * nsplit * sizeof(VSampPart));
+}
+
+int verify_plan_splits(int vocab) {
+  // about 4K ids per split, at most 64 splits
+  int n = (vocab + 4095) / 4096;
+  return n < 1 ? 1 : (n > 64 ? 64 : n);
+}
+
+__device__ __forceinline__ int split_chunk(int vocab, int nsplit) {
+  const int c = (vocab + nsplit - 1) / nsplit;
+  return (c + 7) & ~7;
+}
+
+__device__ __forceinline__ float ld(const float *p, long i) { return p[i]; }
+__device__ __forceinline__ float ld(const bf16 *p, long i) { return static_cast<float>(p[i]); }
+
+// ---- per-row statistics --------------------------------------------------
+template <typename TT>
+__global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
+  __shared__ VRowPart red[4];
+  const int row = blockIdx.x, sp = blockIdx.y;
+  const int V = a.vocab;
+  const int chunk = split_chunk(V, a.nsplit);
+  const int v0 = sp * chunk, v1 = min(v0 + chunk, V);
+  const TT *z = (const TT *)a.target + (long)row * V;
+  const float invT = 1.0f / a.temperature;
+  ArgTop2 arg;
+  arg.best = -INFINITY;
+  arg.second = -INFINITY;
+  arg.idx = 0x7fffffff;
+  float m = -INFINITY;
+  double s = 0.0;
+  int bad = 0;
+  for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
+    const float x = ld(z, v);
+    if (!isfinite(x)) { bad = 1; continue; }
+    top2_push(arg, x, v);
+    const float y = x * invT;
+    if (y > m) {
+      s = s * exp((double)m - (double)y) + 1.0;
+      m = y;
+    } else {
+      s += (double)expf(y - m);
+    }
+  }
+  // wave merge
+  for (int o = 32; o > 0; o >>= 1) {
+    arg = top2_shfl_xor(arg, o);
+    const float m2 = __shfl_xor(m, o, WAVE);
+    const double s2 = __shfl_xor(s, o, WAVE);
+    bad |= __shfl_xor(bad, o, WAVE);
+    if (m2 != -INFINITY) {
+      if (m == -INFINITY) { m = m2; s = s2; }
+      else {
+        const float M = fmaxf(m, m2);
+        s = s * exp((double)m - M) + s2 * exp((double)m2 - M);
+        m = M;
+      }
+    }
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    VRowPart p;
+    p.best = arg.best; p.second = arg.second; p.idx = arg.idx; p.bad = bad;
+    p.m = m; p.pad = 0.f; p.s = s;
+    red[wave] = p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    VRowPart t = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+      const VRowPart u = red[i];
+      ArgTop2 x{t.best, t.second, t.idx}, y{u.best, u.second, u.idx};
+      x = top2_merge(x, y);
+      t.best = x.best; t.second = x.second; t.idx = x.idx;
+      t.bad |= u.bad;
+      if (u.m != -INFINITY) {
+        if (t.m == -INFINITY) { t.m = u.m; t.s = u.s; }
+        else {
+          const float M = fmaxf(t.m, u.m);
+          t.s = t.s * exp((double)t.m - M) + u.s * exp((double)u.m - M);
+          t.m = M;
+        }
+      }
+    }
+    w.rowpart[(long)row * a.nsplit + sp] = t;
+  }
+}
+
+// ---- decision scan ---------------------------------------------------------
+template <typename TT>
+__global__ __launch_bounds__(64) void vdecide_kernel(VerifyArgs a, VerifyWs w) {
+  const int b = blockIdx.x, k = threadIdx.x;
+  const int G = a.gamma, V = a.vocab;
+  const bool rowlane = k <= G;
+  // merge this lane's row
+  ArgTop2 arg;
+  arg.best = -INFINITY;
+  arg.second = -INFINITY;
+  arg.idx = 0x7fffffff;
+  int bad = 0;
+  double lse = 0.0;
+  if (rowlane) {
+    const long row = (long)b * (G + 1) + k;
+    float m = -INFINITY;
+    double s = 0.0;
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const VRowPart p = w.rowpart[row * a.nsplit + sp];
+      ArgTop2 y{p.best, p.second, p.idx};
+      arg = top2_merge(arg, y);
+      bad |= p.bad;
+      if (p.m != -INFINITY) {
+        if (m == -INFINITY) { m = p.m; s = p.s; }
+        else {
+          const float M = fmaxf(m, p.m);
+          s = s * exp((double)m - M) + p.s * exp((double)p.m - M);
+          m = M;
+        }
+      }
+    }
+    lse = (double)m + log(s);
+    w.lse_t[row] = lse;
+  }
+  int y = 0, yraw = 0;
+  if (k < G) {
+    yraw = a.draft_ids[(long)b * G + k];
+    y = yraw < 0 ? 0 : (yraw >= V ? V - 1 : yraw);
+    if (y != yraw) bad = 1;
+  }
+  uint32_t flags = 0;
+  bool ok = false;  // slot k passes its test
+  bool near = false;
+  if (a.mode == 0) {
+    ok = k < G && yraw == arg.idx;
+    near = rowlane && (arg.best - arg.second) < NEAR_BAND;
+  } else if (k < G) {
+    const long row = (long)b * (G + 1) + k;
+    const double zt = (double)ld((const TT *)a.target, row * V + y);
+    const double zd = (double)a.draft_logits[((long)b * G + k) * V + y];
+    const double T = (double)a.temperature;
+    const double lp = zt / T - lse;
+    const double lq = zd / T - (double)a.draft_lse[(long)b * G + k];
+    const double ratio = exp(lp - lq);
+    uint32_t raw[8];
+    philox_block8(a.seed, 1u, (uint64_t)b, (uint64_t)k, a.cycle, 0, raw);
+    const double u = (double)u24(raw[0]);
+    ok = u < ratio;
+    near = fabs(ratio - u) < (double)NEAR_BAND;
+    if (!isfinite(zd)) bad = 1;
+  }
+  // first failing slot (gamma if all pass)
+  const unsigned long long fail = __ballot(k < G && !ok);
+  const int L = fail ? min(__builtin_ctzll(fail), G) : G;
+  const unsigned long long bads = __ballot(bad != 0);
+  if (bads) flags |= 16u;
+  if (a.mode == 0) {
+    if (__ballot(near && k <= L)) flags |= 1u;
+  } else {
+    if (__ballot(near && k <= L && k < G)) flags |= 2u;
+  }
+  // tokens: accepted prefix; slot L gets the target's token (greedy) or is
+  // filled by vfinish (rejection sampling)
+  if (k <= G) {
+    int tok = -1;
+    if (k < L) tok = y;
+    else if (k == L && a.mode == 0) tok = arg.idx;
+    if (!(k == L && a.mode != 0)) a.tokens[(long)b * (G + 1) + k] = tok;
+  }
+  if (k == 0) {
+    a.tau[b] = L + 1;
+    a.flags[b] = flags;
+    w.kstar[b] = L;
+  }
+}
+
+// ---- residual / bonus draw ---------------------------------------------------
+template <typename TT>
+__global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) {
+  __shared__ VSampPart red[4];
+  const int b = blockIdx.x, sp = blockIdx.y;
+  const int G = a.gamma, V = a.vocab;
+  const int ks = w.kstar[b];
+  const long trow = (long)b * (G + 1) + ks;
+  const double lse_t = w.lse_t[trow];
+  const bool bonus = ks >= G;
+  const double lse_d = bonus ? 0.0 : (double)a.draft_lse[(long)b * G + ks];
+  const TT *zt = (const TT *)a.target + trow * V;
+  const float *zd = bonus ? nullptr : a.draft_logits + ((long)b * G + ks) * V;
+  const double T = (double)a.temperature;
+  const int chunk = split_chunk(V, a.nsplit);
+  const int v0 = sp * chunk, v1 = min(v0 + chunk, V);
+  D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
+  int any_r = 0, bad = 0;
+  for (int vb = v0 + 8 * threadIdx.x; vb < v1; vb += 8 * blockDim.x) {
+    uint32_t raw[8];
+    philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int v = vb + e;
+      if (v >= v1) break;
+      const double g = (double)gumbel_of(raw[e]);
+      const double lp = (double)ld(zt, v) / T - lse_t;
+      d2_push(pp, lp + g, v);
+      if (!bonus) {
+        const double zdv = (double)zd[v];
+        if (!isfinite(zdv)) bad = 1;
+        const double r = exp(lp) - exp(zdv / T - lse_d);
+        if (r > 0.0) {
+          any_r = 1;
+          d2_push(rr, log(r) + g, v);
+        }
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    D2 x{__shfl_xor(rr.best, o, WAVE), __shfl_xor(rr.second, o, WAVE), __shfl_xor(rr.idx, o, WAVE)};
+    rr = d2_merge(rr, x);
+    D2 y{__shfl_xor(pp.best, o, WAVE), __shfl_xor(pp.second, o, WAVE), __shfl_xor(pp.idx, o, WAVE)};
+    pp = d2_merge(pp, y);
+    any_r |= __shfl_xor(any_r, o, WAVE);
+    bad |= __shfl_xor(bad, o, WAVE);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    VSampPart p;
+    p.best_r = rr.best; p.second_r = rr.second; p.idx_r = rr.idx;
+    p.best_p = pp.best; p.second_p = pp.second; p.idx_p = pp.idx;
+    p.any_r = any_r; p.bad = bad;
+    red[wave] = p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    VSampPart t = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+      const VSampPart u = red[i];
+      D2 x{t.best_r, t.second_r, t.idx_r}, y{u.best_r, u.second_r, u.idx_r};
+      x = d2_merge(x, y);
+      t.best_r = x.best; t.second_r = x.second; t.idx_r = x.idx;
+      D2 xp{t.best_p, t.second_p, t.idx_p}, yp{u.best_p, u.second_p, u.idx_p};
+      xp = d2_merge(xp, yp);
+      t.best_p = xp.best; t.second_p = xp.second; t.idx_p = xp.idx;
+      t.any_r |= u.any_r;
+      t.bad |= u.bad;
+    }
+    w.samp[(long)b * a.nsplit + sp] = t;
+  }
+}
+
+__global__ __launch_bounds__(64) void vfinish_kernel(VerifyArgs a, VerifyWs w) {
+  const int b = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int G = a.gamma;
+  const int ks = w.kstar[b];
+  D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
+  int any_r = 0, bad = 0;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const VSampPart p = w.samp[(long)b * a.nsplit + sp];
+    rr = d2_merge(rr, D2{p.best_r, p.second_r, p.idx_r});
+    pp = d2_merge(pp, D2{p.best_p, p.second_p, p.idx_p});
+    any_r |= p.any_r;
+    bad |= p.bad;
+  }
+  uint32_t f = 0;
+  int tok;
+  double gap;
+  if (ks < G && any_r) {
+    tok = rr.idx;
+    gap = rr.best - rr.second;
+  } else {
+    if (ks < G) f |= 8u;  // zero residual: drew from p
+    tok = pp.idx;
+    gap = pp.best - pp.second;
+  }
+  if (gap < (double)NEAR_BAND) f |= 4u;
+  if (bad) f |= 16u;
+  a.tokens[(long)b * (G + 1) + ks] = tok;
+  a.flags[b] |= f;
+}
+
+template <typename TT>
+static void launch_typed(const VerifyArgs &a, hipStream_t st) {
+  VerifyWs w = carve(a.ws, a.bs, a.gamma, a.nsplit);
+  const int rows = a.bs * (a.gamma + 1);
+  hipLaunchKernelGGL(vrow_kernel<TT>, dim3(rows, a.nsplit), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(vdecide_kernel<TT>, dim3(a.bs), dim3(64), 0, st, a, w);
+  if (a.mode == 1) {
+    hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsplit), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(vfinish_kernel, dim3(a.bs), dim3(64), 0, st, a, w);
+  }
+}
+
+void launch_verify(const VerifyArgs &a, hipStream_t st) {
+  if (a.bs == 0) return;
+  if (a.tdtype == 1) launch_typed<bf16>(a, st);
+  else launch_typed<float>(a, st);
+}
+
+}  // namespace dstill

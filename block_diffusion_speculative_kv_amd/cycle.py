@@ -1,0 +1,135 @@
+"""One draft + verify cycle over resident synthetic inputs.
+
+A cycle is the four library calls in order (DFlash review, Method /
+Inference and Preliminary; DStill, Inference):
+
+  inject_kv       the target features of the n_new tokens verified last cycle
+                  become context K/V in every draft layer
+  block_draft     one pass over anchor + gamma masks (per copy)
+  lm_head_argmax  shared head: greedy argmax, Gumbel-max sampling, or the
+                  shared-Gumbel argmax of the multi-copy layout
+  verify          greedy prefix match or rejection sampling (none for the
+                  multi-copy layout, whose verify is its own state-equality
+                  rule)
+
+The context cache is filled once by injecting every context row (prefill),
+in chunks.  In steady state each cycle re-injects the n_new most recent
+context positions of every sequence (the same slots every cycle), so every
+timed cycle does identical work over identical shapes.  All tensors live on
+the GPU before the first timed cycle; nothing is copied to or from the host
+inside a cycle.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from synth import gen
+
+from . import Drafter, verify, verify_workspace_bytes
+from ._lib import HEAD_ARGMAX, HEAD_GUMBEL, HEAD_SHARED_GUMBEL, VERIFY_GREEDY, VERIFY_RS
+
+_HEAD_MODE = {"argmax": HEAD_ARGMAX, "gumbel": HEAD_GUMBEL, "shared_gumbel": HEAD_SHARED_GUMBEL}
+
+
+class Cycle:
+    def __init__(self, cfg: dict, device="cuda", n_new: int = 8, prefill_chunk: int = 8192,
+                 seed: int = 0):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        bs, C, B, d = cfg["bs"], cfg["n_copies"], cfg["block"], cfg["hidden"]
+        self.gamma = cfg["gamma"]
+        self.ctx = list(cfg["ctx_lens"])
+        self.max_ctx = max(self.ctx)
+        self.n_new = max(1, min(n_new, min(self.ctx) if min(self.ctx) > 0 else 1))
+        self.w = gen.weights(cfg, device=self.dev)
+        self.dr = Drafter(cfg, self.w)
+        self.kv = self.dr.kv_cache(bs, self.max_ctx + B)
+        self.mode = _HEAD_MODE[cfg["lm_mode"]]
+        self.verify_mode = {"greedy": VERIFY_GREEDY, "rs": VERIFY_RS}.get(cfg["verify"])
+        self.T = float(cfg.get("temperature", 1.0))
+        self.seed = seed
+        # head rows: slots 1..gamma of every block, or all slots of every copy
+        if self.mode == HEAD_SHARED_GUMBEL:
+            self.rows, self.rows_per_seq, self.seq_stride, self.row0 = bs * C * B, B, B, 0
+        else:
+            self.rows, self.rows_per_seq, self.seq_stride, self.row0 = bs * C * self.gamma, \
+                self.gamma, B, 1
+        inj_rows = bs * self.n_new
+        self.ws = self.dr.workspace(max_batch=bs, max_copies=C, max_ctx=self.max_ctx,
+                                    max_inject_rows=max(inj_rows, min(prefill_chunk,
+                                                                      sum(self.ctx) or 1)),
+                                    max_head_rows=self.rows)
+        self._prefill(prefill_chunk)
+        # per-cycle inputs
+        self.tokens = gen.block_tokens(cfg, device=self.dev)
+        self.ctx_len = torch.tensor(self.ctx, dtype=torch.int32, device=self.dev)
+        self.feats = gen.feats(cfg, inj_rows, name="feats_cycle", device=self.dev)
+        seq, pos = [], []
+        for b, S in enumerate(self.ctx):
+            for j in range(self.n_new):
+                p = S - self.n_new + j
+                seq.append(b if p >= 0 else -1)
+                pos.append(max(p, 0))
+        self.inj_seq = torch.tensor(seq, dtype=torch.int32, device=self.dev)
+        self.inj_pos = torch.tensor(pos, dtype=torch.int32, device=self.dev)
+        self.hidden = torch.empty((bs, C, B, d), dtype=self.dr.tdtype, device=self.dev)
+        self.draft_flags = torch.zeros(bs, dtype=torch.int32, device=self.dev)
+        r = self.rows
+        self.ids = torch.empty(r, dtype=torch.int32, device=self.dev)
+        self.zmax = torch.empty(r, dtype=torch.float32, device=self.dev)
+        self.lse = torch.empty(r, dtype=torch.float32, device=self.dev)
+        self.zsel = torch.empty(r, dtype=torch.float32, device=self.dev)
+        self.gap = torch.empty(r, dtype=torch.float32, device=self.dev)
+        self.logits = (torch.empty((r, cfg["vocab"]), dtype=torch.float32, device=self.dev)
+                       if self.verify_mode == VERIFY_RS else None)
+        if self.verify_mode is not None:
+            self.target = gen.target_logits(cfg, device=self.dev)
+            self.out_tokens = torch.empty((bs, self.gamma + 1), dtype=torch.int32,
+                                          device=self.dev)
+            self.tau = torch.empty(bs, dtype=torch.int32, device=self.dev)
+            self.vflags = torch.empty(bs, dtype=torch.int32, device=self.dev)
+            self.vws = torch.empty(verify_workspace_bytes(bs, self.gamma, cfg["vocab"]),
+                                   dtype=torch.uint8, device=self.dev)
+        torch.cuda.synchronize(self.dev)
+
+    def _prefill(self, chunk):
+        rows = [(b, p) for b, S in enumerate(self.ctx) for p in range(S)]
+        for i in range(0, len(rows), chunk):
+            part = rows[i:i + chunk]
+            f = gen.feats(self.cfg, len(part), name=f"feats_prefill{i}", device=self.dev)
+            seq = torch.tensor([b for b, _ in part], dtype=torch.int32, device=self.dev)
+            pos = torch.tensor([p for _, p in part], dtype=torch.int32, device=self.dev)
+            self.dr.inject_kv(f, seq, pos, self.kv, self.ws)
+        torch.cuda.synchronize(self.dev)
+
+    # -- the four calls -------------------------------------------------------
+    def inject(self):
+        self.dr.inject_kv(self.feats, self.inj_seq, self.inj_pos, self.kv, self.ws)
+
+    def draft(self):
+        self.dr.block_draft(self.tokens, self.ctx_len, self.max_ctx, self.kv, self.hidden, self.ws,
+                            flags=self.draft_flags)
+
+    def head(self, cycle: int):
+        hv = self.hidden.view(-1, self.cfg["hidden"])[self.row0:]
+        self.dr.lm_head_argmax(hv, self.rows, self.rows_per_seq, self.seq_stride, self.ids,
+                               self.ws, mode=self.mode, temperature=self.T, seed=self.seed,
+                               cycle=cycle, zmax=self.zmax, lse=self.lse, zsel=self.zsel,
+                               gap=self.gap, logits=self.logits)
+
+    def verify(self, cycle: int):
+        if self.verify_mode is None:
+            return
+        bs = self.cfg["bs"]
+        verify(self.verify_mode, self.ids.view(bs, self.gamma), self.target, self.out_tokens,
+               self.tau, self.vflags, self.vws, temperature=self.T, seed=self.seed, cycle=cycle,
+               draft_lse=self.lse.view(bs, self.gamma) if self.logits is not None else None,
+               draft_logits=(self.logits.view(bs, self.gamma, -1)
+                             if self.logits is not None else None))
+
+    def step(self, cycle: int = 0):
+        self.inject()
+        self.draft()
+        self.head(cycle)
+        self.verify(cycle)

@@ -58,6 +58,10 @@ def verify_greedy(zt, y):
     L = 0
     while L < gamma and int(y[L]) == int(t[L]):
         L += 1
+    # the target rows whose argmax decided the outcome are 0..L
+    for k in range(L + 1):
+        if _argmax_gap(zt[k])[1] < NEAR:
+            flags |= FLAG_NEAR_TIE_TARGET
     tokens = [int(v) for v in y[:L]] + [int(t[L])]
     return tokens, L + 1, flags
 

@@ -1,0 +1,96 @@
+"""GPU parity of dstill_inject_kv against oracle.drafter.Drafter.inject_rows.
+
+Fusion H_t = RMSNorm(W_c feats) and injection K = rope(k_norm(W_k H_t)),
+V = W_v H_t (DFlash review, Method / Inference) on the same features, row
+sequence ids and positions.  Cache rows must match to 1e-5 relative (fp32) or
+within 2 bf16 ulps (bf16 rounds once, after fp32 vs fp64 arithmetic);
+rows with an invalid sequence id or position are not written; incremental
+injection equals injecting everything at once (bit-exact).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_speculative_kv_amd as bd
+from oracle.drafter import Drafter as OracleDrafter
+from synth import configs, gen
+from tests.helpers import assert_close_rel, assert_within_ulps, device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inject(cfg, n, cap, max_batch, seed_rows=0, invalid=()):
+    dev = device()
+    w = gen.weights(cfg, device=dev)
+    dr = bd.Drafter(cfg, w)
+    kv = dr.kv_cache(max_batch, cap)
+    feats = gen.feats(cfg, n, device=dev)
+    rng = np.random.default_rng(seed_rows)
+    slots = rng.permutation(max_batch * cap)[:n]      # distinct cache rows
+    seq, pos = slots // cap, slots % cap
+    for i in invalid:
+        seq[i] = -1 if i % 2 else max_batch
+    seq_t = torch.from_numpy(seq.astype(np.int32)).to(dev)
+    pos_t = torch.from_numpy(pos.astype(np.int32)).to(dev)
+    ws = dr.workspace(max_inject_rows=n)
+    dr.inject_kv(feats, seq_t, pos_t, kv, ws)
+    torch.cuda.synchronize()
+    return dev, w, dr, kv, feats, seq, pos, (seq_t, pos_t, ws)
+
+
+def _check(cfg, w, kv, feats, seq, pos, rows):
+    od = OracleDrafter(cfg, to_np(w))
+    f_np = to_np(feats)[rows]
+    ks, vs = od.inject_rows(f_np, pos[rows])
+    for l in range(cfg["n_layers"]):
+        K = to_np(kv.k[l])
+        V = to_np(kv.v[l])
+        gk = K[seq[rows], :, pos[rows]]          # [n, hkv, dh]
+        gv = V[seq[rows], :, pos[rows]]
+        if cfg["dtype"] == "f32":
+            assert_close_rel(gk, ks[l], 1e-5, f"K layer {l}")
+            assert_close_rel(gv, vs[l], 1e-5, f"V layer {l}")
+        else:
+            assert_within_ulps(gk, ks[l], 2, f"K layer {l}")
+            assert_within_ulps(gv, vs[l], 2, f"V layer {l}")
+
+
+def test_tiny_fp32():
+    cfg = configs.get("tiny_fp32")
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 128, 130, 1)
+    _check(cfg, w, kv, feats, seq, pos, np.arange(128))
+
+
+def test_small_bf16_with_skipped_rows():
+    cfg = configs.small_bf16()
+    n = 77
+    invalid = (3, 10, 11)
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, n, 50, 3, invalid=invalid)
+    ok = np.array([i not in invalid for i in range(n)])
+    _check(cfg, w, kv, feats, seq, pos, np.nonzero(ok)[0])
+    # every cache row not named by a valid input row is still zero
+    written = set(zip(seq[ok].tolist(), pos[ok].tolist()))
+    K = kv.k[0].float().cpu().numpy()
+    for b in range(3):
+        for p in range(50):
+            if (b, p) not in written:
+                assert not K[b, :, p].any()
+
+
+def test_incremental_equals_all_at_once():
+    cfg = configs.small_bf16()
+    dev, w, dr, kv, feats, seq, pos, (seq_t, pos_t, ws) = _inject(cfg, 60, 40, 3)
+    kv2 = dr.kv_cache(3, 40)
+    for a, b in ((0, 7), (7, 31), (31, 60)):
+        dr.inject_kv(feats[a:b].contiguous(), seq_t[a:b].contiguous(), pos_t[a:b].contiguous(),
+                     kv2, ws)
+    torch.cuda.synchronize()
+    for l in range(cfg["n_layers"]):
+        assert torch.equal(kv.k[l], kv2.k[l]) and torch.equal(kv.v[l], kv2.v[l])
+
+
+def test_q8b_rows_sampled():
+    cfg = configs.get("q8b_bs1_greedy")
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 40, 4096, 1)
+    _check(cfg, w, kv, feats, seq, pos, np.arange(0, 40, 5))

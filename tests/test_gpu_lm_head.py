@@ -1,0 +1,145 @@
+"""GPU parity of dstill_lm_head_argmax against oracle.drafter.lm_head.
+
+Both sides get the same hidden rows and the same LM-head weight (bf16 or
+fp32, drawn on the GPU by synth.gen).  The oracle computes the full logits in
+fp64 and takes the argmax / log-sum-exp / Gumbel-max over them; the kernel
+never stores logits unless asked and reduces them on the fly.  Ids must agree
+bit-exactly wherever neither side's top-2 score gap is below 1e-5; zmax,
+zsel, lse and stored logits must agree to the fp32 accumulation bound
+2.5e-4 * sum_k |h_k w_k| (recursive-summation bound for 4096 terms), which for
+these inputs is ~1e-4 absolute; the near-tie count is reported.
+
+Shapes: the tiny fp32 workload (V 1024, d 256, gamma 7 rows), a ragged bf16
+case (V 5003, d 512, rows in blocks of 15 with a stride of 16), and the full
+8B-shaped head (V 151936, d 4096) at the row counts of the greedy bs-1 (15
+rows, argmax), bs-32 rejection-sampling (480 rows, Gumbel, logits stored;
+sampled rows checked) and multi-copy (144 rows, shared Gumbel) workloads.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_speculative_kv_amd as bd
+from oracle import philox
+from oracle.drafter import lm_head as oracle_head
+from synth import configs, gen
+from tests.helpers import compare_ids, device, to_np
+
+pytestmark = pytest.mark.gpu
+
+_TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class _HeadOnly:
+    """A drafter handle whose other weights are tiny placeholders: only the
+    LM head is exercised."""
+
+    def __init__(self, V, d, dtype, seed):
+        self.cfg = configs.finish(dict(
+            n_layers=1, hidden=d, n_q_heads=1, n_kv_heads=1, head_dim=64, mlp=32, vocab=V,
+            n_feat_layers=1, target_hidden=32, gamma=15, dtype=dtype, rms_eps=1e-6,
+            rope_theta=1e6, qk_norm=1, bs=1, ctx=[0], n_copies=1, seed=seed))
+        dev = device()
+        td = _TD[dtype]
+        self.w_lm = gen.normal((V, d), 0.02, seed=seed, name="lm_head", device=dev, dtype=td)
+        z = lambda *s: torch.zeros(*s, dtype=td, device=dev)
+        layer = dict(attn_norm=z(d), wqkv=z(3 * 64, d), q_norm=z(64), k_norm=z(64), wo=z(d, 64),
+                     mlp_norm=z(d), w_gate_up=z(64, d), w_down=z(d, 32))
+        self.w = dict(embed=z(V, d), lm_head=self.w_lm, w_fuse=z(d, 32), g_fuse=z(d),
+                      g_final=z(d), layers=[layer])
+        self.dr = bd.Drafter(self.cfg, self.w)
+
+
+def _gumbel_rows(mode, seed, cycle, seqs, slots, V):
+    purpose = philox.PURPOSE_SHARED if mode == bd.HEAD_SHARED_GUMBEL else philox.PURPOSE_DRAFT
+    out = []
+    for s, p in zip(seqs, slots):
+        if mode == bd.HEAD_SHARED_GUMBEL:
+            s = 0
+        out.append(philox.gumbel_row(seed, purpose, s, p, cycle, V))
+    return np.stack(out)
+
+
+def _run_case(V, d, dtype, rows, rows_per_seq, seq_stride, mode, T=1.0, keep_logits=False,
+              sample=None, seed=5, cycle=3):
+    h = _HeadOnly(V, d, dtype, seed)
+    dev = device()
+    nseq = (rows + rows_per_seq - 1) // rows_per_seq
+    hid_all = gen.normal((nseq * seq_stride, d), 1.0, seed=seed, name="hidden", device=dev,
+                         dtype=_TD[dtype])
+    ids = torch.empty(rows, dtype=torch.int32, device=dev)
+    outs = {k: torch.empty(rows, dtype=torch.float32, device=dev)
+            for k in ("zmax", "lse", "zsel", "gap")}
+    logits = torch.empty((rows, V), dtype=torch.float32, device=dev) if keep_logits else None
+    ws = h.dr.workspace(max_head_rows=rows)
+    h.dr.lm_head_argmax(hid_all, rows, rows_per_seq, seq_stride, ids, ws, mode=mode,
+                        temperature=T, seed=seed, cycle=cycle, logits=logits, **outs)
+    torch.cuda.synchronize()
+    # rows checked against the oracle
+    r_idx = np.arange(rows) if sample is None else np.unique(
+        np.linspace(0, rows - 1, sample).astype(int))
+    seqs, slots = r_idx // rows_per_seq, r_idx % rows_per_seq
+    hrows = seqs * seq_stride + slots
+    hid_np = to_np(hid_all)[hrows]
+    W = to_np(h.w_lm)
+    g = None if mode == bd.HEAD_ARGMAX else _gumbel_rows(mode, seed, cycle, seqs, slots, V)
+    ref = oracle_head(W, hid_np, temperature=T, gumbel=g, keep_logits=True)
+    bound = 2.5e-4 * (np.abs(hid_np) @ np.abs(W).T)        # fp32 accumulation bound
+    zb = bound.max(-1)
+    got = {k: v.cpu().numpy().astype(np.float64)[r_idx] for k, v in outs.items()}
+    gids = ids.cpu().numpy()[r_idx]
+    excl = (ref["gap"] < 1e-5) | (got["gap"] < 1e-5)
+    n = compare_ids(gids, ref["ids"], excl, f"lm_head V{V} mode{mode}")
+    assert np.all(np.abs(got["zmax"] - ref["zmax"]) <= zb)
+    ok = ~excl
+    assert np.all(np.abs(got["zsel"][ok] - ref["zsel"][ok]) <= zb[ok])
+    # lse of z/T: each term's error is bounded by the logit bound / T
+    assert np.all(np.abs(got["lse"] - ref["lse"]) <= zb / T + 1e-6 * np.abs(ref["lse"]))
+    assert np.all(np.abs(got["gap"][ok] - ref["gap"][ok]) <= 2 * zb[ok] / min(T, 1.0) + 1e-5)
+    if keep_logits:
+        L = logits.cpu().numpy().astype(np.float64)[r_idx]
+        assert np.all(np.abs(L - ref["logits"]) <= bound)
+    return n, ids.cpu().numpy(), r_idx
+
+
+def test_tiny_fp32_argmax():
+    n, _, _ = _run_case(1024, 256, "f32", 7, 7, 8, bd.HEAD_ARGMAX, keep_logits=True)
+    assert n == 0
+
+
+def test_ragged_bf16_gumbel_strided_rows():
+    _run_case(5003, 512, "bf16", 37, 15, 16, bd.HEAD_GUMBEL, T=0.8, keep_logits=True)
+
+
+def test_ragged_bf16_argmax():
+    _run_case(5003, 512, "bf16", 45, 15, 16, bd.HEAD_ARGMAX)
+
+
+def test_q8b_greedy_bs1_rows():
+    n, _, _ = _run_case(151936, 4096, "bf16", 15, 15, 16, bd.HEAD_ARGMAX)
+    assert n <= 1
+
+
+def test_q8b_bs32_gumbel_with_logits_sampled():
+    _run_case(151936, 4096, "bf16", 480, 15, 16, bd.HEAD_GUMBEL, keep_logits=True, sample=24)
+
+
+def test_q8b_multicopy_shared_gumbel():
+    n, ids, r_idx = _run_case(151936, 4096, "bf16", 144, 16, 16, bd.HEAD_SHARED_GUMBEL,
+                              sample=18)
+    assert n <= 1
+
+
+def test_shared_gumbel_identical_rows_agree():
+    # copies of one hidden row at the same slot share the noise: same draw
+    h = _HeadOnly(5003, 512, "bf16", 1)
+    dev = device()
+    row = gen.normal((1, 512), 1.0, seed=1, name="hidden", device=dev, dtype=torch.bfloat16)
+    hid = row.repeat(4 * 16, 1).contiguous()
+    ids = torch.empty(64, dtype=torch.int32, device=dev)
+    ws = h.dr.workspace(max_head_rows=64)
+    h.dr.lm_head_argmax(hid, 64, 16, 16, ids, ws, mode=bd.HEAD_SHARED_GUMBEL, seed=3, cycle=1)
+    got = ids.cpu().numpy().reshape(4, 16)
+    assert np.all(got == got[0])           # every copy agrees slot by slot
+    assert len(set(got[0].tolist())) > 1   # slots draw different noise

@@ -22,7 +22,7 @@ from scipy import stats
 
 from oracle import philox
 from oracle.drafter import lm_head
-from oracle.verify import (FLAG_ZERO_RESIDUAL, latency_per_token,
+from oracle.verify import (FLAG_NEAR_TIE_TARGET, FLAG_ZERO_RESIDUAL, latency_per_token,
                            verify_batch, verify_greedy, verify_rs)
 
 
@@ -188,6 +188,19 @@ def test_greedy_planted_matches():
         assert tau == k + 1
         assert toks == list(t[:k]) + [int(t[k])]
         assert f == 0
+
+
+def test_greedy_near_tie_flag():
+    # a target row whose top-2 gap is below 1e-5 is flagged only when it
+    # decides the outcome (rows 0..L)
+    zt = np.zeros((3, 5))
+    zt[0] = [0.0, 1.0, 0.2, 0.0, 0.0]
+    zt[1] = [0.0, 0.5, 0.5 + 5e-6, 0.0, 0.0]
+    zt[2] = [2.0, 0.0, 0.0, 0.0, 0.0]
+    _t, tau, f = verify_greedy(zt, np.array([3, 2]))      # rejects at row 0
+    assert tau == 1 and f == 0
+    _t, tau, f = verify_greedy(zt, np.array([1, 2]))      # row 1 decides
+    assert tau == 3 and f & FLAG_NEAR_TIE_TARGET
 
 
 def test_greedy_lowest_index_tie():
