@@ -20,6 +20,8 @@
 // 4g + i is key 8g + 4t + i, the 8 consecutive keys 8g .. 8g+7 (g = l / 16).
 // Those 8 probabilities are exactly that lane's B fragment of P^T, and the
 // matching A fragment of V^T is 8 consecutive keys of one transposed V row.
+// bf16 probabilities go through P.V as a hi + lo pair of bf16 fragments, so
+// the product keeps about 16 significant bits of P (fp32 accumulation).
 // The row max/sum over a query's keys is then a reduction over the four lane
 // groups: two xor-shuffles (16, 32).
 #include <math.h>
@@ -110,18 +112,28 @@ __device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
     }
     ws.m = mnew;
     // P^T fragments: bf16 packs all 8 keys in one fragment; fp32 uses two.
+    // In bf16 the probabilities are carried as a hi + lo pair (lo = the
+    // rounding residual of hi), so P.V keeps ~16 significant bits of P.
     constexpr int NPF = 8 / VEC;
-    F pf[NPF];
+    constexpr bool SPLIT = VEC == 8;
+    F pf[NPF], pl[NPF];
 #pragma unroll
     for (int f = 0; f < NPF; ++f)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) pf[f][e] = from_f32<T>(p[f * VEC + e]);
+      for (int e = 0; e < VEC; ++e) {
+        const T hi = from_f32<T>(p[f * VEC + e]);
+        pf[f][e] = hi;
+        if (SPLIT) pl[f][e] = from_f32<T>(p[f * VEC + e] - to_f32(hi));
+      }
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
       const T *vp = &sm.vt[(dt * 16 + r16) * AttnSmem<T, DH>::VS + sc * 32 + 8 * g];
 #pragma unroll
-      for (int f = 0; f < NPF; ++f)
-        ws.o[dt] = Mma<T>::run(*reinterpret_cast<const F *>(vp + f * VEC), pf[f], ws.o[dt]);
+      for (int f = 0; f < NPF; ++f) {
+        const F vf = *reinterpret_cast<const F *>(vp + f * VEC);
+        ws.o[dt] = Mma<T>::run(vf, pf[f], ws.o[dt]);
+        if (SPLIT) ws.o[dt] = Mma<T>::run(vf, pl[f], ws.o[dt]);
+      }
     }
   }
 }

@@ -65,6 +65,22 @@ def assert_within_ulps(got, want, ulps, what):
         f"(got {got.flat[i]!r}, want {want.flat[i]!r})")
 
 
+def assert_bf16_rows_close(got, want, what):
+    """bf16 tensors produced by rounding fp32 (kernel) and fp64 (oracle)
+    values: the pre-rounding values differ by far less than the row scale, so
+    each element may differ by one rounding of its own (2 ulps) plus a small
+    fraction of the row's RMS (a rounding flip upstream, e.g. in a bf16 input
+    of the projection, moves a value by ~1e-4 of the row scale)."""
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+    tol = 2 * bf16_ulp(want) + 2.0 ** -8 * rms
+    err = np.abs(got - want) - tol
+    i = int(np.argmax(err)) if err.size else 0
+    assert err.size == 0 or err.max() <= 0, (
+        f"{what}: error exceeds 2 ulps + rms/256 at flat index {i} "
+        f"(got {got.flat[i]!r}, want {want.flat[i]!r})")
+
+
 def compare_ids(gpu_ids, ref_ids, excluded, what):
     """Bit-exact id comparison outside the excluded (flagged) positions.
     Returns the number of excluded positions."""

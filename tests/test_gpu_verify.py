@@ -73,8 +73,11 @@ def test_greedy_parity(bs, gamma, V, tdt):
     y = torch.from_numpy(y_np.astype(np.int32)).to(dev)
     gpu = _gpu_verify(bd.VERIFY_GREEDY, zt, y)
     ref = ov.verify_batch("greedy", zt_np, y_np)
-    n = _check(gpu, ref, f"greedy bs{bs} g{gamma} V{V}")
-    assert n <= max(1, bs // 4)
+    # greedy verification does no arithmetic on the logits (argmax with the
+    # lowest-id tie-break), so everything agrees exactly, flags included --
+    # bf16 logits often hold exact top-2 ties, which both sides flag
+    for g_, r_, name in zip(gpu, ref, ("tokens", "tau", "flags")):
+        assert np.array_equal(g_, r_), f"greedy bs{bs} g{gamma} V{V}: {name} differ"
     # planted prefixes give every tau in 1..gamma+1
     assert sorted(set(gpu[1].tolist())) == sorted(set(ref[1].tolist()))
 
