@@ -91,7 +91,10 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int max_ctx, int pairs) {
   const long want = ((long)max_ctx * pairs + 2047) / 2048;
-  int split = (int)std::max<long>(128, (want + 63) / 64 * 64);
+  // at most 128 splits (the merge kernel stages one weight per split)
+  const long floor_split = std::max<long>(128, ((long)max_ctx + 127) / 128);
+  int split = (int)std::max<long>(floor_split, (want + 63) / 64 * 64);
+  split = (split + 63) / 64 * 64;
   AttnPlan p;
   p.split = split;
   p.nsplit = std::max(1, (max_ctx + split - 1) / split);
@@ -413,7 +416,8 @@ int dstill_verify_workspace_bytes(int32_t bs, int32_t gamma, int32_t vocab, size
   if (!bytes) return fail(DSTILL_EINVAL, "bytes is null");
   if (bs < 0 || gamma < 1 || gamma > 63 || vocab < 2)
     return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= gamma <= 63, vocab >= 2");
-  *bytes = verify_ws_bytes(bs, gamma, verify_plan_splits(vocab));
+  *bytes = verify_ws_bytes(bs, gamma, verify_plan_splits(bs * (gamma + 1), vocab),
+                           verify_plan_splits(bs, vocab));
   return DSTILL_OK;
 }
 
@@ -438,8 +442,9 @@ int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float 
     if (!(temperature > 0.f)) return fail(DSTILL_EINVAL, "temperature must be > 0");
   }
   if (cycle >> 56) return fail(DSTILL_EINVAL, "cycle must be < 2^56");
-  const int nsplit = verify_plan_splits(vocab);
-  const size_t need = verify_ws_bytes(bs, gamma, nsplit);
+  const int nsplit = verify_plan_splits(bs * (gamma + 1), vocab);
+  const int nsamp = verify_plan_splits(bs, vocab);
+  const size_t need = verify_ws_bytes(bs, gamma, nsplit, nsamp);
   if (ws_bytes < need) return fail(DSTILL_EWORKSPACE, "verify needs %zu workspace bytes", need);
   VerifyArgs a;
   a.mode = mode; a.bs = bs; a.gamma = gamma; a.vocab = vocab; a.tdtype = target_dtype;
@@ -448,7 +453,7 @@ int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float 
   a.draft_ids = draft_ids; a.draft_lse = draft_lse; a.draft_logits = draft_logits;
   a.target = target_logits;
   a.tokens = out_tokens; a.tau = out_tau; a.flags = out_flags;
-  a.ws = ws; a.nsplit = nsplit;
+  a.ws = ws; a.nsplit = nsplit; a.nsamp = nsamp;
   launch_verify(a, (hipStream_t)stream);
   return hip_check("verify launch");
 }

@@ -202,27 +202,42 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of one (sequence-copy, head): weights
-// exp2(m_s - M), normalised by the merged sum.
+// exp2(m_s - M) / L with L = sum_s exp2(m_s - M) l_s, computed once per query
+// row into LDS, then a weighted sum of the split outputs, 4 values per thread.
+constexpr int COMBINE_MAX_SPLITS = 128;
+
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wts[16][COMBINE_MAX_SPLITS];
   const int bc = blockIdx.x, head = blockIdx.y;
   const int b = bc / a.C;
   const int S = a.eff_ctx[b];
   const int nvalid = max(1, (S + a.split - 1) / a.split);
   const int dh = a.dh;
-  for (int idx = threadIdx.x; idx < a.B * dh; idx += blockDim.x) {
-    const int s = idx / dh, d = idx % dh;
-    const long rec0 = (((long)bc * a.hq + head) * a.nsplit) * a.B + s;
+  const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B;  // record (sp, s) = rec0 + sp*B + s
+  for (int s = threadIdx.x; s < a.B; s += blockDim.x) {
     float M = -INFINITY;
-    for (int sp = 0; sp < nvalid; ++sp) M = fmaxf(M, a.mlpart[(rec0 + (long)sp * a.B) * 2]);
-    float L = 0.f, O = 0.f;
+    for (int sp = 0; sp < nvalid; ++sp) M = fmaxf(M, a.mlpart[(rec0 + (long)sp * a.B + s) * 2]);
+    float L = 0.f;
     for (int sp = 0; sp < nvalid; ++sp) {
-      const long rec = rec0 + (long)sp * a.B;
-      const float w = exp2f(a.mlpart[rec * 2] - M);
-      L += w * a.mlpart[rec * 2 + 1];
-      O += w * a.opart[rec * dh + d];
+      const long r = rec0 + (long)sp * a.B + s;
+      const float w = exp2f(a.mlpart[r * 2] - M);
+      wts[s][sp] = w;
+      L += w * a.mlpart[r * 2 + 1];
     }
-    ((T *)a.out)[((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d] = from_f32<T>(O / L);
+    const float inv = 1.0f / L;
+    for (int sp = 0; sp < nvalid; ++sp) wts[s][sp] *= inv;
+  }
+  __syncthreads();
+  const int nv4 = dh / 4;
+  for (int idx = threadIdx.x; idx < a.B * nv4; idx += blockDim.x) {
+    const int s = idx / nv4, d = (idx % nv4) * 4;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nvalid; ++sp)
+      o += wts[s][sp] * *reinterpret_cast<const f32x4 *>(a.opart + (rec0 + (long)sp * a.B + s) * dh + d);
+    T *dst = (T *)a.out + ((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e]);
   }
 }
 

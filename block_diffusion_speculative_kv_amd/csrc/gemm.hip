@@ -7,8 +7,14 @@
 // row and stores them as one 16-byte vector.  Partial sums over k-splits are
 // summed in a fixed order by the consumer (the fused epilogue kernels), which
 // keeps results deterministic.
+//
+// Two kernels: with up to 64 rows the projection streams its weight once
+// (HBM-bound) and every MFMA operand fragment is loaded straight from global
+// memory into registers; with more rows (bf16) the 128 x 128 LDS-tiled main
+// loop of mma_tile.hpp re-uses each staged weight tile across 128 rows.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mma_tile.hpp"
 
 namespace dstill {
 
@@ -87,6 +93,59 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
   }
 }
 
+// LDS-tiled path: 128 x 128 blocks, k-split over stages of 64.
+constexpr int LDS_NW = 4, LDS_MW = 4;
+
+__global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
+                                                        const bf16 *__restrict__ W, long ldw,
+                                                        float *__restrict__ out, int M, int N,
+                                                        int nst, int st_per_split, int nnb,
+                                                        int nmb) {
+  constexpr int NW = LDS_NW, MW = LDS_MW;
+  constexpr int BN = 32 * NW, BM = 32 * MW;
+  __shared__ TileSmem<NW, MW> sm;
+  int nb, mb;
+  xcd_block(blockIdx.x, nmb, &nb, &mb);
+  if (nb >= nnb) return;
+  const int s0 = blockIdx.y * st_per_split;
+  const int s1 = min(s0 + st_per_split, nst);
+  const int n0 = nb * BN, m0 = mb * BM;
+  TileLoader<NW, MW> ld;
+  ld.init([&](int r) { return W + (long)min(n0 + r, N - 1) * ldw; },
+          [&](int r) { return X + (long)min(m0 + r, M - 1) * ldx; }, (long)s0 * TK);
+  f32x4 acc[NW][MW];
+  tile_mainloop<NW, MW, false>(sm, ld, s1 - s0, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wn = wave & 1, wm = wave >> 1;
+  float *o = out + (long)blockIdx.y * M * N;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int n = n0 + wn * 16 * NW + 16 * i + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < MW; ++j) {
+      const int m = m0 + wm * 16 * MW + 16 * j + r16;
+      if (m < M) *reinterpret_cast<f32x4 *>(o + (long)m * N + n) = acc[i][j];
+    }
+  }
+}
+
+static bool use_lds(int M, int K, int dtype) { return dtype == 1 && M > 64 && K % TK == 0; }
+
+static void lds_geometry(int M, int N, int K, int ncu, int *nnb, int *nmb, int *nst,
+                         int *splits, int *per) {
+  constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
+  *nnb = (N + BN - 1) / BN;
+  *nmb = (M + BM - 1) / BM;
+  *nst = K / TK;
+  const long tiles = (long)*nnb * *nmb;
+  int s = (int)((2L * ncu + tiles - 1) / tiles);
+  s = max(1, min(s, *nst / 4));
+  *per = (*nst + s - 1) / s;
+  *splits = (*nst + *per - 1) / *per;
+}
+
 // Host-side plan: wave tile of NTW x MTW 16x16 tiles, 4 waves along N, and a
 // k-split that gives the launch at least ~2 workgroups per compute unit.
 template <typename T, int NTW, int MTW>
@@ -105,6 +164,11 @@ static void launch_tile(const GemmArgs &a, hipStream_t st) {
 // Chooses the wave tile from M and the number of k-splits; returns the split
 // count the output buffer must hold.
 int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
+  if (use_lds(M, K, dtype)) {
+    int nnb, nmb, nst, splits, per;
+    lds_geometry(M, N, K, num_cu, &nnb, &nmb, &nst, &splits, &per);
+    return splits;
+  }
   const int KW = dtype == 1 ? 32 : 16;
   const int nks = K / KW;
   int ntw, mtw;
@@ -140,6 +204,16 @@ static void launch_typed(const GemmArgs &a, hipStream_t st) {
 }
 
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
+  if (use_lds(a.M, a.K, a.dtype)) {
+    constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
+    const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / TK;
+    const int per = (nst + a.splits - 1) / a.splits;
+    const int nnb8 = (nnb + 7) / 8 * 8;
+    hipLaunchKernelGGL(gemm_lds_partial, dim3(nnb8 * nmb, a.splits), dim3(256), 0, st,
+                       (const bf16 *)a.X, a.ldx, (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst,
+                       per, nnb, nmb);
+    return;
+  }
   if (a.dtype == 1) launch_typed<bf16>(a, st);
   else launch_typed<float>(a, st);
 }

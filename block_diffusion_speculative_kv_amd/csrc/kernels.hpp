@@ -96,10 +96,12 @@ struct VerifyArgs {
   int32_t *tokens, *tau;
   uint32_t *flags;
   void *ws;
-  int nsplit;          // vocabulary splits per row
+  int nsplit;          // vocabulary splits per target row
+  int nsamp;           // vocabulary splits of the residual / bonus draw
 };
-int verify_plan_splits(int vocab);
-size_t verify_ws_bytes(int bs, int gamma, int nsplit);
+// splits of a vocabulary-wide pass over `rows` rows
+int verify_plan_splits(int rows, int vocab);
+size_t verify_ws_bytes(int bs, int gamma, int nsplit, int nsamp);
 void launch_verify(const VerifyArgs &a, hipStream_t st);
 
 }  // namespace dstill

@@ -17,6 +17,11 @@
 // are permuted so that lane group g of a wave holds the 8 consecutive ids
 // 8g .. 8g+7 of a 32-id span: exactly one Philox4x64-10 block.
 //
+// Two main loops: up to 64 rows the weight is streamed once with fragments
+// loaded straight into registers (HBM-bound); with more rows (bf16) the
+// 128 x 128 LDS-tiled loop of mma_tile.hpp re-uses each staged weight tile
+// across 128 rows.  Both end in the same per-lane reduction epilogue.
+//
 // Launch: the row blocks of one vocabulary block are placed on the same XCD
 // (workgroup i runs on XCD i mod 8) and next to each other in dispatch order,
 // so when there are several row blocks they read the weight tile through the
@@ -25,13 +30,17 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mma_tile.hpp"
 
 namespace dstill {
 
-constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup (64 per wave)
+constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
+constexpr int HEAD_NW = 4, HEAD_MW = 4;  // LDS path: 128 ids x 128 rows per workgroup
+constexpr int HEAD_VB_LDS = 32 * HEAD_NW;
 constexpr int NXCD = 8;
 
-int head_vocab_block() { return HEAD_VB; }
+// Smallest vocabulary block of any path: sizes the partial-record workspace.
+int head_vocab_block() { return HEAD_VB_LDS; }
 
 struct RowStat {
   ArgTop2 arg;
@@ -66,6 +75,87 @@ __device__ __forceinline__ RowStat rowstat_shfl_xor(const RowStat &a, int o) {
   b.m = __shfl_xor(a.m, o, WAVE);
   b.s = __shfl_xor(a.s, o, WAVE);
   return rowstat_merge(a, b);
+}
+
+// Reduction of one row's logits held by a lane: NP pairs of 8 consecutive ids
+// starting at vw + 32p + 8g.  Writes the logits if asked, draws the Gumbel
+// noise (one Philox block per 8 ids), and returns the lane's statistics
+// merged over the wave's four lane groups.
+template <int NP>
+__device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw, int g,
+                                                float (&zz)[NP][8]) {
+  const int V = a.vocab;
+  const float invT = 1.0f / a.temperature;
+  const bool gumbel = a.mode != 0;
+  const bool rvalid = r < a.rows;
+  const int seq = r / a.rows_per_seq, slot = r % a.rows_per_seq;
+  RowStat st;
+  st.arg.best = -INFINITY;
+  st.arg.second = -INFINITY;
+  st.arg.idx = 0x7fffffff;
+  st.zbest = 0.f;
+  st.zmax = -INFINITY;
+  st.m = -INFINITY;
+  st.s = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int v0 = vw + 32 * p + 8 * g;
+    float gn[8];
+    if (gumbel && rvalid && v0 < V) {
+      uint32_t raw[8];
+      if (a.mode == 2)
+        philox_block8(a.seed, 3u, 0, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
+      else
+        philox_block8(a.seed, 0u, (uint64_t)seq, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gn[e] = gumbel_of(raw[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gn[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int v = v0 + e;
+      if (v < V) {
+        const float z = zz[p][e];
+        const float sc = gumbel ? z * invT + gn[e] : z;
+        const bool win = sc > st.arg.best || (sc == st.arg.best && v < st.arg.idx);
+        if (win) st.zbest = z;
+        top2_push(st.arg, sc, v);
+        st.zmax = fmaxf(st.zmax, z);
+        st.m = fmaxf(st.m, z * invT);
+      }
+    }
+    if (a.logits && rvalid) {
+      float *lp = a.logits + (long)r * V + v0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v0 + e < V) lp[e] = zz[p][e];
+    }
+  }
+  if (st.m != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (vw + 32 * p + 8 * g + e < V) st.s += expf(zz[p][e] * invT - st.m);
+  }
+  st = rowstat_shfl_xor(st, 16);
+  st = rowstat_shfl_xor(st, 32);
+  return st;
+}
+
+__device__ __forceinline__ HeadPartial to_partial(const RowStat &st) {
+  HeadPartial hp;
+  hp.best = st.arg.best;
+  hp.second = st.arg.second;
+  hp.idx = st.arg.idx;
+  hp.zbest = st.zbest;
+  hp.zmax = st.zmax;
+  hp.m = st.m;
+  hp.s = st.s;
+  hp.pad = 0;
+  return hp;
 }
 
 template <typename T, int MTW>
@@ -133,71 +223,15 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
     }
   }
 
-  const float invT = 1.0f / a.temperature;
-  const bool gumbel = a.mode != 0;
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
     const int r = rbase + 16 * mt + r16;
-    const bool rvalid = r < a.rows;
-    const int seq = r / a.rows_per_seq, slot = r % a.rows_per_seq;
-    RowStat st;
-    st.arg.best = -INFINITY;
-    st.arg.second = -INFINITY;
-    st.arg.idx = 0x7fffffff;
-    st.zbest = 0.f;
-    st.zmax = -INFINITY;
-    st.m = -INFINITY;
-    st.s = 0.f;
     float zz[2][8];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][mt][e & 3];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int v0 = vw + 32 * p + 8 * g;
-      float gn[8];
-      if (gumbel && rvalid && v0 < V) {
-        uint32_t raw[8];
-        if (a.mode == 2)
-          philox_block8(a.seed, 3u, 0, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
-        else
-          philox_block8(a.seed, 0u, (uint64_t)seq, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gn[e] = gumbel_of(raw[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gn[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = v0 + e;
-        if (v < V) {
-          const float z = zz[p][e];
-          const float sc = gumbel ? z * invT + gn[e] : z;
-          const bool win = sc > st.arg.best || (sc == st.arg.best && v < st.arg.idx);
-          if (win) st.zbest = z;
-          top2_push(st.arg, sc, v);
-          st.zmax = fmaxf(st.zmax, z);
-          st.m = fmaxf(st.m, z * invT);
-        }
-      }
-      if (a.logits && rvalid) {
-        float *lp = a.logits + (long)r * V + v0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (v0 + e < V) lp[e] = zz[p][e];
-      }
-    }
-    if (st.m != -INFINITY) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (vw + 32 * p + 8 * g + e < V) st.s += expf(zz[p][e] * invT - st.m);
-    }
-    st = rowstat_shfl_xor(st, 16);
-    st = rowstat_shfl_xor(st, 32);
+    RowStat st = lane_rowstat<2>(a, r, vw, g, zz);
     if (g == 0) red[wave][16 * mt + r16] = st;
   }
   __syncthreads();
@@ -207,16 +241,54 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
     RowStat st = red[0][i];
 #pragma unroll
     for (int w = 1; w < 4; ++w) st = rowstat_merge(st, red[w][i]);
-    HeadPartial hp;
-    hp.best = st.arg.best;
-    hp.second = st.arg.second;
-    hp.idx = st.arg.idx;
-    hp.zbest = st.zbest;
-    hp.zmax = st.zmax;
-    hp.m = st.m;
-    hp.s = st.s;
-    hp.pad = 0;
-    a.part[(long)r * a.nvb + vb] = hp;
+    a.part[(long)r * a.nvb + vb] = to_partial(st);
+  }
+}
+
+// LDS-tiled variant for batch-scale row counts (bf16).
+__global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
+  constexpr int NW = HEAD_NW, MW = HEAD_MW;
+  constexpr int BN = 32 * NW, BM = 32 * MW;
+  __shared__ TileSmem<NW, MW> sm;
+  int vb, rb;
+  xcd_block(blockIdx.x, nmb, &vb, &rb);
+  if (vb >= a.nvb) return;
+  const int v0 = vb * BN, r0 = rb * BM;
+  const int V = a.vocab, d = a.d;
+  const bf16 *W = (const bf16 *)a.w;
+  const bf16 *H = (const bf16 *)a.hidden;
+  TileLoader<NW, MW> ld;
+  ld.init([&](int i) { return W + (long)min(v0 + i, V - 1) * d; },
+          [&](int i) {
+            const int r = min(r0 + i, a.rows - 1);
+            return H + ((long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq) * d;
+          },
+          0);
+  f32x4 acc[NW][MW];
+  tile_mainloop<NW, MW, true>(sm, ld, d / TK, acc);
+
+  // the main loop ended with a barrier: its LDS is free for the row records
+  RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm.w[0][0]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int vw = v0 + wn * 16 * NW;
+#pragma unroll
+  for (int mt = 0; mt < MW; ++mt) {
+    const int rl = wm * 16 * MW + 16 * mt + r16;
+    float zz[NW / 2][8];
+#pragma unroll
+    for (int p = 0; p < NW / 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][mt][e & 3];
+    RowStat st = lane_rowstat<NW / 2>(a, r0 + rl, vw, g, zz);
+    if (g == 0) red[wn][rl] = st;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < BM; i += blockDim.x) {
+    const int r = r0 + i;
+    if (r >= a.rows) continue;
+    a.part[(long)r * a.nvb + vb] = to_partial(rowstat_merge(red[0][i], red[1][i]));
   }
 }
 
@@ -294,10 +366,20 @@ static void launch_rows(const HeadArgs &a, hipStream_t st) {
   else launch_typed<T, 4>(a, st);
 }
 
-void launch_lm_head(const HeadArgs &a, hipStream_t st) {
-  if (a.rows == 0) return;
-  if (a.dtype == 1) launch_rows<bf16>(a, st);
-  else launch_rows<float>(a, st);
+void launch_lm_head(const HeadArgs &args, hipStream_t st) {
+  if (args.rows == 0) return;
+  HeadArgs a = args;
+  if (a.dtype == 1 && a.rows > 64 && a.d % TK == 0) {
+    constexpr int BM = 32 * HEAD_MW;
+    a.nvb = (a.vocab + HEAD_VB_LDS - 1) / HEAD_VB_LDS;
+    const int nmb = (a.rows + BM - 1) / BM;
+    const int nvb8 = (a.nvb + NXCD - 1) / NXCD * NXCD;
+    hipLaunchKernelGGL(lm_head_lds_kernel, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
+  } else {
+    a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;
+    if (a.dtype == 1) launch_rows<bf16>(a, st);
+    else launch_rows<float>(a, st);
+  }
   hipLaunchKernelGGL(lm_combine_kernel, dim3(a.rows), dim3(64), 0, st, a);
 }
 

@@ -62,12 +62,13 @@ struct VerifyWs {
   VRowPart *rowpart;   // [bs*(gamma+1)][nsplit]
   double *lse_t;       // [bs*(gamma+1)]
   int *kstar;          // [bs]
-  VSampPart *samp;     // [bs][nsplit]
+  VSampPart *samp;     // [bs][nsamp]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline VerifyWs carve(void *ws, int bs, int gamma, int nsplit) {
+  // (the sampling records come last, so their count does not move the rest)
   char *p = (char *)ws;
   VerifyWs w;
   const size_t rows = (size_t)bs * (gamma + 1);
@@ -81,21 +82,42 @@ __host__ __device__ inline VerifyWs carve(void *ws, int bs, int gamma, int nspli
   return w;
 }
 
-size_t verify_ws_bytes(int bs, int gamma, int nsplit) {
+size_t verify_ws_bytes(int bs, int gamma, int nsplit, int nsamp) {
   const size_t rows = (size_t)bs * (gamma + 1);
   return align256(rows * nsplit * sizeof(VRowPart)) + align256(rows * sizeof(double)) +
-         align256((size_t)bs * sizeof(int)) + align256((size_t)bs * nsplit * sizeof(VSampPart));
+         align256((size_t)bs * sizeof(int)) + align256((size_t)bs * nsamp * sizeof(VSampPart));
 }
 
-int verify_plan_splits(int vocab) {
-  // about 4K ids per split, at most 64 splits
-  int n = (vocab + 4095) / 4096;
-  return n < 1 ? 1 : (n > 64 ? 64 : n);
+int verify_plan_splits(int rows_, int vocab) {
+  // about 1024 workgroups over the rows, at least 2048 ids each, at most 64
+  const long rows = rows_ < 1 ? 1 : rows_;
+  long n = (1024 + rows - 1) / rows;
+  const long most = (vocab + 2047) / 2048;
+  if (n > most) n = most;
+  if (n > 64) n = 64;
+  return n < 1 ? 1 : (int)n;
 }
 
 __device__ __forceinline__ int split_chunk(int vocab, int nsplit) {
   const int c = (vocab + nsplit - 1) / nsplit;
   return (c + 7) & ~7;
+}
+
+// Eight consecutive logits starting at p (16-byte aligned for bf16 rows of
+// length % 8 == 0, two 16-byte loads for fp32).
+__device__ __forceinline__ void ld8(const bf16 *p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+}
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
 }
 
 __device__ __forceinline__ float ld(const float *p, long i) { return p[i]; }
@@ -118,9 +140,8 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
   float m = -INFINITY;
   double s = 0.0;
   int bad = 0;
-  for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) {
-    const float x = ld(z, v);
-    if (!isfinite(x)) { bad = 1; continue; }
+  auto push = [&](float x, int v) {
+    if (!isfinite(x)) { bad = 1; return; }
     top2_push(arg, x, v);
     const float y = x * invT;
     if (y > m) {
@@ -129,6 +150,17 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
     } else {
       s += (double)expf(y - m);
     }
+  };
+  if ((V & 7) == 0) {
+    // 8 consecutive ids per thread per step (v0 and v1 are multiples of 8)
+    for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * blockDim.x) {
+      float x[8];
+      ld8(z + v, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) push(x[e], v + e);
+    }
+  } else {
+    for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) push(ld(z, v), v);
   }
   // wave merge
   for (int o = 32; o > 0; o >>= 1) {
@@ -274,7 +306,7 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
   const TT *zt = (const TT *)a.target + trow * V;
   const float *zd = bonus ? nullptr : a.draft_logits + ((long)b * G + ks) * V;
   const double T = (double)a.temperature;
-  const int chunk = split_chunk(V, a.nsplit);
+  const int chunk = split_chunk(V, a.nsamp);
   const int v0 = sp * chunk, v1 = min(v0 + chunk, V);
   D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
   int any_r = 0, bad = 0;
@@ -329,7 +361,7 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
       t.any_r |= u.any_r;
       t.bad |= u.bad;
     }
-    w.samp[(long)b * a.nsplit + sp] = t;
+    w.samp[(long)b * a.nsamp + sp] = t;
   }
 }
 
@@ -340,8 +372,8 @@ __global__ __launch_bounds__(64) void vfinish_kernel(VerifyArgs a, VerifyWs w) {
   const int ks = w.kstar[b];
   D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
   int any_r = 0, bad = 0;
-  for (int sp = 0; sp < a.nsplit; ++sp) {
-    const VSampPart p = w.samp[(long)b * a.nsplit + sp];
+  for (int sp = 0; sp < a.nsamp; ++sp) {
+    const VSampPart p = w.samp[(long)b * a.nsamp + sp];
     rr = d2_merge(rr, D2{p.best_r, p.second_r, p.idx_r});
     pp = d2_merge(pp, D2{p.best_p, p.second_p, p.idx_p});
     any_r |= p.any_r;
@@ -371,7 +403,7 @@ static void launch_typed(const VerifyArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(vrow_kernel<TT>, dim3(rows, a.nsplit), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(vdecide_kernel<TT>, dim3(a.bs), dim3(64), 0, st, a, w);
   if (a.mode == 1) {
-    hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsplit), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsamp), dim3(256), 0, st, a, w);
     hipLaunchKernelGGL(vfinish_kernel, dim3(a.bs), dim3(64), 0, st, a, w);
   }
 }

@@ -5,13 +5,15 @@ N(0, 1) K/V standing in for injected rows) and the same block tokens.
 
 Tolerances.  The tiny fp32 workload must match to 1e-5 relative.  bf16
 drafters are compared on the LM-head logits of the final hidden state: 2e-2
-absolute for the 2-layer reduced drafter and for one full 8B-shaped layer.  A
-chain of bf16 rounding points amplifies any fp32-sized difference into
-rounding flips that the oracle cannot mirror; nudging the fp64 oracle's own
-norm inputs by 2^-24 relative moves its 5-layer 8B-shaped logits by ~0.03
-(and one layer's by ~0.01).  So the 5-layer chain is held to a bound derived
-in the test from that same experiment: the GPU may differ from the oracle by
-at most 3x what the oracle differs from itself under that perturbation.
+absolute for the 2-layer reduced drafter.  A chain of bf16 rounding points
+amplifies any fp32-sized difference into rounding flips that the oracle
+cannot mirror; nudging the fp64 oracle's own norm inputs by 2^-24 relative
+moves its 8B-shaped logits by ~0.01 (one layer) and ~0.03 (five layers), and
+the kernel's fp32 sums carry more than that (the attention output is a sum of
+~1-sized terms that cancels to ~0.016, so its fp32 relative error is ~2e-4
+before rounding).  So the 8B-shaped drafters are held to a bound derived in
+the test from that experiment: the GPU may differ from the oracle by at most
+max(2e-2, 3x what the oracle differs from itself under the perturbation).
 
 Cases: the tiny workload; a reduced bf16 drafter with ragged contexts (37,
 300, 1029: several 64-key chunks, several context splits and ragged tails),
@@ -159,8 +161,11 @@ def test_q8b_one_layer_ctx4096():
     dev, w, dr, kv = _setup(cfg, 4096)
     tok, out, flags = _draft(cfg, dr, kv, dev, [4096], 4096)
     w_np = to_np(w)
-    want = _oracle(cfg, w_np, kv, tok, [4096])
-    _compare(cfg, w_np, out, want, "q8b one layer")
+    want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, [4096])
+    err = _logit_err(cfg, w_np, out, want)
+    print(f"q8b one layer: GPU-oracle logit error {err.max():.3e}, "
+          f"oracle self-divergence {self_div:.3e}")
+    assert err.max() <= max(2e-2, 3 * self_div)
     assert flags.cpu().tolist() == [0]
 
 
