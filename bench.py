@@ -86,7 +86,7 @@ def _cpu_baseline(cfg, cyc, budget_s):
     done, t_total = 0, 0.0
     for b, S in enumerate(cfg["ctx_lens"]):
         ck = [host(k[b]) for k in cyc.kv.k]
-        cv = [host(v[b]) for v in cyc.kv.v]
+        cv = [host(v[b]).transpose(0, 2, 1).copy() for v in cyc.kv.v]   # d-major -> [h, pos, dh]
         t0 = time.perf_counter()
         ks, vs = od.inject_rows(feats[b * n_new:(b + 1) * n_new], np.arange(S - n_new, S))
         for l in range(cfg["n_layers"]):

@@ -92,13 +92,16 @@ class Drafter:
 
     # -- memory helpers ------------------------------------------------------
     def kv_cache(self, max_batch: int, cap: int, device="cuda"):
-        """Allocate (zeroed) per-layer K and V caches [max_batch, h_kv, cap, dh]."""
+        """Allocate (zeroed) per-layer caches: K [max_batch, h_kv, cap, dh] and
+        V d-major [max_batch, h_kv, dh, cap] (cap a multiple of 8)."""
         n = ctypes.c_size_t()
         _lib.check(self.lib.dstill_kv_bytes(ctypes.byref(self._cfg_c), max_batch, cap,
                                             ctypes.byref(n)), "dstill_kv_bytes")
-        shape = (max_batch, self.cfg["n_kv_heads"], cap, self.cfg["head_dim"])
-        ks = [torch.zeros(shape, dtype=self.tdtype, device=device) for _ in range(self.cfg["n_layers"])]
-        vs = [torch.zeros(shape, dtype=self.tdtype, device=device) for _ in range(self.cfg["n_layers"])]
+        hk, dh = self.cfg["n_kv_heads"], self.cfg["head_dim"]
+        ks = [torch.zeros((max_batch, hk, cap, dh), dtype=self.tdtype, device=device)
+              for _ in range(self.cfg["n_layers"])]
+        vs = [torch.zeros((max_batch, hk, dh, cap), dtype=self.tdtype, device=device)
+              for _ in range(self.cfg["n_layers"])]
         assert ks[0].numel() * ks[0].element_size() == n.value
         return KVCache(ks, vs)
 
@@ -149,7 +152,8 @@ class Drafter:
 
 
 class KVCache:
-    """Per-layer K and V cache tensors plus the C view the library reads."""
+    """Per-layer K [max_batch, h_kv, cap, dh] and d-major V [max_batch, h_kv,
+    dh, cap] cache tensors plus the C view the library reads."""
 
     def __init__(self, ks, vs):
         self.k, self.v = ks, vs

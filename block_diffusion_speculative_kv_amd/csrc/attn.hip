@@ -7,11 +7,15 @@
 // scaled by 1/sqrt(dh), through a softmax over all S_b + B keys.
 //
 // Work decomposition ("split context"): one workgroup per (split, kv head,
-// sequence-copy).  Its `group` waves each own one query head of the GQA
+// sequence-copy).  Its first `group` waves each own one query head of the GQA
 // group, i.e. B <= 16 query rows (one 16-row MFMA tile).  The workgroup walks
-// its context range in chunks of 64 keys staged in LDS (K row-major, V
-// transposed), computes S^T = K Q^T and O^T = V^T P^T on the matrix cores and
-// keeps an online softmax per query; split 0 also takes the block keys.  The
+// its context range in chunks of 64 keys, computes S^T = K Q^T and
+// O^T = V^T P^T on the matrix cores and keeps an online softmax per query;
+// split 0 also takes the block keys.  Chunks are pipelined: the next chunk's
+// K and V^T are loaded into registers while the waves work on the current
+// one out of LDS, then written to the other LDS buffer (one barrier per
+// chunk).  The V cache is d-major ([dh][cap] per sequence and head), so V^T
+// of a chunk is a plain coalesced copy.  The
 // partial (m, l, O) of every split is merged by attn_combine with the
 // log-sum-exp rule, which reproduces the single softmax up to rounding.
 //
@@ -19,10 +23,8 @@
 // with the key rows of each 32-key sub-chunk permuted so that tile t row
 // 4g + i is key 8g + 4t + i, the 8 consecutive keys 8g .. 8g+7 (g = l / 16).
 // Those 8 probabilities are exactly that lane's B fragment of P^T, and the
-// matching A fragment of V^T is 8 consecutive keys of one transposed V row.
-// bf16 probabilities go through P.V as a hi + lo pair of bf16 fragments, so
-// the product keeps about 16 significant bits of P (fp32 accumulation).
-// The row max/sum over a query's keys is then a reduction over the four lane
+// matching A fragment of V^T is 8 consecutive keys of one V^T row.  The row
+// max/sum over a query's keys is then a reduction over the four lane
 // groups: two xor-shuffles (16, 32).
 #include <math.h>
 
@@ -32,36 +34,61 @@
 namespace dstill {
 
 constexpr int ATT_KC = 64;  // keys per LDS chunk
+constexpr int ATT_VBS = 16;  // key stride of the block V^T workspace
 
+// Two LDS buffers of one chunk: K row-major [key][dh], V^T [dh][key]; rows
+// padded by 16 bytes so fragment reads of 16 rows hit distinct banks.
 template <typename T, int DH>
 struct AttnSmem {
   static constexpr int VEC = Mma<T>::VEC;
-  static constexpr int KS = DH + VEC;      // K row stride (elements), 16-byte pad
-  static constexpr int VS = ATT_KC + VEC;  // V^T row stride
-  T k[ATT_KC * KS];
-  T vt[DH * VS];
+  static constexpr int KS = DH + VEC;
+  static constexpr int VS = ATT_KC + VEC;
+  T k[2][ATT_KC * KS];
+  T vt[2][DH * VS];
 };
 
-// Stage `nk` keys (rows 0..nk-1 of src, row stride `stride` elements) into
-// LDS; rows nk..63 are zero-filled so no stale value can reach P*V.
-template <typename T, int DH>
-__device__ __forceinline__ void stage_chunk(AttnSmem<T, DH> &sm, const T *__restrict__ ksrc,
-                                            const T *__restrict__ vsrc, long stride, int nk) {
-  constexpr int VEC = Mma<T>::VEC;
-  constexpr int VPR = DH / VEC;  // vectors per row
+// Copies one chunk global -> registers (issued early) -> LDS (after the
+// current chunk's compute).  K rows are contiguous dh-vectors; the V cache is
+// d-major, so a V^T row of the chunk is 64 consecutive keys of one d.
+// Positions at or beyond nk are zero-filled, so no stale value reaches P.V.
+template <typename T, int DH, int NTHR>
+struct ChunkLoader {
   typedef typename Mma<T>::frag F;
-  for (int idx = threadIdx.x; idx < ATT_KC * VPR; idx += blockDim.x) {
-    const int key = idx / VPR, c = (idx % VPR) * VEC;
-    F kv = zero_frag<T>(), vv = zero_frag<T>();
-    if (key < nk) {
-      kv = load_frag<T>(ksrc + key * stride + c);
-      vv = load_frag<T>(vsrc + key * stride + c);
-    }
-    *reinterpret_cast<F *>(&sm.k[key * AttnSmem<T, DH>::KS + c]) = kv;
+  static constexpr int VEC = Mma<T>::VEC;
+  static constexpr int NV = ATT_KC * DH / VEC / NTHR;  // vectors of K (and of V) per thread
+  F kr[NV], vr[NV];
+  int nk;
+
+  __device__ __forceinline__ void load(const T *__restrict__ ksrc, long kstride,
+                                       const T *__restrict__ vsrc, long vstride, int nkeys) {
+    nk = nkeys;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) sm.vt[(c + e) * AttnSmem<T, DH>::VS + key] = vv[e];
+    for (int i = 0; i < NV; ++i) {
+      const int item = threadIdx.x + NTHR * i;
+      const int key = item / (DH / VEC), c = (item % (DH / VEC)) * VEC;
+      kr[i] = key < nk ? load_frag<T>(ksrc + key * kstride + c) : zero_frag<T>();
+      const int d = item / (ATT_KC / VEC), kc = (item % (ATT_KC / VEC)) * VEC;
+      if (kc < nk) {
+        vr[i] = load_frag<T>(vsrc + d * vstride + kc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (kc + e >= nk) vr[i][e] = T(0.0f);
+      } else {
+        vr[i] = zero_frag<T>();
+      }
+    }
   }
-}
+  __device__ __forceinline__ void store(AttnSmem<T, DH> &sm, int buf) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int item = threadIdx.x + NTHR * i;
+      const int key = item / (DH / VEC), c = (item % (DH / VEC)) * VEC;
+      *reinterpret_cast<F *>(&sm.k[buf][key * AttnSmem<T, DH>::KS + c]) = kr[i];
+      const int d = item / (ATT_KC / VEC), kc = (item % (ATT_KC / VEC)) * VEC;
+      *reinterpret_cast<F *>(&sm.vt[buf][d * AttnSmem<T, DH>::VS + kc]) = vr[i];
+    }
+  }
+};
 
 template <typename T, int DH>
 struct WaveState {
@@ -71,10 +98,12 @@ struct WaveState {
 
 // One wave's pass over a staged chunk holding `nk` valid keys.
 template <typename T, int DH>
-__device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
+__device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
+                                             const T *__restrict__ vt_lds,
                                              const typename Mma<T>::frag *qf, int nk,
                                              float scale_log2, WaveState<T, DH> &ws) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
+  constexpr int KS = AttnSmem<T, DH>::KS, VS = AttnSmem<T, DH>::VS;
   typedef typename Mma<T>::frag F;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   for (int sc = 0; sc * 32 < nk; ++sc) {
@@ -82,7 +111,7 @@ __device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int krow = sc * 32 + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-      const T *kp = &sm.k[krow * AttnSmem<T, DH>::KS + VEC * g];
+      const T *kp = ks_lds + krow * KS + VEC * g;
 #pragma unroll
       for (int ks = 0; ks < DH / KW; ++ks)
         s[t] = Mma<T>::run(*reinterpret_cast<const F *>(kp + ks * KW), qf[ks], s[t]);
@@ -111,9 +140,9 @@ __device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
       ws.l += p[e];
     }
     ws.m = mnew;
-    // P^T fragments: bf16 packs all 8 keys in one fragment; fp32 uses two.
-    // In bf16 the probabilities are carried as a hi + lo pair (lo = the
-    // rounding residual of hi), so P.V keeps ~16 significant bits of P.
+    // P^T fragments: bf16 packs all 8 keys in one fragment, carried as a
+    // hi + lo pair (lo = the rounding residual of hi) so P.V keeps ~16
+    // significant bits of P; fp32 uses two exact fragments.
     constexpr int NPF = 8 / VEC;
     constexpr bool SPLIT = VEC == 8;
     F pf[NPF], pl[NPF];
@@ -127,7 +156,7 @@ __device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
       }
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
-      const T *vp = &sm.vt[(dt * 16 + r16) * AttnSmem<T, DH>::VS + sc * 32 + 8 * g];
+      const T *vp = vt_lds + (dt * 16 + r16) * VS + sc * 32 + 8 * g;
 #pragma unroll
       for (int f = 0; f < NPF; ++f) {
         const F vf = *reinterpret_cast<const F *>(vp + f * VEC);
@@ -138,8 +167,8 @@ __device__ __forceinline__ void attend_chunk(const AttnSmem<T, DH> &sm,
   }
 }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
+template <typename T, int DH, int NTHR>
+__global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
   typedef typename Mma<T>::frag F;
   __shared__ AttnSmem<T, DH> sm;
@@ -152,14 +181,15 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
   const int group = a.hq / a.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int head = h * group + wave;
+  const bool active = wave < group;  // spare waves only help staging
+  const int head = h * group + (active ? wave : 0);
 
   // Q^T fragments (B operand): query row r16 of this head.
   F qf[DH / KW];
   const T *qrow = (const T *)a.q + ((long)bc * a.B + r16) * a.hq * DH + head * DH + VEC * g;
 #pragma unroll
   for (int ks = 0; ks < DH / KW; ++ks)
-    qf[ks] = r16 < a.B ? load_frag<T>(qrow + ks * KW) : zero_frag<T>();
+    qf[ks] = (active && r16 < a.B) ? load_frag<T>(qrow + ks * KW) : zero_frag<T>();
 
   WaveState<T, DH> st;
   st.m = -INFINITY;
@@ -168,22 +198,34 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
   for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float scale_log2 = a.scale * 1.4426950408889634f;
 
-  const long cache_row0 = ((long)b * a.hkv + h) * a.cap;
-  for (int k0 = k_beg; k0 < k_end; k0 += ATT_KC) {
-    const int nk = min(ATT_KC, k_end - k0);
+  // chunks: the context range, then (split 0 only) the B block keys
+  const int nctx = k_end > k_beg ? (k_end - k_beg + ATT_KC - 1) / ATT_KC : 0;
+  const int nchunk = nctx + (sp == 0 ? 1 : 0);
+  const T *kcache = (const T *)a.kc + ((long)b * a.hkv + h) * a.cap * DH;
+  const T *vcache = (const T *)a.vc + ((long)b * a.hkv + h) * DH * a.cap;
+  const T *kblock = (const T *)a.kb + (long)bc * a.B * a.hkv * DH + (long)h * DH;
+  const T *vblock = (const T *)a.vb + ((long)bc * a.hkv + h) * DH * ATT_VBS;
+  ChunkLoader<T, DH, NTHR> ld;
+  auto issue = [&](int c) {
+    if (c < nctx) {
+      const int k0 = k_beg + c * ATT_KC;
+      ld.load(kcache + (long)k0 * DH, DH, vcache + k0, a.cap, min(ATT_KC, k_end - k0));
+    } else {
+      ld.load(kblock, (long)a.hkv * DH, vblock, ATT_VBS, a.B);
+    }
+  };
+  issue(0);
+  ld.store(sm, 0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int cur = c & 1;
+    const int nk = ld.nk;
+    if (c + 1 < nchunk) issue(c + 1);
+    if (active) attend_chunk<T, DH>(sm.k[cur], sm.vt[cur], qf, nk, scale_log2, st);
+    if (c + 1 < nchunk) ld.store(sm, cur ^ 1);
     __syncthreads();
-    stage_chunk<T, DH>(sm, (const T *)a.kc + (cache_row0 + k0) * DH,
-                       (const T *)a.vc + (cache_row0 + k0) * DH, DH, nk);
-    __syncthreads();
-    attend_chunk<T, DH>(sm, qf, nk, scale_log2, st);
   }
-  if (sp == 0) {
-    const long boff = ((long)bc * a.B) * a.hkv * DH + (long)h * DH;
-    __syncthreads();
-    stage_chunk<T, DH>(sm, (const T *)a.kb + boff, (const T *)a.vb + boff, (long)a.hkv * DH, a.B);
-    __syncthreads();
-    attend_chunk<T, DH>(sm, qf, a.B, scale_log2, st);
-  }
+  if (!active) return;
 
   // Row sum over the four lane groups, then the partial record.
   st.l += __shfl_xor(st.l, 16, WAVE);
@@ -241,11 +283,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+template <typename T, int DH, int NTHR>
+static void launch_nthr(const AttnArgs &a, hipStream_t st) {
+  dim3 grid(a.nsplit, a.hkv, a.bs * a.C);
+  hipLaunchKernelGGL((attn_split_kernel<T, DH, NTHR>), grid, dim3(NTHR), 0, st, a);
+}
+
 template <typename T, int DH>
 static void launch_typed(const AttnArgs &a, hipStream_t st) {
   const int group = a.hq / a.hkv;
-  dim3 grid(a.nsplit, a.hkv, a.bs * a.C);
-  hipLaunchKernelGGL((attn_split_kernel<T, DH>), grid, dim3(64 * group), 0, st, a);
+  if (group <= 4) launch_nthr<T, DH, 256>(a, st);
+  else if (group <= 8) launch_nthr<T, DH, 512>(a, st);
+  else launch_nthr<T, DH, 1024>(a, st);
   hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.bs * a.C, a.hq), dim3(256), 0, st, a);
 }
 
@@ -255,8 +304,7 @@ void launch_attention(const AttnArgs &a, hipStream_t st) {
     if (a.dh == 128) launch_typed<bf16, 128>(a, st);
     else launch_typed<bf16, 64>(a, st);
   } else {
-    if (a.dh == 128) launch_typed<float, 128>(a, st);
-    else launch_typed<float, 64>(a, st);
+    launch_typed<float, 64>(a, st);
   }
 }
 

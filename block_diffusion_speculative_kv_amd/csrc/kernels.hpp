@@ -48,9 +48,9 @@ struct AttnArgs {
   int dtype;
   const void *q;       // [bs*C*B, hq*dh]
   const void *kb;      // [bs*C*B, hkv*dh] block keys
-  const void *vb;      // [bs*C*B, hkv*dh] block values
+  const void *vb;      // [bs*C][hkv][dh][16] block values, d-major
   const void *kc;      // cache K of this layer [max_batch][hkv][cap][dh]
-  const void *vc;
+  const void *vc;      // cache V of this layer [max_batch][hkv][dh][cap]
   const int32_t *eff_ctx;  // [bs] clamped context lengths
   int bs, C, B, hq, hkv, dh, cap;
   int split;           // context keys per split (multiple of 64)

@@ -10,6 +10,9 @@
 //   pos * theta^(-2i/dh), computed in fp64 so that positions up to 2^20 keep
 //   full fp32 accuracy;
 //   SwiGLU: silu(gate) * up, silu(x) = x / (1 + exp(-x)).
+// Layouts: K is stored as dh-vectors ([cap][dh] per sequence and kv head),
+// V d-major ([dh][cap]; block V in the workspace as [dh][16]), which is the
+// layout the attention kernel's P.V operand reads.
 #include <math.h>
 
 #include "common.hpp"
@@ -189,12 +192,21 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(
       }
     }
   }
-  T *dst;
-  if (is_q) dst = q + (long)r * hq * dh + head * dh;
-  else if (is_k) dst = kb + (long)r * hkv * dh + (head - hq) * dh;
-  else dst = vb + (long)r * hkv * dh + (head - hq - hkv) * dh;
-  if (is_q || is_k)
-    head_norm_rope<T>(x1, x2, dh, qk_norm != 0, is_q ? q_norm : k_norm, eps, true, pos, theta);
+  if (!is_q && !is_k) {
+    // block V, d-major per (sequence-copy, kv head): [dh][16 key slots]
+    T *dst = vb + (((long)(r / block) * hkv + (head - hq - hkv)) * dh) * 16 + r % block;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = lane + 64 * i;
+      if (p < half) {
+        dst[(long)p * 16] = from_f32<T>(x1[i]);
+        dst[(long)(p + half) * 16] = from_f32<T>(x2[i]);
+      }
+    }
+    return;
+  }
+  T *dst = is_q ? q + (long)r * hq * dh + head * dh : kb + (long)r * hkv * dh + (head - hq) * dh;
+  head_norm_rope<T>(x1, x2, dh, qk_norm != 0, is_q ? q_norm : k_norm, eps, true, pos, theta);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
@@ -276,14 +288,16 @@ __global__ __launch_bounds__(64) void inject_post_kernel(
       }
     }
   }
+  // K cache rows are dh-vectors [cap][dh]; the V cache is d-major [dh][cap]
+  const long stride = is_k ? 1 : cap;
+  T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh : vc + ((long)sq * hkv + h) * dh * cap + ps;
   if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, true, ps, theta);
-  T *dst = (is_k ? kc : vc) + (((long)sq * hkv + h) * cap + ps) * dh;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
     if (p < half) {
-      dst[p] = from_f32<T>(x1[i]);
-      dst[p + half] = from_f32<T>(x2[i]);
+      dst[p * stride] = from_f32<T>(x1[i]);
+      dst[(p + half) * stride] = from_f32<T>(x2[i]);
     }
   }
 }

@@ -49,7 +49,7 @@ def _check(cfg, w, kv, feats, seq, pos, rows):
         K = to_np(kv.k[l])
         V = to_np(kv.v[l])
         gk = K[seq[rows], :, pos[rows]]          # [n, hkv, dh]
-        gv = V[seq[rows], :, pos[rows]]
+        gv = V[seq[rows], :, :, pos[rows]]       # V is d-major: [b, h, dh, pos]
         if cfg["dtype"] == "f32":
             assert_close_rel(gk, ks[l], 1e-5, f"K layer {l}")
             assert_close_rel(gv, vs[l], 1e-5, f"V layer {l}")
@@ -60,7 +60,7 @@ def _check(cfg, w, kv, feats, seq, pos, rows):
 
 def test_tiny_fp32():
     cfg = configs.get("tiny_fp32")
-    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 128, 130, 1)
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 128, 136, 1)
     _check(cfg, w, kv, feats, seq, pos, np.arange(128))
 
 
@@ -68,14 +68,14 @@ def test_small_bf16_with_skipped_rows():
     cfg = configs.small_bf16()
     n = 77
     invalid = (3, 10, 11)
-    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, n, 50, 3, invalid=invalid)
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, n, 56, 3, invalid=invalid)
     ok = np.array([i not in invalid for i in range(n)])
     _check(cfg, w, kv, feats, seq, pos, np.nonzero(ok)[0])
     # every cache row not named by a valid input row is still zero
     written = set(zip(seq[ok].tolist(), pos[ok].tolist()))
     K = kv.k[0].float().cpu().numpy()
     for b in range(3):
-        for p in range(50):
+        for p in range(56):
             if (b, p) not in written:
                 assert not K[b, :, p].any()
 
