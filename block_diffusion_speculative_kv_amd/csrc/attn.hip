@@ -49,8 +49,11 @@ struct AttnSmem {
 
 // Copies one chunk global -> registers (issued early) -> LDS (after the
 // current chunk's compute).  K rows are contiguous dh-vectors; the V cache is
-// d-major, so a V^T row of the chunk is 64 consecutive keys of one d.
-// Positions at or beyond nk are zero-filled, so no stale value reaches P.V.
+// d-major, so a V^T row of the chunk is 64 consecutive keys of one d.  Loads
+// are unconditional from clamped, in-bounds addresses (no branch, so nothing
+// waits on them until the store); keys at or beyond nk are masked at store
+// time: V to zero so no stale value reaches P.V, K left as is (its scores are
+// replaced by -inf).
 template <typename T, int DH, int NTHR>
 struct ChunkLoader {
   typedef typename Mma<T>::frag F;
@@ -65,26 +68,23 @@ struct ChunkLoader {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int item = threadIdx.x + NTHR * i;
-      const int key = item / (DH / VEC), c = (item % (DH / VEC)) * VEC;
-      kr[i] = key < nk ? load_frag<T>(ksrc + key * kstride + c) : zero_frag<T>();
+      const int key = min(item / (DH / VEC), nk - 1), c = (item % (DH / VEC)) * VEC;
+      kr[i] = load_frag<T>(ksrc + key * kstride + c);
       const int d = item / (ATT_KC / VEC), kc = (item % (ATT_KC / VEC)) * VEC;
-      if (kc < nk) {
-        vr[i] = load_frag<T>(vsrc + d * vstride + kc);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if (kc + e >= nk) vr[i][e] = T(0.0f);
-      } else {
-        vr[i] = zero_frag<T>();
-      }
+      // a vector starting below nk stays inside the row (rows hold a multiple of 8)
+      vr[i] = load_frag<T>(vsrc + d * vstride + (kc < nk ? kc : 0));
     }
   }
-  __device__ __forceinline__ void store(AttnSmem<T, DH> &sm, int buf) const {
+  __device__ __forceinline__ void store(AttnSmem<T, DH> &sm, int buf) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int item = threadIdx.x + NTHR * i;
       const int key = item / (DH / VEC), c = (item % (DH / VEC)) * VEC;
       *reinterpret_cast<F *>(&sm.k[buf][key * AttnSmem<T, DH>::KS + c]) = kr[i];
       const int d = item / (ATT_KC / VEC), kc = (item % (ATT_KC / VEC)) * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        if (kc + e >= nk) vr[i][e] = T(0.0f);
       *reinterpret_cast<F *>(&sm.vt[buf][d * AttnSmem<T, DH>::VS + kc]) = vr[i];
     }
   }
@@ -217,12 +217,15 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   issue(0);
   ld.store(sm, 0);
   __syncthreads();
+  int nk = ld.nk;
   for (int c = 0; c < nchunk; ++c) {
     const int cur = c & 1;
-    const int nk = ld.nk;
     if (c + 1 < nchunk) issue(c + 1);
     if (active) attend_chunk<T, DH>(sm.k[cur], sm.vt[cur], qf, nk, scale_log2, st);
-    if (c + 1 < nchunk) ld.store(sm, cur ^ 1);
+    if (c + 1 < nchunk) {
+      nk = ld.nk;
+      ld.store(sm, cur ^ 1);
+    }
     __syncthreads();
   }
   if (!active) return;
