@@ -82,9 +82,11 @@ struct ChunkLoader {
       const int key = item / (DH / VEC), c = (item % (DH / VEC)) * VEC;
       *reinterpret_cast<F *>(&sm.k[buf][key * AttnSmem<T, DH>::KS + c]) = kr[i];
       const int d = item / (ATT_KC / VEC), kc = (item % (ATT_KC / VEC)) * VEC;
+      if (nk < ATT_KC) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if (kc + e >= nk) vr[i][e] = T(0.0f);
+        for (int e = 0; e < VEC; ++e)
+          if (kc + e >= nk) vr[i][e] = T(0.0f);
+      }
       *reinterpret_cast<F *>(&sm.vt[buf][d * AttnSmem<T, DH>::VS + kc]) = vr[i];
     }
   }
@@ -96,63 +98,85 @@ struct WaveState {
   f32x4 o[DH / 16];
 };
 
-// One wave's pass over a staged chunk holding `nk` valid keys.
+// One wave's pass over a staged chunk holding `nk` valid keys (1..64), with
+// one online-softmax update for the whole chunk.  Scores stay in raw units
+// (m is the running max of raw scores); probabilities are
+// exp2(s * c - m * c) with c = log2(e) / sqrt(dh), one FMA and one v_exp_f32
+// each.  The accumulators are rescaled only when some query's max grows
+// (a wave-uniform branch), which after the first chunks is rare.
 template <typename T, int DH>
 __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
                                              const T *__restrict__ vt_lds,
-                                             const typename Mma<T>::frag *qf, int nk,
-                                             float scale_log2, WaveState<T, DH> &ws) {
+                                             const typename Mma<T>::frag *qf, int nk, float c,
+                                             WaveState<T, DH> &ws) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
   constexpr int KS = AttnSmem<T, DH>::KS, VS = AttnSmem<T, DH>::VS;
   typedef typename Mma<T>::frag F;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  for (int sc = 0; sc * 32 < nk; ++sc) {
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const int nsub = nk > 32 ? 2 : 1;  // 32-key sub-chunks holding a valid key
+  // S^T tiles: tile t covers sub-chunk t >> 1; lane holds keys
+  // 32 (t >> 1) + 8 g + 4 (t & 1) + i, i = 0..3
+  f32x4 s[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int krow = sc * 32 + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
+  for (int t = 0; t < 4; ++t) {
+    s[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if ((t >> 1) < nsub) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int krow = 32 * (t >> 1) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3);
       const T *kp = ks_lds + krow * KS + VEC * g;
 #pragma unroll
       for (int ks = 0; ks < DH / KW; ++ks)
         s[t] = Mma<T>::run(*reinterpret_cast<const F *>(kp + ks * KW), qf[ks], s[t]);
     }
-    float p[8];
-    float cmax = -INFINITY;
+  }
+  if (nk < ATT_KC) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = sc * 32 + 8 * g + 4 * t + i;
-        const float v = key < nk ? s[t][i] * scale_log2 : -INFINITY;
-        p[4 * t + i] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, WAVE));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, WAVE));
-    const float mnew = fmaxf(ws.m, cmax);
-    const float alpha = exp2f(ws.m - mnew);
+      for (int i = 0; i < 4; ++i)
+        if (32 * (t >> 1) + 8 * g + 4 * (t & 1) + i >= nk) s[t][i] = -INFINITY;
+  }
+  float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  cmax = fmaxf(cmax, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                           fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, WAVE));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, WAVE));
+  const float mnew = fmaxf(ws.m, cmax);
+  if (__any(mnew > ws.m)) {
+    const float alpha = __builtin_amdgcn_exp2f((ws.m - mnew) * c);
     ws.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) ws.o[dt] *= alpha;
+  }
+  ws.m = mnew;
+  const float mc = mnew * c;
+  float p[4][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(p[e] - mnew);
-      ws.l += p[e];
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[t][i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], c, -mc));
+      ws.l += p[t][i];
     }
-    ws.m = mnew;
-    // P^T fragments: bf16 packs all 8 keys in one fragment, carried as a
-    // hi + lo pair (lo = the rounding residual of hi) so P.V keeps ~16
-    // significant bits of P; fp32 uses two exact fragments.
-    constexpr int NPF = 8 / VEC;
-    constexpr bool SPLIT = VEC == 8;
+  // P^T fragments per sub-chunk: keys 8g .. 8g+7 are p[2sc][0..3], p[2sc+1][0..3].
+  // bf16 carries them as a hi + lo pair (lo = the rounding residual of hi) so
+  // P.V keeps ~16 significant bits of P; fp32 uses two exact fragments.
+  constexpr int NPF = 8 / VEC;
+  constexpr bool SPLIT = VEC == 8;
+#pragma unroll
+  for (int sc = 0; sc < 2; ++sc) {
+    if (sc >= nsub) break;
     F pf[NPF], pl[NPF];
 #pragma unroll
     for (int f = 0; f < NPF; ++f)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const T hi = from_f32<T>(p[f * VEC + e]);
+        const int k8 = f * VEC + e;  // 0..7
+        const float pv = p[2 * sc + (k8 >> 2)][k8 & 3];
+        const T hi = from_f32<T>(pv);
         pf[f][e] = hi;
-        if (SPLIT) pl[f][e] = from_f32<T>(p[f * VEC + e] - to_f32(hi));
+        if (SPLIT) pl[f][e] = from_f32<T>(pv - to_f32(hi));
       }
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
@@ -196,7 +220,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const float c_log2 = a.scale * 1.4426950408889634f;  // score -> log2 units
 
   // chunks: the context range, then (split 0 only) the B block keys
   const int nctx = k_end > k_beg ? (k_end - k_beg + ATT_KC - 1) / ATT_KC : 0;
@@ -221,7 +245,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   for (int c = 0; c < nchunk; ++c) {
     const int cur = c & 1;
     if (c + 1 < nchunk) issue(c + 1);
-    if (active) attend_chunk<T, DH>(sm.k[cur], sm.vt[cur], qf, nk, scale_log2, st);
+    if (active) attend_chunk<T, DH>(sm.k[cur], sm.vt[cur], qf, nk, c_log2, st);
     if (c + 1 < nchunk) {
       nk = ld.nk;
       ld.store(sm, cur ^ 1);
@@ -240,7 +264,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
     for (int dt = 0; dt < DH / 16; ++dt)
       *reinterpret_cast<f32x4 *>(op + dt * 16 + 4 * g) = st.o[dt];
     if (g == 0) {
-      a.mlpart[rec * 2] = st.m;
+      a.mlpart[rec * 2] = st.m * c_log2;  // running max in log2 units
       a.mlpart[rec * 2 + 1] = st.l;
     }
   }
