@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--n-new", type=int, default=8)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the calibration copy for HBM byte counters (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path shards "
@@ -213,6 +215,25 @@ def main():
         stages[n] = dict(ms=round(per_call[n], 4), gbs=round(b / t / 1e9, 1) if t else None,
                          tflops=round(f / t / 1e12, 2) if t else None)
 
+    # calibration copy of known size for HBM byte counters (outside timing):
+    # one elementwise kernel that reads and writes `copy_mib` MiB
+    copy_info = None
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(st)
+        torch.mul(src, 1.0, out=dst)
+        c1.record(st)
+        torch.cuda.synchronize()
+        t = c0.elapsed_time(c1) * 1e-3
+        copy_info = dict(kernel="torch mul-by-1 (elementwise copy)", read_bytes=n * 4,
+                         write_bytes=n * 4, gbs=round(2 * n * 4 / t / 1e9, 1))
+        del src, dst
+
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -241,6 +262,7 @@ def main():
         "stages": stages,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "calibration_copy": copy_info,
     }
     print(json.dumps(out), flush=True)
 
