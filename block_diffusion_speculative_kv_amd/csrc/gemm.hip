@@ -111,8 +111,9 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   const int s1 = min(s0 + st_per_split, nst);
   const int n0 = nb * BN, m0 = mb * BM;
   TileLoader<NW, MW> ld;
-  ld.init([&](int r) { return W + (long)min(n0 + r, N - 1) * ldw; },
-          [&](int r) { return X + (long)min(m0 + r, M - 1) * ldx; }, (long)s0 * TK);
+  ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
+          X + (long)m0 * ldx, [&](int r) { return (min(m0 + r, M - 1) - m0) * (int)ldx; },
+          (long)s0 * TK);
   f32x4 acc[NW][MW];
   tile_mainloop<NW, MW, false>(sm, ld, s1 - s0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

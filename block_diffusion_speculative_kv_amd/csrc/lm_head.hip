@@ -258,12 +258,10 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   const bf16 *W = (const bf16 *)a.w;
   const bf16 *H = (const bf16 *)a.hidden;
   TileLoader<NW, MW> ld;
-  ld.init([&](int i) { return W + (long)min(v0 + i, V - 1) * d; },
-          [&](int i) {
-            const int r = min(r0 + i, a.rows - 1);
-            return H + ((long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq) * d;
-          },
-          0);
+  auto hrow = [&](int r) { return (r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq; };
+  const int h0 = hrow(r0);
+  ld.init(W + (long)v0 * d, [&](int i) { return (min(v0 + i, V - 1) - v0) * d; },
+          H + (long)h0 * d, [&](int i) { return (hrow(min(r0 + i, a.rows - 1)) - h0) * d; }, 0);
   f32x4 acc[NW][MW];
   tile_mainloop<NW, MW, true>(sm, ld, d / TK, acc);
 

@@ -30,46 +30,58 @@ struct TileSmem {
   bf16 x[2][BM * TKP];
 };
 
-// Global -> register -> LDS copier for one workgroup's W and X tiles.
+// One stage of a workgroup's W and X tiles held in registers.
+template <int NW, int MW>
+struct TileRegs {
+  bf16x8 w[NW], x[MW];
+};
+
+// Global -> register -> LDS copier for one workgroup's W and X tiles.  Each
+// matrix is addressed from one wave-uniform base (the block's first row,
+// advanced by whole stages) plus a 32-bit per-thread element offset, which
+// keeps the per-thread address state small.
 template <int NW, int MW>
 struct TileLoader {
   static constexpr int BN = 32 * NW, BM = 32 * MW;
-  const bf16 *wp[NW];
-  const bf16 *xp[MW];
-  int wl[NW], xl[MW];
-  bf16x8 wr[NW], xr[MW];
+  const bf16 *wbase, *xbase;
+  int woff[NW], xoff[MW];
 
-  // wrow(i) / xrow(i): global row pointer of tile row i (already clamped to
-  // a valid row); k0: first k of this workgroup's range.
+  // wrow(i) / xrow(i): element offset of tile row i from wb / xb (already
+  // clamped to a valid row; must fit in 31 bits); k0: first k of this
+  // workgroup's range.
   template <typename WRow, typename XRow>
-  __device__ __forceinline__ void init(WRow wrow, XRow xrow, long k0) {
+  __device__ __forceinline__ void init(const bf16 *wb, WRow wrow, const bf16 *xb, XRow xrow,
+                                       long k0) {
+    wbase = wb + k0;
+    xbase = xb + k0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int idx = threadIdx.x + 256 * i;
-      const int row = idx >> 3, c = (idx & 7) * 8;
-      wp[i] = wrow(row) + k0 + c;
-      wl[i] = row * TKP + c;
+      woff[i] = wrow(idx >> 3) + (idx & 7) * 8;
     }
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
       const int idx = threadIdx.x + 256 * i;
-      const int row = idx >> 3, c = (idx & 7) * 8;
-      xp[i] = xrow(row) + k0 + c;
-      xl[i] = row * TKP + c;
+      xoff[i] = xrow(idx >> 3) + (idx & 7) * 8;
     }
   }
-  __device__ __forceinline__ void load(int stage) {
-    const long off = (long)stage * TK;
+  __device__ __forceinline__ void load(TileRegs<NW, MW> &r, int stage) const {
+    const bf16 *wb = wbase + (long)stage * TK;
+    const bf16 *xb = xbase + (long)stage * TK;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) wr[i] = *reinterpret_cast<const bf16x8 *>(wp[i] + off);
+    for (int i = 0; i < NW; ++i) r.w[i] = *reinterpret_cast<const bf16x8 *>(wb + woff[i]);
 #pragma unroll
-    for (int i = 0; i < MW; ++i) xr[i] = *reinterpret_cast<const bf16x8 *>(xp[i] + off);
+    for (int i = 0; i < MW; ++i) r.x[i] = *reinterpret_cast<const bf16x8 *>(xb + xoff[i]);
   }
-  __device__ __forceinline__ void store(TileSmem<NW, MW> &sm, int buf) {
+  __device__ __forceinline__ void store(TileSmem<NW, MW> &sm, int buf,
+                                        const TileRegs<NW, MW> &r) const {
+    const int base = (threadIdx.x >> 3) * TKP + (threadIdx.x & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) *reinterpret_cast<bf16x8 *>(&sm.w[buf][wl[i]]) = wr[i];
+    for (int i = 0; i < NW; ++i)
+      *reinterpret_cast<bf16x8 *>(&sm.w[buf][base + 32 * TKP * i]) = r.w[i];
 #pragma unroll
-    for (int i = 0; i < MW; ++i) *reinterpret_cast<bf16x8 *>(&sm.x[buf][xl[i]]) = xr[i];
+    for (int i = 0; i < MW; ++i)
+      *reinterpret_cast<bf16x8 *>(&sm.x[buf][base + 32 * TKP * i]) = r.x[i];
   }
 };
 
@@ -97,12 +109,7 @@ __device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW> &sm, TileLoader<N
 #pragma unroll
   for (int j = 0; j < MW; ++j) brow[j] = (wm * 16 * MW + 16 * j + r16) * TKP + 8 * g;
 
-  ld.load(0);
-  ld.store(sm, 0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) ld.load(s + 1);
+  auto compute = [&](int cur) {
     const bf16 *ws = sm.w[cur];
     const bf16 *xs = sm.x[cur];
 #pragma unroll
@@ -117,7 +124,17 @@ __device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW> &sm, TileLoader<N
 #pragma unroll
         for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
     }
-    if (s + 1 < nst) ld.store(sm, cur ^ 1);
+  };
+  // stage s lives in LDS buffer s & 1; the next stage waits in registers
+  TileRegs<NW, MW> r;
+  ld.load(r, 0);
+  ld.store(sm, 0, r);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nst) ld.load(r, s + 1);
+    compute(cur);
+    if (s + 1 < nst) ld.store(sm, cur ^ 1, r);
     __syncthreads();
   }
 }
