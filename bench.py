@@ -240,7 +240,8 @@ def main():
         cpu = _cpu_baseline(cfg, cyc, args.cpu_budget)
 
     out = {
-        "metric": "draft+verify cycles/s (bs=32, 8B-shaped drafter)",
+        "metric": "draft+verify cycles/s (bs=32, 8B-shaped drafter)" if args.workload == "q8b_bs32_rs"
+        else f"draft+verify cycles/s ({args.workload})",
         "value": round(cycles_per_s, 3),
         "unit": "cycles/s",
         "n_gpus": 1,

@@ -69,6 +69,73 @@ __device__ __forceinline__ typename Mma<T>::frag zero_frag() {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming main loop for weight-bound contractions (few rows): operand
+// fragments come straight from global memory into registers, U k-steps at a
+// time, into two register banks used in turn, so the loads of the next U
+// k-steps are in flight while the current U are multiplied (no register
+// copies between banks).  ap[i] / bp[j]: per-lane pointers of the A / B
+// operand rows at the first k of the range; nks k-steps of Mma<T>::KW.
+// ---------------------------------------------------------------------------
+template <typename T, int NA, int NB, int U>
+struct StreamBank {
+  typename Mma<T>::frag a[U][NA], b[U][NB];
+};
+
+template <typename T, int NA, int NB, int U>
+__device__ __forceinline__ void stream_load(StreamBank<T, NA, NB, U> &bk, const T *const (&ap)[NA],
+                                            const T *const (&bp)[NB], int ks, int nks) {
+  constexpr int KW = Mma<T>::KW;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const long off = (long)min(ks + u, nks - 1) * KW;  // clamped: in bounds, unused if past nks
+#pragma unroll
+    for (int i = 0; i < NA; ++i) bk.a[u][i] = load_frag<T>(ap[i] + off);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bk.b[u][j] = load_frag<T>(bp[j] + off);
+  }
+}
+
+template <typename T, int NA, int NB, int U>
+__device__ __forceinline__ void stream_mma(const StreamBank<T, NA, NB, U> &bk, int ks, int nks,
+                                           f32x4 (&acc)[NA][NB]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (ks + u < nks) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = Mma<T>::run(bk.a[u][i], bk.b[u][j], acc[i][j]);
+    }
+  }
+}
+
+template <typename T, int NA, int NB, int U>
+__device__ __forceinline__ void stream_mainloop(const T *const (&ap)[NA], const T *const (&bp)[NB],
+                                                int nks, f32x4 (&acc)[NA][NB]) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nks <= 0) return;
+  StreamBank<T, NA, NB, U> b0, b1;
+  stream_load(b0, ap, bp, 0, nks);
+  for (int ks = 0; ks < nks; ks += 2 * U) {
+    if (ks + U < nks) stream_load(b1, ap, bp, ks + U, nks);
+    stream_mma(b0, ks, nks, acc);
+    if (ks + U >= nks) break;
+    if (ks + 2 * U < nks) stream_load(b0, ap, bp, ks + 2 * U, nks);
+    stream_mma(b1, ks + U, nks, acc);
+  }
+}
+
+// Groups of k-steps per bank: enough bytes in flight per wave without
+// exceeding ~100 fragment registers per bank pair.
+template <int NA, int NB>
+struct StreamDepth {
+  static constexpr int U = (NA + NB) <= 5 ? 4 : ((NA + NB) <= 8 ? 2 : 1);
+};
+
+// ---------------------------------------------------------------------------
 // Conversions.  float -> bf16 rounds to nearest even (the hardware convert).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }

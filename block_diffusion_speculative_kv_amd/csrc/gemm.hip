@@ -10,8 +10,9 @@
 //
 // Two kernels: with up to 64 rows the projection streams its weight once
 // (HBM-bound) and every MFMA operand fragment is loaded straight from global
-// memory into registers; with more rows (bf16) the 128 x 128 LDS-tiled main
-// loop of mma_tile.hpp re-uses each staged weight tile across 128 rows.
+// memory into registers by the streaming loop of common.hpp (groups of
+// k-steps in flight); with more rows (bf16) the 128 x 128 LDS-tiled main loop
+// of mma_tile.hpp re-uses each staged weight tile across 128 rows.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mma_tile.hpp"
@@ -47,38 +48,7 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
   }
 
   f32x4 acc[NTW][MTW];
-#pragma unroll
-  for (int i = 0; i < NTW; ++i)
-#pragma unroll
-    for (int j = 0; j < MTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  F a[NTW], b[MTW];
-  if (ks0 < ks1) {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) a[t] = load_frag<T>(wp[t]);
-#pragma unroll
-    for (int t = 0; t < MTW; ++t) b[t] = load_frag<T>(xp[t]);
-  }
-  for (int ks = ks0; ks < ks1; ++ks) {
-    F an[NTW], bn[MTW];
-    const long off = (long)(ks + 1 - ks0) * KW;
-    if (ks + 1 < ks1) {
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) an[t] = load_frag<T>(wp[t] + off);
-#pragma unroll
-      for (int t = 0; t < MTW; ++t) bn[t] = load_frag<T>(xp[t] + off);
-    }
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) acc[i][j] = Mma<T>::run(a[i], b[j], acc[i][j]);
-    if (ks + 1 < ks1) {
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) a[t] = an[t];
-#pragma unroll
-      for (int t = 0; t < MTW; ++t) b[t] = bn[t];
-    }
-  }
+  stream_mainloop<T, NTW, MTW, StreamDepth<NTW, MTW>::U>(wp, xp, ks1 - ks0, acc);
 
   float *o = out + (long)blockIdx.z * M * N;
 #pragma unroll
@@ -178,8 +148,9 @@ int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
   const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
   const long target = 2L * num_cu;
   int splits = (int)((target + tiles - 1) / tiles);
-  // at least 8 k-steps per split, so each wave keeps enough loads in flight
-  splits = max(1, min(splits, nks / 8));
+  // at least 16 k-steps per split: the streaming loop keeps groups of up to
+  // 4 k-steps in flight, and a split should run several groups
+  splits = max(1, min(splits, nks / 16));
   const int per = (nks + splits - 1) / splits;
   splits = (nks + per - 1) / per;  // no empty split
   return splits;

@@ -191,37 +191,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
   }
 
   f32x4 acc[4][MTW];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < MTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = d / KW;
-  F fa[4], fb[MTW];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) fa[t] = load_frag<T>(wp[t]);
-#pragma unroll
-  for (int t = 0; t < MTW; ++t) fb[t] = load_frag<T>(xp[t]);
-  for (int ks = 0; ks < nks; ++ks) {
-    F na[4], nb[MTW];
-    const long off = (long)(ks + 1) * KW;
-    if (ks + 1 < nks) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) na[t] = load_frag<T>(wp[t] + off);
-#pragma unroll
-      for (int t = 0; t < MTW; ++t) nb[t] = load_frag<T>(xp[t] + off);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) acc[i][j] = Mma<T>::run(fa[i], fb[j], acc[i][j]);
-    if (ks + 1 < nks) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) fa[t] = na[t];
-#pragma unroll
-      for (int t = 0; t < MTW; ++t) fb[t] = nb[t];
-    }
-  }
+  stream_mainloop<T, 4, MTW, StreamDepth<4, MTW>::U>(wp, xp, d / KW, acc);
 
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
