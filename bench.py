@@ -68,6 +68,7 @@ def _cpu_baseline(cfg, cyc, budget_s):
     cycles for as many sequences as fit in ~budget_s, scaled to the batch."""
     import numpy as np
 
+    from block_diffusion_speculative_kv_amd import KVCache
     from oracle.drafter import Drafter as OracleDrafter, lm_head
     from oracle import philox
     from oracle.verify import verify_batch
@@ -86,7 +87,7 @@ def _cpu_baseline(cfg, cyc, budget_s):
     done, t_total = 0, 0.0
     for b, S in enumerate(cfg["ctx_lens"]):
         ck = [host(k[b]) for k in cyc.kv.k]
-        cv = [host(v[b]).transpose(0, 2, 1).copy() for v in cyc.kv.v]   # d-major -> [h, pos, dh]
+        cv = [host(KVCache.untile_v(v[b:b + 1])[0]) for v in cyc.kv.v]   # -> [h, pos, dh]
         t0 = time.perf_counter()
         ks, vs = od.inject_rows(feats[b * n_new:(b + 1) * n_new], np.arange(S - n_new, S))
         for l in range(cfg["n_layers"]):

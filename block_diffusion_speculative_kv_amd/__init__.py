@@ -93,14 +93,15 @@ class Drafter:
     # -- memory helpers ------------------------------------------------------
     def kv_cache(self, max_batch: int, cap: int, device="cuda"):
         """Allocate (zeroed) per-layer caches: K [max_batch, h_kv, cap, dh] and
-        V d-major [max_batch, h_kv, dh, cap] (cap a multiple of 8)."""
+        V in 64-position tiles [max_batch, h_kv, cap/64, dh, 64] (cap a
+        multiple of 64)."""
         n = ctypes.c_size_t()
         _lib.check(self.lib.dstill_kv_bytes(ctypes.byref(self._cfg_c), max_batch, cap,
                                             ctypes.byref(n)), "dstill_kv_bytes")
         hk, dh = self.cfg["n_kv_heads"], self.cfg["head_dim"]
         ks = [torch.zeros((max_batch, hk, cap, dh), dtype=self.tdtype, device=device)
               for _ in range(self.cfg["n_layers"])]
-        vs = [torch.zeros((max_batch, hk, dh, cap), dtype=self.tdtype, device=device)
+        vs = [torch.zeros((max_batch, hk, cap // 64, dh, 64), dtype=self.tdtype, device=device)
               for _ in range(self.cfg["n_layers"])]
         assert ks[0].numel() * ks[0].element_size() == n.value
         return KVCache(ks, vs)
@@ -152,8 +153,20 @@ class Drafter:
 
 
 class KVCache:
-    """Per-layer K [max_batch, h_kv, cap, dh] and d-major V [max_batch, h_kv,
-    dh, cap] cache tensors plus the C view the library reads."""
+    """Per-layer K [max_batch, h_kv, cap, dh] and tiled V [max_batch, h_kv,
+    cap/64, dh, 64] cache tensors plus the C view the library reads."""
+
+    @staticmethod
+    def tile_v(v_rows):
+        """[b, h, cap, dh] position-major V -> the library's tiled layout."""
+        b, h, cap, dh = v_rows.shape
+        return v_rows.view(b, h, cap // 64, 64, dh).transpose(-1, -2).contiguous()
+
+    @staticmethod
+    def untile_v(v_tiled):
+        """The library's tiled V -> [b, h, cap, dh]."""
+        b, h, nt, dh, _ = v_tiled.shape
+        return v_tiled.transpose(-1, -2).reshape(b, h, nt * 64, dh)
 
     def __init__(self, ks, vs):
         self.k, self.v = ks, vs

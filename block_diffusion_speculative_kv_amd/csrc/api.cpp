@@ -183,7 +183,7 @@ int check_config(const dstill_config *c) {
 int check_kv(const dstill_handle *h, const dstill_kv *kv) {
   if (!kv || !kv->k || !kv->v) return fail(DSTILL_EINVAL, "kv or its pointer arrays are null");
   if (kv->max_batch < 1 || kv->cap < 1) return fail(DSTILL_ESHAPE, "kv max_batch/cap must be >= 1");
-  if (kv->cap % 8) return fail(DSTILL_ESHAPE, "kv cap %d is not a multiple of 8", kv->cap);
+  if (kv->cap % 64) return fail(DSTILL_ESHAPE, "kv cap %d is not a multiple of 64", kv->cap);
   for (int l = 0; l < h->cfg.n_layers; ++l)
     if (!kv->k[l] || !kv->v[l]) return fail(DSTILL_EINVAL, "kv cache of layer %d is null", l);
   return DSTILL_OK;
@@ -226,8 +226,8 @@ int dstill_destroy(dstill_handle *h) {
 int dstill_kv_bytes(const dstill_config *cfg, int32_t max_batch, int32_t cap, size_t *bytes) {
   if (int e = check_config(cfg)) return e;
   if (!bytes) return fail(DSTILL_EINVAL, "bytes is null");
-  if (max_batch < 1 || cap < 1 || cap % 8)
-    return fail(DSTILL_ESHAPE, "max_batch must be >= 1 and cap a positive multiple of 8");
+  if (max_batch < 1 || cap < 1 || cap % 64)
+    return fail(DSTILL_ESHAPE, "max_batch must be >= 1 and cap a positive multiple of 64");
   *bytes = (size_t)max_batch * cfg->n_kv_heads * cap * cfg->head_dim * elem_bytes(cfg->dtype);
   return DSTILL_OK;
 }

@@ -14,8 +14,9 @@
 // split 0 also takes the block keys.  Chunks are pipelined: the next chunk's
 // K and V^T are loaded into registers while the waves work on the current
 // one out of LDS, then written to the other LDS buffer (one barrier per
-// chunk).  The V cache is d-major ([dh][cap] per sequence and head), so V^T
-// of a chunk is a plain coalesced copy.  The
+// chunk).  The V cache is stored in tiles of 64 keys, each d-major
+// ([cap/64][dh][64] per sequence and head), so V^T of a chunk is one
+// contiguous 16 KB block, like the chunk of K.  The
 // partial (m, l, O) of every split is merged by attn_combine with the
 // log-sum-exp rule, which reproduces the single softmax up to rounding.
 //
@@ -48,7 +49,7 @@ struct AttnSmem {
 };
 
 // Copies one chunk global -> registers (issued early) -> LDS (after the
-// current chunk's compute).  K rows are contiguous dh-vectors; the V cache is
+// current chunk's compute).  K rows are contiguous dh-vectors; a V tile is
 // d-major, so a V^T row of the chunk is 64 consecutive keys of one d.  Loads
 // are unconditional from clamped, in-bounds addresses (no branch, so nothing
 // waits on them until the store); keys at or beyond nk are masked at store
@@ -226,6 +227,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   const int nctx = k_end > k_beg ? (k_end - k_beg + ATT_KC - 1) / ATT_KC : 0;
   const int nchunk = nctx + (sp == 0 ? 1 : 0);
   const T *kcache = (const T *)a.kc + ((long)b * a.hkv + h) * a.cap * DH;
+  // V cache: tiles of ATT_KC keys, each tile d-major [DH][ATT_KC] and contiguous
   const T *vcache = (const T *)a.vc + ((long)b * a.hkv + h) * DH * a.cap;
   const T *kblock = (const T *)a.kb + (long)bc * a.B * a.hkv * DH + (long)h * DH;
   const T *vblock = (const T *)a.vb + ((long)bc * a.hkv + h) * DH * ATT_VBS;
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   auto issue = [&](int c) {
     if (c < nctx) {
       const int k0 = k_beg + c * ATT_KC;
-      ld.load(kcache + (long)k0 * DH, DH, vcache + k0, a.cap, min(ATT_KC, k_end - k0));
+      ld.load(kcache + (long)k0 * DH, DH, vcache + (long)k0 * DH, ATT_KC, min(ATT_KC, k_end - k0));
     } else {
       ld.load(kblock, (long)a.hkv * DH, vblock, ATT_VBS, a.B);
     }

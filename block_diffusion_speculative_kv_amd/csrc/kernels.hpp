@@ -50,7 +50,7 @@ struct AttnArgs {
   const void *kb;      // [bs*C*B, hkv*dh] block keys
   const void *vb;      // [bs*C][hkv][dh][16] block values, d-major
   const void *kc;      // cache K of this layer [max_batch][hkv][cap][dh]
-  const void *vc;      // cache V of this layer [max_batch][hkv][dh][cap]
+  const void *vc;      // cache V of this layer [max_batch][hkv][cap/64][dh][64]
   const int32_t *eff_ctx;  // [bs] clamped context lengths
   int bs, C, B, hq, hkv, dh, cap;
   int split;           // context keys per split (multiple of 64)

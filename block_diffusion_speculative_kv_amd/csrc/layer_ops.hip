@@ -11,8 +11,9 @@
 //   full fp32 accuracy;
 //   SwiGLU: silu(gate) * up, silu(x) = x / (1 + exp(-x)).
 // Layouts: K is stored as dh-vectors ([cap][dh] per sequence and kv head),
-// V d-major ([dh][cap]; block V in the workspace as [dh][16]), which is the
-// layout the attention kernel's P.V operand reads.
+// V in tiles of 64 keys, d-major inside a tile ([cap/64][dh][64]; block V in
+// the workspace as [dh][16]): the layout the attention kernel's P.V operand
+// reads as contiguous blocks.
 #include <math.h>
 
 #include "common.hpp"
@@ -288,9 +289,11 @@ __global__ __launch_bounds__(64) void inject_post_kernel(
       }
     }
   }
-  // K cache rows are dh-vectors [cap][dh]; the V cache is d-major [dh][cap]
-  const long stride = is_k ? 1 : cap;
-  T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh : vc + ((long)sq * hkv + h) * dh * cap + ps;
+  // K cache rows are dh-vectors [cap][dh]; the V cache is stored in tiles of
+  // 64 keys, d-major inside a tile: [cap/64][dh][64]
+  const long stride = is_k ? 1 : 64;
+  T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
+                : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
   if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, true, ps, theta);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {

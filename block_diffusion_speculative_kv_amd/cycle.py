@@ -44,7 +44,7 @@ class Cycle:
         self.n_new = max(1, min(n_new, min(self.ctx) if min(self.ctx) > 0 else 1))
         self.w = gen.weights(cfg, device=self.dev)
         self.dr = Drafter(cfg, self.w)
-        self.kv = self.dr.kv_cache(bs, (self.max_ctx + B + 7) // 8 * 8)
+        self.kv = self.dr.kv_cache(bs, (self.max_ctx + B + 63) // 64 * 64)
         self.mode = _HEAD_MODE[cfg["lm_mode"]]
         self.verify_mode = {"greedy": VERIFY_GREEDY, "rs": VERIFY_RS}.get(cfg["verify"])
         self.T = float(cfg.get("temperature", 1.0))

@@ -137,9 +137,11 @@ typedef struct {
 /* Persistent draft KV cache: k[l], v[l] (HOST arrays of n_layers DEVICE
  * pointers) in the config dtype.  k[l] is [max_batch][n_kv_heads][cap][head_dim]
  * (row (b, h, p) is the injected key of context position p of sequence b);
- * v[l] is d-major, [max_batch][n_kv_heads][head_dim][cap] (element (b, h, d, p)
- * is component d of the injected value of position p), which is the layout
- * the attention's P.V product consumes.  cap must be a multiple of 8. */
+ * v[l] is stored in tiles of 64 positions, d-major inside a tile:
+ * [max_batch][n_kv_heads][cap/64][head_dim][64] (element (b, h, p/64, d, p%64)
+ * is component d of the injected value of position p), so the attention's
+ * P.V product reads each 64-key tile of V^T as one contiguous block.  cap
+ * must be a multiple of 64. */
 typedef struct {
   void *const *k;
   void *const *v;
@@ -156,7 +158,7 @@ typedef struct dstill_handle dstill_handle;
 int dstill_create(const dstill_config *cfg, const dstill_weights *w, dstill_handle **out);
 int dstill_destroy(dstill_handle *h);
 
-/* Bytes of ONE K (or V) cache tensor of one layer (cap a multiple of 8). */
+/* Bytes of ONE K (or V) cache tensor of one layer (cap a multiple of 64). */
 int dstill_kv_bytes(const dstill_config *cfg, int32_t max_batch, int32_t cap, size_t *bytes);
 
 /* Upper bounds a caller plans with; every call's workspace need is a

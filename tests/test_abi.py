@@ -70,16 +70,16 @@ def test_create_and_size_queries_without_launching(lib):
     h = ctypes.c_void_p()
     assert lib.dstill_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == _lib.OK
     n = ctypes.c_size_t()
-    assert lib.dstill_kv_bytes(ctypes.byref(c), 3, 104, ctypes.byref(n)) == _lib.OK
-    assert n.value == 3 * 2 * 104 * 128 * 2
-    assert lib.dstill_kv_bytes(ctypes.byref(c), 3, 100, ctypes.byref(n)) == _lib.ESHAPE
+    assert lib.dstill_kv_bytes(ctypes.byref(c), 3, 128, ctypes.byref(n)) == _lib.OK
+    assert n.value == 3 * 2 * 128 * 128 * 2
+    assert lib.dstill_kv_bytes(ctypes.byref(c), 3, 104, ctypes.byref(n)) == _lib.ESHAPE
     lim = _lib.Limits(max_batch=3, max_copies=2, max_ctx=1029, max_inject_rows=77,
                       max_head_rows=45)
     assert lib.dstill_workspace_bytes(h, ctypes.byref(lim), ctypes.byref(n)) == _lib.OK
     assert n.value > 0
     # calls that fail validation enqueue nothing and need no device
     kvp = (ctypes.c_void_p * 2)(4096, 4096)
-    kv = _lib.KV(k=kvp, v=kvp, max_batch=3, cap=104)
+    kv = _lib.KV(k=kvp, v=kvp, max_batch=3, cap=128)
     s = _lib.Sample(mode=0, temperature=1.0, seed=0, cycle=0)
     assert lib.dstill_block_draft(h, 4096, 4096, 4, 16, 1, 50, ctypes.byref(kv), 4096, None,
                                   4096, 10**9, None) == _lib.ESHAPE      # bs > max_batch

@@ -41,8 +41,8 @@ def _setup(cfg, cap):
     w = gen.weights(cfg, device=dev)
     dr = bd.Drafter(cfg, w)
     ks, vs = gen.kv_cache(cfg, cap, device=dev)
-    # the library's V cache is d-major; keep the [h, pos, dh] copies for the oracle
-    kv = bd.KVCache(ks, [v.transpose(-1, -2).contiguous() for v in vs])
+    # the library's V cache is tiled; keep the [h, pos, dh] copies for the oracle
+    kv = bd.KVCache(ks, [bd.KVCache.tile_v(v) for v in vs])
     kv.v_rows = vs
     return dev, w, dr, kv
 
@@ -120,7 +120,7 @@ def test_tiny_fp32():
 @pytest.mark.parametrize("ctx", [[37, 300, 1029], [0, 1, 64]])
 def test_small_bf16_ragged(ctx):
     cfg = configs.small_bf16(ctx=ctx)
-    dev, w, dr, kv = _setup(cfg, 1104)
+    dev, w, dr, kv = _setup(cfg, 1152)
     tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
     want = _oracle(cfg, to_np(w), kv, tok, ctx)
     _compare(cfg, to_np(w), out, want, f"small ctx {ctx}")
@@ -129,7 +129,7 @@ def test_small_bf16_ragged(ctx):
 
 def test_small_bf16_multicopy():
     cfg = configs.small_bf16(ctx=[200, 513, 7], n_copies=3)
-    dev, w, dr, kv = _setup(cfg, 600)
+    dev, w, dr, kv = _setup(cfg, 640)
     tok, out, _ = _draft(cfg, dr, kv, dev, cfg["ctx_lens"], 513)
     want = _oracle(cfg, to_np(w), kv, tok, cfg["ctx_lens"])
     _compare(cfg, to_np(w), out, want, "multicopy")
@@ -137,7 +137,7 @@ def test_small_bf16_multicopy():
 
 def test_small_bf16_ctx_clamped_and_bad_token():
     cfg = configs.small_bf16(ctx=[400, 100, 90])
-    dev, w, dr, kv = _setup(cfg, 504)
+    dev, w, dr, kv = _setup(cfg, 512)
     tok = gen.block_tokens(cfg, device=dev)
     tok[2, 0, 3] = cfg["vocab"] + 5           # out of range: clamped to V-1, flagged
     # max_ctx 256 < 400: sequence 0 is clamped to 256 and flagged
@@ -152,7 +152,7 @@ def test_small_bf16_ctx_clamped_and_bad_token():
 
 def test_deterministic():
     cfg = configs.small_bf16()
-    dev, w, dr, kv = _setup(cfg, 1104)
+    dev, w, dr, kv = _setup(cfg, 1152)
     _, a, _ = _draft(cfg, dr, kv, dev, cfg["ctx_lens"], 1029)
     _, b, _ = _draft(cfg, dr, kv, dev, cfg["ctx_lens"], 1029)
     assert torch.equal(a, b)

@@ -47,9 +47,9 @@ def _check(cfg, w, kv, feats, seq, pos, rows):
     ks, vs = od.inject_rows(f_np, pos[rows])
     for l in range(cfg["n_layers"]):
         K = to_np(kv.k[l])
-        V = to_np(kv.v[l])
+        V = to_np(bd.KVCache.untile_v(kv.v[l]))
         gk = K[seq[rows], :, pos[rows]]          # [n, hkv, dh]
-        gv = V[seq[rows], :, :, pos[rows]]       # V is d-major: [b, h, dh, pos]
+        gv = V[seq[rows], :, pos[rows]]
         if cfg["dtype"] == "f32":
             assert_close_rel(gk, ks[l], 1e-5, f"K layer {l}")
             assert_close_rel(gv, vs[l], 1e-5, f"V layer {l}")
@@ -60,7 +60,7 @@ def _check(cfg, w, kv, feats, seq, pos, rows):
 
 def test_tiny_fp32():
     cfg = configs.get("tiny_fp32")
-    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 128, 136, 1)
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 128, 192, 1)
     _check(cfg, w, kv, feats, seq, pos, np.arange(128))
 
 
@@ -68,22 +68,22 @@ def test_small_bf16_with_skipped_rows():
     cfg = configs.small_bf16()
     n = 77
     invalid = (3, 10, 11)
-    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, n, 56, 3, invalid=invalid)
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, n, 64, 3, invalid=invalid)
     ok = np.array([i not in invalid for i in range(n)])
     _check(cfg, w, kv, feats, seq, pos, np.nonzero(ok)[0])
     # every cache row not named by a valid input row is still zero
     written = set(zip(seq[ok].tolist(), pos[ok].tolist()))
     K = kv.k[0].float().cpu().numpy()
     for b in range(3):
-        for p in range(56):
+        for p in range(64):
             if (b, p) not in written:
                 assert not K[b, :, p].any()
 
 
 def test_incremental_equals_all_at_once():
     cfg = configs.small_bf16()
-    dev, w, dr, kv, feats, seq, pos, (seq_t, pos_t, ws) = _inject(cfg, 60, 40, 3)
-    kv2 = dr.kv_cache(3, 40)
+    dev, w, dr, kv, feats, seq, pos, (seq_t, pos_t, ws) = _inject(cfg, 60, 64, 3)
+    kv2 = dr.kv_cache(3, 64)
     for a, b in ((0, 7), (7, 31), (31, 60)):
         dr.inject_kv(feats[a:b].contiguous(), seq_t[a:b].contiguous(), pos_t[a:b].contiguous(),
                      kv2, ws)
