@@ -104,7 +104,7 @@ AttnPlan attn_plan(int max_ctx, int pairs) {
 // Workspace of one block_draft call.
 struct DraftWs {
   int32_t *eff_ctx, *tok;
-  float *h, *parts, *opart, *mlpart;
+  float *h, *parts, *opart, *mlpart, *ssp;
   void *u, *q, *kb, *vb, *attn, *act;
 };
 size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int ncu, void *ws,
@@ -116,6 +116,7 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
   w.eff_ctx = cv.take<int32_t>(bs);
   w.tok = cv.take<int32_t>(R);
   w.h = cv.take<float>((size_t)R * d);
+  w.ssp = cv.take<float>((size_t)R * ((d + 1023) / 1024));
   w.u = cv.take<char>((size_t)R * d * eb);
   w.q = cv.take<char>((size_t)R * qd * eb);
   w.kb = cv.take<char>((size_t)R * kvd * eb);
@@ -132,12 +133,14 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
 
 struct InjectWs {
   void *ht;
-  float *parts;
+  float *parts, *xtmp, *ssp;
 };
 size_t inject_ws(const dstill_config &c, int n, int ncu, void *ws, InjectWs *out) {
   Carver cv(ws);
   InjectWs w;
   w.ht = cv.take<char>((size_t)n * c.hidden * elem_bytes(c.dtype));
+  w.xtmp = cv.take<float>((size_t)n * c.hidden);
+  w.ssp = cv.take<float>((size_t)n * ((c.hidden + 1023) / 1024));
   w.parts = cv.take<float>(gemm_parts_floats(c, n, ncu));
   if (out) *out = w;
   return cv.off;
@@ -290,7 +293,7 @@ int dstill_inject_kv(const dstill_handle *h, const void *feats, const int32_t *s
   g.splits = gemm_plan_splits(n, d, F, c.dtype, ncu);
   launch_gemm(g, st);
   launch_norm_rows(c.dtype, w.parts, g.splits, n, d, nullptr, 0, h->w.g_fuse, c.rms_eps, w.ht, d,
-                   st);
+                   w.xtmp, w.ssp, st);
   for (int l = 0; l < c.n_layers; ++l) {
     const dstill_layer_weights &L = h->layers[l];
     GemmArgs k;
@@ -338,7 +341,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
   launch_embed(c.dtype, h->w.embed, w.tok, R, d, w.h, st);
   // pre-attention norm of layer 0; later layers get it fused after the MLP
   launch_norm_rows(c.dtype, nullptr, 0, R, d, w.h, 0, h->layers[0].attn_norm, c.rms_eps, w.u, d,
-                   st);
+                   nullptr, w.ssp, st);
   for (int l = 0; l < c.n_layers; ++l) {
     const dstill_layer_weights &L = h->layers[l];
     GemmArgs g;
@@ -364,7 +367,8 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     g.X = w.attn; g.ldx = qd; g.W = L.wo; g.ldw = qd; g.N = d; g.K = qd;
     g.splits = gemm_plan_splits(R, d, qd, c.dtype, ncu);
     launch_gemm(g, st);
-    launch_norm_rows(c.dtype, w.parts, g.splits, R, d, w.h, 1, L.mlp_norm, c.rms_eps, w.u, d, st);
+    launch_norm_rows(c.dtype, w.parts, g.splits, R, d, w.h, 1, L.mlp_norm, c.rms_eps, w.u, d,
+                     nullptr, w.ssp, st);
     // gate|up, SwiGLU, down
     g.X = w.u; g.ldx = d; g.W = L.w_gate_up; g.ldw = d; g.N = 2 * c.mlp; g.K = d;
     g.splits = gemm_plan_splits(R, 2 * c.mlp, d, c.dtype, ncu);
@@ -377,7 +381,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     const bool last = l + 1 == c.n_layers;
     launch_norm_rows(c.dtype, w.parts, g.splits, R, d, w.h, 1,
                      last ? h->w.g_final : h->layers[l + 1].attn_norm, c.rms_eps,
-                     last ? hidden_out : w.u, d, st);
+                     last ? hidden_out : w.u, d, nullptr, w.ssp, st);
   }
   return hip_check("block_draft launch");
 }

@@ -272,44 +272,35 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence-copy, head): weights
-// exp2(m_s - M) / L with L = sum_s exp2(m_s - M) l_s, computed once per query
-// row into LDS, then a weighted sum of the split outputs, 4 values per thread.
-constexpr int COMBINE_MAX_SPLITS = 128;
-
+// Merge the split partials: out = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = exp2(m_s - M), M the largest split max.  One workgroup per
+// (sequence-copy, head, group of 512/dh query rows), one float4 of one row
+// per thread; splits are merged in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  __shared__ float wts[16][COMBINE_MAX_SPLITS];
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int bc = blockIdx.x, head = blockIdx.y;
+  const int dh = a.dh, per_row = dh / 4, rows_per_wg = 128 / per_row;
+  const int s = blockIdx.z * rows_per_wg + threadIdx.x / per_row;
+  const int d = (threadIdx.x % per_row) * 4;
+  if (s >= a.B) return;
   const int b = bc / a.C;
   const int S = a.eff_ctx[b];
   const int nvalid = max(1, (S + a.split - 1) / a.split);
-  const int dh = a.dh;
-  const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B;  // record (sp, s) = rec0 + sp*B + s
-  for (int s = threadIdx.x; s < a.B; s += blockDim.x) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < nvalid; ++sp) M = fmaxf(M, a.mlpart[(rec0 + (long)sp * a.B + s) * 2]);
-    float L = 0.f;
-    for (int sp = 0; sp < nvalid; ++sp) {
-      const long r = rec0 + (long)sp * a.B + s;
-      const float w = exp2f(a.mlpart[r * 2] - M);
-      wts[s][sp] = w;
-      L += w * a.mlpart[r * 2 + 1];
-    }
-    const float inv = 1.0f / L;
-    for (int sp = 0; sp < nvalid; ++sp) wts[s][sp] *= inv;
+  const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B + s;  // record of split sp: rec0 + sp*B
+  float M = -INFINITY;
+  for (int sp = 0; sp < nvalid; ++sp) M = fmaxf(M, a.mlpart[(rec0 + (long)sp * a.B) * 2]);
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nvalid; ++sp) {
+    const long r = rec0 + (long)sp * a.B;
+    const float w = exp2f(a.mlpart[r * 2] - M);
+    L += w * a.mlpart[r * 2 + 1];
+    o += w * *reinterpret_cast<const f32x4 *>(a.opart + r * dh + d);
   }
-  __syncthreads();
-  const int nv4 = dh / 4;
-  for (int idx = threadIdx.x; idx < a.B * nv4; idx += blockDim.x) {
-    const int s = idx / nv4, d = (idx % nv4) * 4;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nvalid; ++sp)
-      o += wts[s][sp] * *reinterpret_cast<const f32x4 *>(a.opart + (rec0 + (long)sp * a.B + s) * dh + d);
-    T *dst = (T *)a.out + ((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d;
+  const float inv = 1.0f / L;
+  T *dst = (T *)a.out + ((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e]);
-  }
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e] * inv);
 }
 
 template <typename T, int DH, int NTHR>
@@ -324,7 +315,10 @@ static void launch_typed(const AttnArgs &a, hipStream_t st) {
   if (group <= 4) launch_nthr<T, DH, 256>(a, st);
   else if (group <= 8) launch_nthr<T, DH, 512>(a, st);
   else launch_nthr<T, DH, 1024>(a, st);
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.bs * a.C, a.hq), dim3(256), 0, st, a);
+  const int rows_per_wg = 128 / (a.dh / 4);
+  hipLaunchKernelGGL(attn_combine_kernel<T>,
+                     dim3(a.bs * a.C, a.hq, (a.B + rows_per_wg - 1) / rows_per_wg), dim3(128), 0,
+                     st, a);
 }
 
 void launch_attention(const AttnArgs &a, hipStream_t st) {

@@ -28,10 +28,11 @@ void launch_draft_prep(const int32_t *tokens, const int32_t *ctx_len, int bs, in
 void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d, float *h,
                   hipStream_t st);
 // out = RMSNorm(x) * gain with x = sum of `nsplit` partial planes (+ resid);
-// the new residual is written back when write_resid is set.
+// the new residual is written back when write_resid is set.  Scratch: xtmp
+// [M, d] fp32 (used when x has nowhere else to live), ssp [M, ceil(d/1024)].
 void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
                       int write_resid, const void *gain, float eps, void *out, long out_stride,
-                      hipStream_t st);
+                      float *xtmp, float *ssp, hipStream_t st);
 void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, int hkv, int dh,
                      const int32_t *eff_ctx, int rows_per_seq, int block, const void *q_norm,
                      const void *k_norm, int qk_norm, float eps, float theta, void *q, void *kb,

@@ -79,52 +79,67 @@ void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d
 }
 
 // ---- RMSNorm over rows, fused with the split-sum and the residual add --------
-constexpr int NORM_MAX_PER_THREAD = 32;  // hidden <= 8192 with 256 threads
+// Two passes, each over a grid of (row, 1024-column chunk) workgroups so that
+// even a handful of rows keeps the GPU busy: (1) x = resid + sum of the
+// partial planes (fixed order), written back as the new residual (or to a
+// scratch row), with the chunk's sum of squares; (2) out = x * rs * gain with
+// rs = 1 / sqrt(mean(x^2) + eps) from the chunk sums (fixed order).
+constexpr int NORM_CHUNK = 1024;  // columns per workgroup (256 threads x 4)
 
-template <typename T>
-__global__ __launch_bounds__(256) void norm_rows_kernel(const float *__restrict__ parts,
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ parts,
                                                         int nsplit, int M, int d,
-                                                        float *__restrict__ resid,
-                                                        int write_resid,
-                                                        const T *__restrict__ gain, float eps,
-                                                        T *__restrict__ out, long out_stride) {
+                                                        const float *resid, float *xout,
+                                                        float *__restrict__ ssp, int nchunk) {
   __shared__ float red[4];
-  const int r = blockIdx.x;
-  float x[NORM_MAX_PER_THREAD];
+  const int r = blockIdx.x, ch = blockIdx.y;
+  const int c = ch * NORM_CHUNK + threadIdx.x * 4;
   float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NORM_MAX_PER_THREAD; ++i) {
-    const int j = threadIdx.x + i * 256;
-    float v = 0.f;
-    if (j < d) {
-      for (int s = 0; s < nsplit; ++s) v += parts[((long)s * M + r) * d + j];
-      if (resid) {
-        v += resid[(long)r * d + j];
-        if (write_resid) resid[(long)r * d + j] = v;
-      }
-    }
-    x[i] = v;
-    ss += v * v;
+  if (c < d) {
+    f32x4 x = resid ? *reinterpret_cast<const f32x4 *>(resid + (long)r * d + c)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp)
+      x += *reinterpret_cast<const f32x4 *>(parts + ((long)sp * M + r) * d + c);
+    if (xout) *reinterpret_cast<f32x4 *>(xout + (long)r * d + c) = x;
+    ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   ss = block_sum(ss, red);
+  if (threadIdx.x == 0) ssp[(long)r * nchunk + ch] = ss;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_apply_kernel(const float *__restrict__ x, int d,
+                                                         const float *__restrict__ ssp, int nchunk,
+                                                         const T *__restrict__ gain, float eps,
+                                                         T *__restrict__ out, long out_stride) {
+  const int r = blockIdx.x, ch = blockIdx.y;
+  float ss = 0.f;
+  for (int i = 0; i < nchunk; ++i) ss += ssp[(long)r * nchunk + i];
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  const int c = ch * NORM_CHUNK + threadIdx.x * 4;
+  if (c >= d) return;
+  const f32x4 v = *reinterpret_cast<const f32x4 *>(x + (long)r * d + c);
 #pragma unroll
-  for (int i = 0; i < NORM_MAX_PER_THREAD; ++i) {
-    const int j = threadIdx.x + i * 256;
-    if (j < d) out[(long)r * out_stride + j] = from_f32<T>(x[i] * rs * to_f32(gain[j]));
-  }
+  for (int e = 0; e < 4; ++e)
+    out[(long)r * out_stride + c + e] = from_f32<T>(v[e] * rs * to_f32(gain[c + e]));
 }
 
 void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
                       int write_resid, const void *gain, float eps, void *out, long out_stride,
-                      hipStream_t st) {
+                      float *xtmp, float *ssp, hipStream_t st) {
   if (M == 0) return;
+  const int nchunk = (d + NORM_CHUNK - 1) / NORM_CHUNK;
+  // where x lives for the second pass
+  float *xout = (resid && write_resid) ? resid : ((nsplit > 0 || !resid) ? xtmp : nullptr);
+  const float *xsrc = xout ? xout : resid;
+  dim3 grid(M, nchunk);
+  hipLaunchKernelGGL(split_sum_kernel, grid, dim3(256), 0, st, parts, nsplit, M, d,
+                     (const float *)resid, xout, ssp, nchunk);
   if (dtype == 1)
-    hipLaunchKernelGGL(norm_rows_kernel<bf16>, dim3(M), dim3(256), 0, st, parts, nsplit, M, d,
-                       resid, write_resid, (const bf16 *)gain, eps, (bf16 *)out, out_stride);
+    hipLaunchKernelGGL(norm_apply_kernel<bf16>, grid, dim3(256), 0, st, xsrc, d, ssp, nchunk,
+                       (const bf16 *)gain, eps, (bf16 *)out, out_stride);
   else
-    hipLaunchKernelGGL(norm_rows_kernel<float>, dim3(M), dim3(256), 0, st, parts, nsplit, M, d,
-                       resid, write_resid, (const float *)gain, eps, (float *)out, out_stride);
+    hipLaunchKernelGGL(norm_apply_kernel<float>, grid, dim3(256), 0, st, xsrc, d, ssp, nchunk,
+                       (const float *)gain, eps, (float *)out, out_stride);
 }
 
 // ---- per-head RMSNorm + rotary embedding -------------------------------------
