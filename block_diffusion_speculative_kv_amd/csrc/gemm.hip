@@ -65,6 +65,10 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
 
 // LDS-tiled path: 128 x 128 blocks, k-split over stages of 64.
 constexpr int LDS_NW = 4, LDS_MW = 4;
+// k per stage; W and X ring depths (80 KB: two workgroups per CU)
+constexpr int LDS_KT = 64, LDS_NSW = 3, LDS_NSX = 2;
+using LdsSmem = TileSmem<LDS_NW, LDS_MW, LDS_KT, LDS_NSW, LDS_NSX>;
+constexpr int LDS_PER_CU = 160 * 1024 / (int)sizeof(LdsSmem);  // workgroups per compute unit
 
 __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
                                                         const bf16 *__restrict__ W, long ldw,
@@ -73,19 +77,19 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
                                                         int nmb) {
   constexpr int NW = LDS_NW, MW = LDS_MW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
-  __shared__ TileSmem<NW, MW> sm;
+  __shared__ LdsSmem sm;
   int nb, mb;
   xcd_block(blockIdx.x, nmb, &nb, &mb);
   if (nb >= nnb) return;
   const int s0 = blockIdx.y * st_per_split;
   const int s1 = min(s0 + st_per_split, nst);
   const int n0 = nb * BN, m0 = mb * BM;
-  TileLoader<NW, MW> ld;
+  TileLoader<NW, MW, LDS_KT, LDS_NSW, LDS_NSX> ld;
   ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
           X + (long)m0 * ldx, [&](int r) { return (min(m0 + r, M - 1) - m0) * (int)ldx; },
-          (long)s0 * TK);
+          (long)s0 * LDS_KT);
   f32x4 acc[NW][MW];
-  tile_mainloop<NW, MW, false>(sm, ld, s1 - s0, acc);
+  tile_mainloop<NW, MW, LDS_KT, LDS_NSW, LDS_NSX, false>(sm, ld, s1 - s0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int wn = wave & 1, wm = wave >> 1;
@@ -102,17 +106,32 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   }
 }
 
-static bool use_lds(int M, int K, int dtype) { return dtype == 1 && M > 64 && K % TK == 0; }
+static bool use_lds(int M, int K, int dtype) { return dtype == 1 && M > 64 && K % LDS_KT == 0; }
 
 static void lds_geometry(int M, int N, int K, int ncu, int *nnb, int *nmb, int *nst,
                          int *splits, int *per) {
   constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
   *nnb = (N + BN - 1) / BN;
   *nmb = (M + BM - 1) / BM;
-  *nst = K / TK;
+  *nst = K / LDS_KT;
   const long tiles = (long)*nnb * *nmb;
-  int s = (int)((2L * ncu + tiles - 1) / tiles);
-  s = max(1, min(s, *nst / 4));
+  // Workgroups run in rounds of ncu x LDS_PER_CU.  Estimated time of a
+  // split count s: rounds x (stages per workgroup x ~0.3 us per 64-deep
+  // stage, shared by the workgroups of a compute unit, + ~1 us of pipeline
+  // fill), plus the fp32 partial plane each split writes and the consumer
+  // reads back (~6 TB/s).  The smallest s within 3% of the best wins.
+  auto est = [&](int s) {
+    const int per = (*nst + s - 1) / s;
+    const long slots = (long)ncu * LDS_PER_CU;
+    const long rounds = (tiles * s + slots - 1) / slots;
+    return (double)rounds * (per * 0.3 * LDS_KT / 64 * LDS_PER_CU + 1.0) +
+           (double)s * M * N * 8.0 / 6e6;
+  };
+  const int smax = max(1, min(16, *nst / 2));
+  double best = est(1);
+  for (int s = 2; s <= smax; ++s) best = fmin(best, est(s));
+  int s = 1;
+  while (est(s) > best * 1.03) ++s;
   *per = (*nst + s - 1) / s;
   *splits = (*nst + *per - 1) / *per;
 }
@@ -178,7 +197,7 @@ static void launch_typed(const GemmArgs &a, hipStream_t st) {
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (use_lds(a.M, a.K, a.dtype)) {
     constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
-    const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / TK;
+    const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
     const int per = (nst + a.splits - 1) / a.splits;
     const int nnb8 = (nnb + 7) / 8 * 8;
     hipLaunchKernelGGL(gemm_lds_partial, dim3(nnb8 * nmb, a.splits), dim3(256), 0, st,

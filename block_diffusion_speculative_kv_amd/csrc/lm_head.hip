@@ -37,6 +37,8 @@ namespace dstill {
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
 constexpr int HEAD_NW = 4, HEAD_MW = 4;  // LDS path: 128 ids x 128 rows per workgroup
 constexpr int HEAD_VB_LDS = 32 * HEAD_NW;
+// LDS path: k per stage; W and X ring depths (80 KB: two workgroups per CU)
+constexpr int HEAD_KT = 64, HEAD_NSW = 3, HEAD_NSX = 2;
 constexpr int NXCD = 8;
 
 // Smallest vocabulary block of any path: sizes the partial-record workspace.
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
 __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   constexpr int NW = HEAD_NW, MW = HEAD_MW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
-  __shared__ TileSmem<NW, MW> sm;
+  __shared__ TileSmem<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> sm;
   int vb, rb;
   xcd_block(blockIdx.x, nmb, &vb, &rb);
   if (vb >= a.nvb) return;
@@ -227,13 +229,13 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   const int V = a.vocab, d = a.d;
   const bf16 *W = (const bf16 *)a.w;
   const bf16 *H = (const bf16 *)a.hidden;
-  TileLoader<NW, MW> ld;
+  TileLoader<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> ld;
   auto hrow = [&](int r) { return (r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq; };
   const int h0 = hrow(r0);
   ld.init(W + (long)v0 * d, [&](int i) { return (min(v0 + i, V - 1) - v0) * d; },
           H + (long)h0 * d, [&](int i) { return (hrow(min(r0 + i, a.rows - 1)) - h0) * d; }, 0);
   f32x4 acc[NW][MW];
-  tile_mainloop<NW, MW, true>(sm, ld, d / TK, acc);
+  tile_mainloop<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX, true>(sm, ld, d / HEAD_KT, acc);
 
   // the main loop ended with a barrier: its LDS is free for the row records
   RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm.w[0][0]);
@@ -447,8 +449,10 @@ static void launch_rows(const HeadArgs &a, hipStream_t st) {
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
-  if (a.dtype == 1 && a.rows > 64 && a.d % TK == 0) {
-    constexpr int BM = 32 * HEAD_MW;
+  // the LDS kernel addresses a block's hidden rows with 32-bit byte offsets
+  constexpr int BM = 32 * HEAD_MW;
+  const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
+  if (a.dtype == 1 && a.rows > 64 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
     a.nvb = (a.vocab + HEAD_VB_LDS - 1) / HEAD_VB_LDS;
     const int nmb = (a.rows + BM - 1) / BM;
     const int nvb8 = (a.nvb + NXCD - 1) / NXCD * NXCD;

@@ -4,11 +4,17 @@
 // A workgroup of 4 waves (2 x 2) computes a BN x BM block of C = W . X^T,
 // W [N, K] the weight (MFMA A operand, output features), X [M, K] the
 // activations (MFMA B operand, rows); each wave owns NW x MW 16x16 tiles.
-// k advances in stages of 64: every thread copies NW + MW 16-byte vectors of
-// the next stage from global memory into registers while the waves multiply
-// the current stage out of LDS, then writes them to the other LDS buffer;
-// one barrier per stage.  LDS rows are padded by 16 bytes (row stride 144 B),
-// so the 16 rows one fragment read touches fall on distinct banks.
+// k advances in stages of KT through rings of LDS buffers filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the instruction's LDS base + 16 * lane), issued ahead of the multiply: the copies need no registers and no LDS write
+// instructions, and the only wait is one vmcnt + barrier per stage.  The
+// loads are issued from inline assembly with an explicit vmcnt, because the
+// compiler, which cannot tell the ring buffers apart, would otherwise wait
+// for every outstanding copy before each LDS read.
+//
+// LDS rows are KT * 2 bytes (unpadded); 16-byte chunk c of row r sits at
+// chunk c ^ tile_swz(r), so the 16 rows of one fragment read (contiguous
+// rows, or the permuted rows below) fall on 16 distinct bank groups.
 //
 // PERM: inside each pair of vocabulary tiles, A-operand row 4q + e of tile
 // 2p + s is output feature 32p + 8q + 4s + e, so lane group g ends up with
@@ -16,72 +22,110 @@
 // the LM head's sampling epilogue).
 #pragma once
 
+#include <cstdint>
+
 #include "common.hpp"
 
 namespace dstill {
 
-constexpr int TK = 64;       // k per LDS stage
-constexpr int TKP = TK + 8;  // padded LDS row (elements)
-
-template <int NW, int MW>
+// KT: k per LDS stage (64 or 32).  W stages sit in a ring of NSW buffers,
+// X stages in a ring of NSX: the weight, streamed once from HBM, is fetched
+// NSW - 1 stages ahead of the multiply, the activations (re-read by every
+// weight block, mostly from L2) NSX - 1 stages ahead.  A row of a stage is
+// KT * 2 bytes, CPR = KT / 8 chunks of 16 bytes; one copy instruction (64
+// lanes x 16 bytes) fills RPI = 1024 / (KT * 2) rows.
+template <int NW, int MW, int KT, int NSW, int NSX>
 struct TileSmem {
+  static_assert(KT == 64 || KT == 32, "stage depth");
+  static_assert(NSX == 2 && (NSW == 2 || NSW == 3), "ring depths");
   static constexpr int BN = 32 * NW, BM = 32 * MW;
-  bf16 w[2][BN * TKP];
-  bf16 x[2][BM * TKP];
+  bf16 w[NSW][BN * KT];
+  bf16 x[NSX][BM * KT];
 };
 
-// One stage of a workgroup's W and X tiles held in registers.
-template <int NW, int MW>
-struct TileRegs {
-  bf16x8 w[NW], x[MW];
-};
+// Chunk swizzle.  KT = 64 (8 chunks, 2 rows per 256-byte bank window): bits
+// (r1, r3, r2 ^ r4); KT = 32 (4 chunks, 4 rows per window): bits (r2 ^ r4,
+// r3).  Over 16 contiguous rows (r0..r3 vary) and over the permuted rows of
+// one tile (r0, r1, r3, r4 vary) the 16-byte slot of a given logical chunk
+// within its bank window takes 16 distinct values.
+template <int KT>
+__device__ __forceinline__ int tile_swz(int r) {
+  if (KT == 64) return ((r >> 1) & 1) | ((r >> 2) & 2) | ((((r >> 2) ^ (r >> 4)) & 1) << 2);
+  return (((r >> 2) ^ (r >> 4)) & 1) | ((r >> 2) & 2);
+}
 
-// Global -> register -> LDS copier for one workgroup's W and X tiles.  Each
-// matrix is addressed from one wave-uniform base (the block's first row,
-// advanced by whole stages) plus a 32-bit per-thread element offset, which
-// keeps the per-thread address state small.
-template <int NW, int MW>
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One direct global->LDS copy of 16 bytes per lane: global address base +
+// voff (base wave-uniform, voff per lane, bytes), LDS address lds + 16 * lane
+// (lds wave-uniform).  M0 carries the LDS address; s_nop covers the M0 write
+// -> LDS-DMA read hazard.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(sl)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Copier for one workgroup's W and X tiles.  Per stage, each wave issues
+// NCW copies of W and NCX of X; copy i of wave w fills row group 4i + w (RPI
+// rows), lane L loading row RPI * group + L / CPR, logical chunk
+// (L % CPR) ^ tile_swz(row).  Each matrix is addressed from one wave-uniform
+// base (the block's first row, advanced by whole stages) plus a 32-bit
+// per-lane byte offset.
+template <int NW, int MW, int KT, int NSW, int NSX>
 struct TileLoader {
-  static constexpr int BN = 32 * NW, BM = 32 * MW;
-  const bf16 *wbase, *xbase;
-  int woff[NW], xoff[MW];
+  static constexpr int CPR = KT / 8, RPI = 64 / CPR;
+  static constexpr int NCW = 32 * NW / RPI / 4, NCX = 32 * MW / RPI / 4;
+  static constexpr int OPS = NCW + NCX;  // copies per wave per stage
+  const char *wbase, *xbase;
+  uint32_t woff[NCW], xoff[NCX];
 
-  // wrow(i) / xrow(i): element offset of tile row i from wb / xb (already
-  // clamped to a valid row; must fit in 31 bits); k0: first k of this
-  // workgroup's range.
+  // wrow(r) / xrow(r): element offset of tile row r from wb / xb (already
+  // clamped to a valid row; twice it must fit in 32 bits); k0: first k of
+  // this workgroup's range.
   template <typename WRow, typename XRow>
   __device__ __forceinline__ void init(const bf16 *wb, WRow wrow, const bf16 *xb, XRow xrow,
                                        long k0) {
-    wbase = wb + k0;
-    xbase = xb + k0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wbase = reinterpret_cast<const char *>(wb + k0);
+    xbase = reinterpret_cast<const char *>(xb + k0);
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      woff[i] = wrow(idx >> 3) + (idx & 7) * 8;
+    for (int i = 0; i < NCW; ++i) {
+      const int r = RPI * (4 * i + wave) + lane / CPR;
+      woff[i] = (uint32_t)wrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      xoff[i] = xrow(idx >> 3) + (idx & 7) * 8;
+    for (int i = 0; i < NCX; ++i) {
+      const int r = RPI * (4 * i + wave) + lane / CPR;
+      xoff[i] = (uint32_t)xrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
     }
   }
-  __device__ __forceinline__ void load(TileRegs<NW, MW> &r, int stage) const {
-    const bf16 *wb = wbase + (long)stage * TK;
-    const bf16 *xb = xbase + (long)stage * TK;
+  __device__ __forceinline__ void issue_w(TileSmem<NW, MW, KT, NSW, NSX> &sm, int stage) const {
+    const char *wb = wbase + (long)stage * KT * 2;
+    const uint32_t wl = lds_u32(&sm.w[stage % NSW][0]) + (threadIdx.x >> 6) * 1024;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) r.w[i] = *reinterpret_cast<const bf16x8 *>(wb + woff[i]);
-#pragma unroll
-    for (int i = 0; i < MW; ++i) r.x[i] = *reinterpret_cast<const bf16x8 *>(xb + xoff[i]);
+    for (int i = 0; i < NCW; ++i) dma16(wb, woff[i], wl + i * 4096);
   }
-  __device__ __forceinline__ void store(TileSmem<NW, MW> &sm, int buf,
-                                        const TileRegs<NW, MW> &r) const {
-    const int base = (threadIdx.x >> 3) * TKP + (threadIdx.x & 7) * 8;
+  __device__ __forceinline__ void issue_x(TileSmem<NW, MW, KT, NSW, NSX> &sm, int stage) const {
+    const char *xb = xbase + (long)stage * KT * 2;
+    const uint32_t xl = lds_u32(&sm.x[stage % NSX][0]) + (threadIdx.x >> 6) * 1024;
 #pragma unroll
-    for (int i = 0; i < NW; ++i)
-      *reinterpret_cast<bf16x8 *>(&sm.w[buf][base + 32 * TKP * i]) = r.w[i];
-#pragma unroll
-    for (int i = 0; i < MW; ++i)
-      *reinterpret_cast<bf16x8 *>(&sm.x[buf][base + 32 * TKP * i]) = r.x[i];
+    for (int i = 0; i < NCX; ++i) dma16(xb, xoff[i], xl + i * 4096);
   }
 };
 
@@ -92,9 +136,18 @@ __device__ __forceinline__ int tile_a_row(int wn, int i, int r16) {
   return wn * 16 * NW + 16 * i + r16;
 }
 
-template <int NW, int MW, bool PERM>
-__device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW> &sm, TileLoader<NW, MW> &ld,
-                                              int nst, f32x4 (&acc)[NW][MW]) {
+// Byte offset of lane (g, r16)'s 16-byte k-chunk 4 kk + g of LDS row r.
+template <int KT>
+__device__ __forceinline__ int tile_frag_off(int r, int kk, int g) {
+  return r * (KT * 2) + (((4 * kk + g) ^ tile_swz<KT>(r)) * 16);
+}
+
+template <int NW, int MW, int KT, int NSW, int NSX, bool PERM>
+__device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW, KT, NSW, NSX> &sm,
+                                              const TileLoader<NW, MW, KT, NSW, NSX> &ld, int nst,
+                                              f32x4 (&acc)[NW][MW]) {
+  constexpr int NCW = TileLoader<NW, MW, KT, NSW, NSX>::NCW;
+  constexpr int NKK = KT / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int wn = wave & 1, wm = wave >> 1;
@@ -103,40 +156,49 @@ __device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW> &sm, TileLoader<N
 #pragma unroll
     for (int j = 0; j < MW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (nst <= 0) return;
-  int arow[NW], brow[MW];
+  int aoff[NW][NKK], boff[MW][NKK];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) arow[i] = tile_a_row<NW, PERM>(wn, i, r16) * TKP + 8 * g;
+  for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-  for (int j = 0; j < MW; ++j) brow[j] = (wm * 16 * MW + 16 * j + r16) * TKP + 8 * g;
-
-  auto compute = [&](int cur) {
-    const bf16 *ws = sm.w[cur];
-    const bf16 *xs = sm.x[cur];
+    for (int i = 0; i < NW; ++i)
+      aoff[i][kk] = tile_frag_off<KT>(tile_a_row<NW, PERM>(wn, i, r16), kk, g);
 #pragma unroll
-    for (int kk = 0; kk < TK / 32; ++kk) {
+    for (int j = 0; j < MW; ++j) boff[j][kk] = tile_frag_off<KT>(wm * 16 * MW + 16 * j + r16, kk, g);
+  }
+  auto compute = [&](int s) {
+    const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
+    const char *xs = reinterpret_cast<const char *>(&sm.x[s % NSX][0]);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 a[NW], b[MW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(ws + arow[i] + 32 * kk);
+      for (int i = 0; i < NW; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
 #pragma unroll
-      for (int j = 0; j < MW; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(xs + brow[j] + 32 * kk);
+      for (int j = 0; j < MW; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
 #pragma unroll
       for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
     }
   };
-  // stage s lives in LDS buffer s & 1; the next stage waits in registers
-  TileRegs<NW, MW> r;
-  ld.load(r, 0);
-  ld.store(sm, 0, r);
-  __syncthreads();
+  // Issue order: W0, X0, (W1 if NSW = 3); then per stage s, after its wait:
+  // X(s + 1), W(s + NSW - 1).  So when stage s is waited for, the only copies
+  // issued after X(s) are W(s + 1) (NSW = 3, if it exists), and W(s) was
+  // issued before X(s) (NSW = 3) or right after it (NSW = 2).
+  ld.issue_w(sm, 0);
+  ld.issue_x(sm, 0);
+  if (NSW == 3 && nst > 1) ld.issue_w(sm, 1);
   for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) ld.load(r, s + 1);
-    compute(cur);
-    if (s + 1 < nst) ld.store(sm, cur ^ 1, r);
+    if (NSW == 3 && s + 1 < nst) wait_vmcnt<NCW>();
+    else wait_vmcnt<0>();
+    // every wave's copies of stage s are visible after the barrier, and the
+    // buffers refilled next (last read at stage s - 1) are free
     __syncthreads();
+    if (s + 1 < nst) ld.issue_x(sm, s + 1);
+    if (s + NSW - 1 < nst) ld.issue_w(sm, s + NSW - 1);
+    compute(s);
   }
+  __syncthreads();  // every wave is done with the rings: the caller may reuse them
 }
 
 // XCD-aware placement: workgroup L runs on XCD L mod 8.  The m-blocks of one
