@@ -90,7 +90,10 @@ struct AttnPlan {
   int split, nsplit;
 };
 AttnPlan attn_plan(int max_ctx, int pairs) {
-  const long want = ((long)max_ctx * pairs + 2047) / 2048;
+  // about 1536 splits of the longest context over all (sequence, kv head)
+  // pairs: ~3 rounds of two workgroups per compute unit, long enough that
+  // each workgroup's start and end costs are small next to its streaming
+  const long want = ((long)max_ctx * pairs + 1535) / 1536;
   // at most 128 splits (the merge kernel stages one weight per split)
   const long floor_split = std::max<long>(128, ((long)max_ctx + 127) / 128);
   int split = (int)std::max<long>(floor_split, (want + 63) / 64 * 64);

@@ -7,18 +7,19 @@
 // scaled by 1/sqrt(dh), through a softmax over all S_b + B keys.
 //
 // Work decomposition ("split context"): one workgroup per (split, kv head,
-// sequence-copy).  Its first `group` waves each own one query head of the GQA
-// group, i.e. B <= 16 query rows (one 16-row MFMA tile).  The workgroup walks
-// its context range in chunks of 64 keys, computes S^T = K Q^T and
-// O^T = V^T P^T on the matrix cores and keeps an online softmax per query;
-// split 0 also takes the block keys.  Chunks are pipelined: the next chunk's
-// K and V^T are loaded into registers while the waves work on the current
-// one out of LDS, then written to the other LDS buffer (one barrier per
-// chunk).  The V cache is stored in tiles of 64 keys, each d-major
-// ([cap/64][dh][64] per sequence and head), so V^T of a chunk is one
-// contiguous 16 KB block, like the chunk of K.  The
-// partial (m, l, O) of every split is merged by attn_combine with the
-// log-sum-exp rule, which reproduces the single softmax up to rounding.
+// sequence-copy), placed by split_coords.  Its query waves each own one
+// query head of the GQA group, i.e. B <= 16 query rows (one 16-row MFMA
+// tile).  The workgroup walks its context range in chunks of 64 keys,
+// computes S^T = K Q^T and O^T = V^T P^T on the matrix cores and keeps an
+// online softmax per query; split 0 also takes the block keys.  The V cache
+// is stored in tiles of 64 keys, each d-major ([cap/64][dh][64] per sequence
+// and head), so V^T of a chunk is one contiguous 16 KB block, like the chunk
+// of K.  bf16 chunks stream through a ring of LDS buffers filled by direct
+// global->LDS copies (attn_split_dma_kernel); fp32 chunks, and bf16 shapes
+// whose copies do not split evenly over the waves, are staged through
+// registers (attn_split_kernel).  The partial (m, l, O) of every split is
+// merged by attn_combine with the log-sum-exp rule, which reproduces the
+// single softmax up to rounding.
 //
 // Lane layout (see Mma in common.hpp): in S^T, lane l holds query l % 16 and,
 // with the key rows of each 32-key sub-chunk permuted so that tile t row
@@ -29,7 +30,10 @@
 // groups: two xor-shuffles (16, 32).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
+#include "dma.hpp"
 #include "kernels.hpp"
 
 namespace dstill {
@@ -93,25 +97,98 @@ struct ChunkLoader {
   }
 };
 
+// Where a chunk's elements sit in LDS.  PadLayout: the register-staged
+// buffers above (rows padded by one vector).  SwzLayout (bf16): the ring
+// buffers filled by direct copies, unpadded, 16-byte chunk c of a row at
+// chunk c ^ swz(row): K rows (dh * 2 bytes) swizzled on key bits
+// {0, 1, 3, 4}, the bits that vary across the 16 keys one fragment read
+// touches (see attend_chunk); V^T rows (128 bytes, two per 256-byte bank
+// window) on bits {1, 2, 3} of d.
+template <typename T, int DH>
+struct PadLayout {
+  static __device__ __forceinline__ const T *k(const T *base, int key, int col) {
+    return base + key * AttnSmem<T, DH>::KS + col;
+  }
+  static __device__ __forceinline__ const T *v(const T *base, int d, int key) {
+    return base + d * AttnSmem<T, DH>::VS + key;
+  }
+};
+
+template <int DH>
+struct SwzLayout {
+  static __device__ __forceinline__ int kswz(int key) {
+    if (DH == 128) return (key & 3) | (((key >> 3) & 3) << 2);
+    return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);
+  }
+  static __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+  static __device__ __forceinline__ int kbyte(int key, int chunk) {
+    return key * DH * 2 + ((chunk ^ kswz(key)) << 4);
+  }
+  static __device__ __forceinline__ int vbyte(int d, int chunk) {
+    return d * ATT_KC * 2 + ((chunk ^ vswz(d)) << 4);
+  }
+  static __device__ __forceinline__ const bf16 *k(const bf16 *base, int key, int col) {
+    return reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(base) +
+                                          kbyte(key, col >> 3));
+  }
+  static __device__ __forceinline__ const bf16 *v(const bf16 *base, int d, int key) {
+    return reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(base) +
+                                          vbyte(d, key >> 3));
+  }
+};
+
 template <typename T, int DH>
 struct WaveState {
   float m, l;
   f32x4 o[DH / 16];
 };
 
+// Online-softmax reference update for a new block of scores with per-query
+// max cmax (finite).  The reference m moves only when some query's max
+// exceeds it by more than RESCALE_LOG2 in log2 units (a wave-uniform branch);
+// until then probabilities up to 2^RESCALE_LOG2 accumulate against the old
+// reference, which l and O share, so their ratio is unchanged.  A split
+// starts at m = -inf and takes the first block's max.
+constexpr float RESCALE_LOG2 = 8.0f;
+
+template <int DH, typename WS>
+__device__ __forceinline__ void rescale(WS &ws, float cmax, float c) {
+  if (__any((cmax - ws.m) * c > RESCALE_LOG2)) {
+    const float mnew = fmaxf(ws.m, cmax);
+    const float alpha = __builtin_amdgcn_exp2f((ws.m - mnew) * c);
+    ws.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) ws.o[dt] *= alpha;
+    ws.m = mnew;
+  }
+}
+
+// Workgroup -> (split, kv head, sequence-copy).  The grid is one-dimensional
+// with the split index varying slowest: consecutive workgroups, which the
+// dispatcher deals round-robin to the 8 XCDs, are different (sequence, head)
+// pairs of the same split, so every XCD gets an even share of long and
+// short contexts (with the split fastest, XCD k would run every split k,
+// and the late splits of ragged contexts are mostly empty), and the busy
+// low splits are dispatched first.
+__device__ __forceinline__ void split_coords(const AttnArgs &a, int *sp, int *h, int *bc) {
+  const int pairs = a.hkv * a.bs * a.C;
+  const int L = blockIdx.x;
+  *sp = L / pairs;
+  *h = (L % pairs) % a.hkv;
+  *bc = (L % pairs) / a.hkv;
+}
+
 // One wave's pass over a staged chunk holding `nk` valid keys (1..64), with
 // one online-softmax update for the whole chunk.  Scores stay in raw units
-// (m is the running max of raw scores); probabilities are
+// (m is the reference max of raw scores); probabilities are
 // exp2(s * c - m * c) with c = log2(e) / sqrt(dh), one FMA and one v_exp_f32
-// each.  The accumulators are rescaled only when some query's max grows
-// (a wave-uniform branch), which after the first chunks is rare.
-template <typename T, int DH>
+// each.
+template <typename T, int DH, class Lay>
 __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
                                              const T *__restrict__ vt_lds,
                                              const typename Mma<T>::frag *qf, int nk, float c,
                                              WaveState<T, DH> &ws) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
-  constexpr int KS = AttnSmem<T, DH>::KS, VS = AttnSmem<T, DH>::VS;
   typedef typename Mma<T>::frag F;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int nsub = nk > 32 ? 2 : 1;  // 32-key sub-chunks holding a valid key
@@ -124,10 +201,10 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
     if ((t >> 1) < nsub) {
       s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int krow = 32 * (t >> 1) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3);
-      const T *kp = ks_lds + krow * KS + VEC * g;
 #pragma unroll
       for (int ks = 0; ks < DH / KW; ++ks)
-        s[t] = Mma<T>::run(*reinterpret_cast<const F *>(kp + ks * KW), qf[ks], s[t]);
+        s[t] = Mma<T>::run(*reinterpret_cast<const F *>(Lay::k(ks_lds, krow, ks * KW + VEC * g)),
+                           qf[ks], s[t]);
     }
   }
   if (nk < ATT_KC) {
@@ -143,15 +220,8 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
                            fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, WAVE));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, WAVE));
-  const float mnew = fmaxf(ws.m, cmax);
-  if (__any(mnew > ws.m)) {
-    const float alpha = __builtin_amdgcn_exp2f((ws.m - mnew) * c);
-    ws.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) ws.o[dt] *= alpha;
-  }
-  ws.m = mnew;
-  const float mc = mnew * c;
+  rescale<DH>(ws, cmax, c);
+  const float mc = ws.m * c;
   float p[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -181,14 +251,64 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
       }
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
-      const T *vp = vt_lds + (dt * 16 + r16) * VS + sc * 32 + 8 * g;
 #pragma unroll
       for (int f = 0; f < NPF; ++f) {
-        const F vf = *reinterpret_cast<const F *>(vp + f * VEC);
+        const F vf =
+            *reinterpret_cast<const F *>(Lay::v(vt_lds, dt * 16 + r16, sc * 32 + 8 * g + f * VEC));
         ws.o[dt] = Mma<T>::run(vf, pf[f], ws.o[dt]);
         if (SPLIT) ws.o[dt] = Mma<T>::run(vf, pl[f], ws.o[dt]);
       }
     }
+  }
+}
+
+// One wave's pass over the 32-key sub-chunk `sub` of a staged chunk, of which
+// the first nk (1..32) keys are valid: two S^T tiles, one online-softmax
+// update, one P.V pass (same lane layout as attend_chunk).
+template <int DH, class Lay>
+__device__ __forceinline__ void attend_sub(const bf16 *__restrict__ ks_lds,
+                                           const bf16 *__restrict__ vt_lds, const bf16x8 *qf,
+                                           int sub, int nk, float c, WaveState<bf16, DH> &ws) {
+  typedef bf16x8 F;
+  constexpr int KW = 32;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  f32x4 s[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int krow = 32 * sub + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < DH / KW; ++ks)
+      s[t] = Mma<bf16>::run(*reinterpret_cast<const F *>(Lay::k(ks_lds, krow, ks * KW + 8 * g)),
+                            qf[ks], s[t]);
+  }
+  if (nk < 32) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (8 * g + 4 * t + i >= nk) s[t][i] = -INFINITY;
+  }
+  float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, WAVE));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, WAVE));
+  rescale<DH>(ws, cmax, c);
+  const float mc = ws.m * c;
+  F pf, pl;
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) {
+    const float pv = __builtin_amdgcn_exp2f(fmaf(s[k8 >> 2][k8 & 3], c, -mc));
+    ws.l += pv;
+    const bf16 hi = from_f32<bf16>(pv);
+    pf[k8] = hi;
+    pl[k8] = from_f32<bf16>(pv - to_f32(hi));
+  }
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) {
+    const F vf = *reinterpret_cast<const F *>(Lay::v(vt_lds, dt * 16 + r16, sub * 32 + 8 * g));
+    ws.o[dt] = Mma<bf16>::run(vf, pf, ws.o[dt]);
+    ws.o[dt] = Mma<bf16>::run(vf, pl, ws.o[dt]);
   }
 }
 
@@ -197,7 +317,8 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
   typedef typename Mma<T>::frag F;
   __shared__ AttnSmem<T, DH> sm;
-  const int sp = blockIdx.x, h = blockIdx.y, bc = blockIdx.z;
+  int sp, h, bc;
+  split_coords(a, &sp, &h, &bc);
   const int b = bc / a.C;
   const int S = a.eff_ctx[b];
   const int k_beg = sp * a.split;
@@ -247,7 +368,7 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   for (int c = 0; c < nchunk; ++c) {
     const int cur = c & 1;
     if (c + 1 < nchunk) issue(c + 1);
-    if (active) attend_chunk<T, DH>(sm.k[cur], sm.vt[cur], qf, nk, c_log2, st);
+    if (active) attend_chunk<T, DH, PadLayout<T, DH>>(sm.k[cur], sm.vt[cur], qf, nk, c_log2, st);
     if (c + 1 < nchunk) {
       nk = ld.nk;
       ld.store(sm, cur ^ 1);
@@ -267,6 +388,207 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
       *reinterpret_cast<f32x4 *>(op + dt * 16 + 4 * g) = st.o[dt];
     if (g == 0) {
       a.mlpart[rec * 2] = st.m * c_log2;  // running max in log2 units
+      a.mlpart[rec * 2 + 1] = st.l;
+    }
+  }
+}
+
+// bf16 variant fed by direct global->LDS copies: the context chunks stream
+// through a ring of ATT_NS buffers, ATT_NS - 1 chunks ahead of the waves
+// (K and V^T of a cached chunk are each one contiguous block of 64 keys).
+// A ring of two (64 KB at dh = 128) lets two workgroups share a compute
+// unit, so one's start (Q load, first copy) and end (merge, partial record)
+// overlap the other's streaming.
+// Split 0 first takes its B block keys, staged through registers into the
+// ring buffer the prologue leaves free.  A last chunk holding nk < 64 valid
+// keys has its V^T columns nk..63 zeroed in LDS once its copies have landed,
+// so whatever the cache holds beyond the context cannot reach P.V; its K rows
+// are covered by the score mask.
+constexpr int ATT_NS = 2;
+static_assert(ATT_NS >= 2 && ATT_NS <= 4, "the wait ladder covers rings of 2 to 4");
+
+template <int DH>
+struct AttnRing {
+  bf16 k[ATT_NS][ATT_KC * DH];
+  bf16 vt[ATT_NS][DH * ATT_KC];
+};
+
+template <int DH, int NTHR, int KSPLIT>
+__global__ __launch_bounds__(NTHR) void attn_split_dma_kernel(AttnArgs a) {
+  using T = bf16;
+  using Lay = SwzLayout<DH>;
+  constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
+  constexpr int NWV = NTHR / 64;
+  constexpr int CPK = ATT_KC * DH * 2 / 1024;  // copies per chunk, K (and V^T)
+  constexpr int PER = CPK / NWV;               // copies per wave per chunk, each of K and V^T
+  constexpr int OPS = 2 * PER;
+  constexpr int KROWS = 1024 / (DH * 2);       // K rows per copy
+  static_assert(CPK % NWV == 0, "copies must split evenly over the waves");
+  typedef typename Mma<T>::frag F;
+  __shared__ AttnRing<DH> sm;
+  int sp, h, bc;
+  split_coords(a, &sp, &h, &bc);
+  const int b = bc / a.C;
+  const int S = a.eff_ctx[b];
+  const int k_beg = sp * a.split;
+  if (sp > 0 && k_beg >= S) return;
+  const int k_end = min(k_beg + a.split, S);
+  const int group = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  // KSPLIT = 2: wave set ks = wave / group takes keys 32 ks .. 32 ks + 31 of
+  // every chunk with a softmax state of its own; the sets merge at the end
+  const int kset = wave / group;
+  const bool active = kset < KSPLIT;
+  const int head = h * group + (active ? wave % group : 0);
+
+  const int nctx = k_end > k_beg ? (k_end - k_beg + ATT_KC - 1) / ATT_KC : 0;
+  const T *kcache = (const T *)a.kc + ((long)b * a.hkv + h) * a.cap * DH;
+  const T *vcache = (const T *)a.vc + ((long)b * a.hkv + h) * DH * a.cap;
+  // per-lane byte offsets of this wave's copies within a chunk: copy j of
+  // wave w fills LDS bytes [1024 q, 1024 q + 1024), q = j * NWV + w
+  uint32_t koff[PER], voff[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int q = j * NWV + wave;
+    const int key = q * KROWS + lane / (DH / 8), kch = (lane % (DH / 8)) ^ Lay::kswz(key);
+    koff[j] = (uint32_t)(key * DH * 2 + kch * 16);
+    const int d = q * 8 + lane / 8, vch = (lane % 8) ^ Lay::vswz(d);
+    voff[j] = (uint32_t)(d * ATT_KC * 2 + vch * 16);
+  }
+  auto issue = [&](int c) {
+    const int k0 = k_beg + c * ATT_KC;
+    const T *kb = kcache + (long)k0 * DH, *vb = vcache + (long)k0 * DH;
+    const int slot = c % ATT_NS;
+    const uint32_t kl = lds_u32(&sm.k[slot][0]), vl = lds_u32(&sm.vt[slot][0]);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dma16(kb, koff[j], kl + (j * NWV + wave) * 1024);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dma16(vb, voff[j], vl + (j * NWV + wave) * 1024);
+  };
+  // Q^T fragments (B operand): query row r16 of this head.  Loaded and
+  // waited for before the first copy, so that no compiler-tracked load is in
+  // flight inside the chunk loop (the compiler would otherwise wait for all
+  // vector memory, the copies included, at their first use there).
+  F qf[DH / KW];
+  const T *qrow = (const T *)a.q + ((long)bc * a.B + r16) * a.hq * DH + head * DH + VEC * g;
+#pragma unroll
+  for (int ks = 0; ks < DH / KW; ++ks)
+    qf[ks] = (active && r16 < a.B) ? load_frag<T>(qrow + ks * KW) : zero_frag<T>();
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int p = 0; p < ATT_NS - 1; ++p)
+    if (p < nctx) issue(p);
+
+  WaveState<T, DH> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c_log2 = a.scale * 1.4426950408889634f;  // score -> log2 units
+
+  if (sp == 0) {
+    // block keys -> ring buffer ATT_NS - 1: K rows 0..B-1, V^T columns 0..B-1,
+    // every other V^T column zero
+    constexpr int BS = ATT_NS - 1;
+    const T *kblock = (const T *)a.kb + (long)bc * a.B * a.hkv * DH + (long)h * DH;
+    const T *vblock = (const T *)a.vb + ((long)bc * a.hkv + h) * DH * ATT_VBS;
+    char *kl = reinterpret_cast<char *>(&sm.k[BS][0]);
+    char *vl = reinterpret_cast<char *>(&sm.vt[BS][0]);
+    for (int i = threadIdx.x; i < a.B * (DH / 8); i += NTHR) {
+      const int key = i / (DH / 8), ch = i % (DH / 8);
+      *reinterpret_cast<F *>(kl + Lay::kbyte(key, ch)) =
+          load_frag<T>(kblock + (long)key * a.hkv * DH + ch * 8);
+    }
+    for (int i = threadIdx.x; i < DH * (ATT_KC / 8); i += NTHR) {
+      const int d = i / (ATT_KC / 8), ch = i % (ATT_KC / 8);
+      F v = zero_frag<T>();
+      if (ch * 8 < a.B) {  // ATT_VBS = 16 columns, the first B of them valid
+        v = load_frag<T>(vblock + (long)d * ATT_VBS + ch * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (ch * 8 + e >= a.B) v[e] = T(0.0f);
+      }
+      *reinterpret_cast<F *>(vl + Lay::vbyte(d, ch)) = v;
+    }
+    __syncthreads();
+    if (KSPLIT == 1) {
+      if (active) attend_chunk<T, DH, Lay>(sm.k[BS], sm.vt[BS], qf, a.B, c_log2, st);
+    } else if (kset == 0) {  // B <= 16 keys: all in the first sub-chunk
+      attend_sub<DH, Lay>(sm.k[BS], sm.vt[BS], qf, 0, a.B, c_log2, st);
+    }
+  }
+
+  for (int c = 0; c < nctx; ++c) {
+    // this wave's copies of chunk c are done once at most the copies of the
+    // chunks after it (up to ATT_NS - 2) are outstanding
+    const int ahead = min(nctx - 1 - c, ATT_NS - 2);
+    if (ATT_NS >= 4 && ahead >= 2) wait_vmcnt<2 * OPS>();
+    else if (ATT_NS >= 3 && ahead >= 1) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's copies visible; slot (c - 1) % ATT_NS free
+    const int slot = c % ATT_NS;
+    const int nk = min(ATT_KC, k_end - (k_beg + c * ATT_KC));
+    if (nk < ATT_KC) {
+      char *vl = reinterpret_cast<char *>(&sm.vt[slot][0]);
+      for (int i = threadIdx.x; i < DH * (ATT_KC / 8); i += NTHR) {
+        const int d = i / (ATT_KC / 8), ch = i % (ATT_KC / 8);
+        if (ch * 8 + 8 <= nk) continue;
+        F *p = reinterpret_cast<F *>(vl + Lay::vbyte(d, ch));
+        F v = *p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (ch * 8 + e >= nk) v[e] = T(0.0f);
+        *p = v;
+      }
+      __syncthreads();
+    }
+    if (c + ATT_NS - 1 < nctx) issue(c + ATT_NS - 1);
+    if (KSPLIT == 1) {
+      if (active) attend_chunk<T, DH, Lay>(sm.k[slot], sm.vt[slot], qf, nk, c_log2, st);
+    } else if (active) {
+      const int nks = min(32, nk - 32 * kset);
+      if (nks > 0) attend_sub<DH, Lay>(sm.k[slot], sm.vt[slot], qf, kset, nks, c_log2, st);
+    }
+  }
+  if constexpr (KSPLIT == 2) {
+    // set 1 hands its (m, l, O) to set 0 through the (now idle) ring: per
+    // head and lane, 4 f32 of O per dh tile, then l and m
+    constexpr int REC = DH / 4 + 4;  // floats per lane record (16-byte multiple)
+    static_assert(NTHR / 64 / KSPLIT * 64 * REC * 4 <= (int)sizeof(AttnRing<DH>),
+                  "merge staging must fit the ring");
+    float *xs = reinterpret_cast<float *>(&sm) + (long)((wave % group) * 64 + lane) * REC;
+    __syncthreads();
+    if (kset == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) *reinterpret_cast<f32x4 *>(xs + 4 * dt) = st.o[dt];
+      xs[DH / 4] = st.l;
+      xs[DH / 4 + 1] = st.m;
+    }
+    __syncthreads();
+    if (kset != 0) return;
+    const float m1 = xs[DH / 4 + 1];
+    const float mm = fmaxf(st.m, m1);  // finite: set 0 always saw a key
+    const float a0 = __builtin_amdgcn_exp2f((st.m - mm) * c_log2);
+    const float a1 = __builtin_amdgcn_exp2f((m1 - mm) * c_log2);
+    st.l = a0 * st.l + a1 * xs[DH / 4];
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      st.o[dt] = a0 * st.o[dt] + a1 * *reinterpret_cast<const f32x4 *>(xs + 4 * dt);
+    st.m = mm;
+  }
+  if (!active) return;
+
+  st.l += __shfl_xor(st.l, 16, WAVE);
+  st.l += __shfl_xor(st.l, 32, WAVE);
+  if (r16 < a.B) {
+    const long rec = (((long)bc * a.hq + head) * a.nsplit + sp) * a.B + r16;
+    float *op = a.opart + rec * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<f32x4 *>(op + dt * 16 + 4 * g) = st.o[dt];
+    if (g == 0) {
+      a.mlpart[rec * 2] = st.m * c_log2;
       a.mlpart[rec * 2 + 1] = st.l;
     }
   }
@@ -305,16 +627,47 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 template <typename T, int DH, int NTHR>
 static void launch_nthr(const AttnArgs &a, hipStream_t st) {
-  dim3 grid(a.nsplit, a.hkv, a.bs * a.C);
+  const dim3 grid(a.nsplit * a.hkv * a.bs * a.C);
   hipLaunchKernelGGL((attn_split_kernel<T, DH, NTHR>), grid, dim3(NTHR), 0, st, a);
+}
+
+// Whether two wave sets of NTHR / 128 heads can merge through the ring.
+template <int DH, int NTHR>
+constexpr bool ksplit_fits() {
+  return NTHR / 128 * 64 * (DH / 4 + 4) * 4 <= (int)sizeof(AttnRing<DH>);
+}
+
+template <int DH, int NTHR, int KSPLIT>
+static void launch_dma(const AttnArgs &a, hipStream_t st) {
+  const dim3 grid(a.nsplit * a.hkv * a.bs * a.C);
+  hipLaunchKernelGGL((attn_split_dma_kernel<DH, NTHR, KSPLIT>), grid, dim3(NTHR), 0, st, a);
 }
 
 template <typename T, int DH>
 static void launch_typed(const AttnArgs &a, hipStream_t st) {
   const int group = a.hq / a.hkv;
-  if (group <= 4) launch_nthr<T, DH, 256>(a, st);
-  else if (group <= 8) launch_nthr<T, DH, 512>(a, st);
-  else launch_nthr<T, DH, 1024>(a, st);
+  if constexpr (std::is_same<T, bf16>::value) {
+    // direct-copy ring; two wave sets per head while they fit in 1024 threads
+    // and their merge fits the ring
+    // (the K and V^T copies of a chunk must split evenly over the waves)
+    constexpr int CPK = ATT_KC * DH * 2 / 1024;
+    if (group <= 4) launch_dma<DH, 512, 2>(a, st);
+    else if constexpr (CPK % 16 == 0) {
+      if constexpr (ksplit_fits<DH, 1024>()) {
+        if (group <= 8) launch_dma<DH, 1024, 2>(a, st);
+        else launch_dma<DH, 1024, 1>(a, st);
+      } else {
+        launch_dma<DH, 1024, 1>(a, st);
+      }
+    } else {
+      if (group <= 8) launch_nthr<T, DH, 512>(a, st);
+      else launch_nthr<T, DH, 1024>(a, st);
+    }
+  } else {
+    if (group <= 4) launch_nthr<T, DH, 256>(a, st);
+    else if (group <= 8) launch_nthr<T, DH, 512>(a, st);
+    else launch_nthr<T, DH, 1024>(a, st);
+  }
   const int rows_per_wg = 128 / (a.dh / 4);
   hipLaunchKernelGGL(attn_combine_kernel<T>,
                      dim3(a.bs * a.C, a.hq, (a.B + rows_per_wg - 1) / rows_per_wg), dim3(128), 0,

@@ -25,6 +25,7 @@
 #include <cstdint>
 
 #include "common.hpp"
+#include "dma.hpp"
 
 namespace dstill {
 
@@ -52,33 +53,6 @@ template <int KT>
 __device__ __forceinline__ int tile_swz(int r) {
   if (KT == 64) return ((r >> 1) & 1) | ((r >> 2) & 2) | ((((r >> 2) ^ (r >> 4)) & 1) << 2);
   return (((r >> 2) ^ (r >> 4)) & 1) | ((r >> 2) & 2);
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// One direct global->LDS copy of 16 bytes per lane: global address base +
-// voff (base wave-uniform, voff per lane, bytes), LDS address lds + 16 * lane
-// (lds wave-uniform).  M0 carries the LDS address; s_nop covers the M0 write
-// -> LDS-DMA read hazard.
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
-  const uint64_t b = (uint64_t)base;
-  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sb), "s"(sl)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Copier for one workgroup's W and X tiles.  Per stage, each wave issues
