@@ -221,9 +221,13 @@ __device__ __forceinline__ float u24(uint32_t x) {
   return (float)((x >> 8) | 1u) * 5.9604644775390625e-08f;
 }
 
-// Standard Gumbel draw g = -log(-log u); logf is the accurate device log.
+// Standard Gumbel draw g = -log(-log u), through the hardware base-2
+// logarithm (v_log_f32, ~1 ulp on the normal inputs that occur here: u and
+// -log u lie in [2^-25, 17.4]); g is off by a few ulp, far inside the
+// near-tie band that decides which argmaxes are compared exactly.
 __device__ __forceinline__ float gumbel_of(uint32_t x) {
-  return -logf(-logf(u24(x)));
+  constexpr float LN2 = 0.6931471805599453f;
+  return -LN2 * __builtin_amdgcn_logf(-LN2 * __builtin_amdgcn_logf(u24(x)));
 }
 
 // Argmax merge with lowest-index tie-break; `second` tracks the runner-up

@@ -140,7 +140,8 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (vw + 32 * p + 8 * g + e < V) st.s += expf(zz[p][e] * invT - st.m);
+        if (vw + 32 * p + 8 * g + e < V)
+          st.s += __builtin_amdgcn_exp2f((zz[p][e] * invT - st.m) * 1.4426950408889634f);
   }
   st = rowstat_shfl_xor(st, 16);
   st = rowstat_shfl_xor(st, 32);

@@ -152,12 +152,37 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
     }
   };
   if ((V & 7) == 0) {
-    // 8 consecutive ids per thread per step (v0 and v1 are multiples of 8)
+    // 8 consecutive ids per thread per step (v0 and v1 are multiples of 8):
+    // the running max moves once per group (one fp64 rescale), the 8 terms
+    // exp(y - m) <= 1 are summed in fp32 with the hardware exp2 and folded
+    // into the fp64 sum once
     for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * blockDim.x) {
       float x[8];
       ld8(z + v, x);
+      bool fin = true;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) push(x[e], v + e);
+      for (int e = 0; e < 8; ++e) fin = fin && isfinite(x[e]);
+      if (!fin) {  // rare: element by element, skipping (and flagging) non-finite ones
+#pragma unroll
+        for (int e = 0; e < 8; ++e) push(x[e], v + e);
+        continue;
+      }
+      float gm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        top2_push(arg, x[e], v + e);
+        gm = fmaxf(gm, x[e] * invT);
+      }
+      if (gm > m) {
+        s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
+        m = gm;
+      }
+      const float mc = m * 1.4426950408889634f;
+      float s8 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        s8 += __builtin_amdgcn_exp2f(fmaf(x[e] * invT, 1.4426950408889634f, -mc));
+      s += (double)s8;
     }
   } else {
     for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) push(ld(z, v), v);
