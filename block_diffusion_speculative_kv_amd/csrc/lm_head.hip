@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "dma.hpp"
 #include "mma_tile.hpp"
 
 namespace dstill {
@@ -218,9 +219,13 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
   }
 }
 
-// LDS-tiled variant for batch-scale row counts (bf16).
+// LDS-tiled variant (bf16): 128 vocabulary ids x 32 * MW rows per
+// workgroup.  MW = 4 at batch scale; MW = 1 or 2 for up to 32 or 64 rows,
+// where each weight tile has a single reader and the direct-copy ring keeps
+// two stages of it in flight per workgroup.
+template <int MW>
 __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
-  constexpr int NW = HEAD_NW, MW = HEAD_MW;
+  constexpr int NW = HEAD_NW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
   __shared__ TileSmem<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> sm;
   int vb, rb;
@@ -263,21 +268,20 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   }
 }
 
-// Weight-streaming variant for up to 64 rows (bf16): the weight tile of 128
-// vocabulary rows is staged through LDS in k-stages of 256 so that every
-// global load instruction reads long contiguous runs (2 rows x 512 bytes per
-// wave), which the MFMA fragment layout (16 rows x 64 bytes per instruction)
-// cannot; the hidden rows are small and read straight from global memory.
-// LDS rows are unpadded and XOR-swizzled per 16-byte chunk, so that the 16
-// rows one fragment read touches (in the permuted vocabulary order) fall on
-// distinct banks.
+// Weight-streaming variant for up to 16 rows (bf16, one row tile): the
+// weight tile of 128 vocabulary rows streams through a two-stage LDS ring in
+// k-stages of 256 (512 contiguous bytes of every row per stage, 64 KB),
+// filled by direct global->LDS copies one stage ahead; the hidden row
+// fragments of the next stage are loaded into the other of two register sets
+// meanwhile.  LDS rows are unpadded and XOR-swizzled per 16-byte chunk, so
+// the 16 rows one fragment read touches (in the permuted vocabulary order)
+// fall on distinct banks.
 constexpr int HS_K = 256;       // k per stage
 constexpr int HS_ROWS = 128;    // vocabulary rows per workgroup (32 per wave)
-constexpr int HS_VEC = HS_ROWS * HS_K / 8 / 256;  // 16-byte vectors per thread per stage
+constexpr int HS_COPIES = HS_ROWS * HS_K * 2 / 1024 / 4;  // direct copies per wave per stage
 
 __device__ __forceinline__ int hs_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
 
-template <int MT>
 __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a) {
   __shared__ bf16 wsm[2][HS_ROWS * HS_K];
   const int vb = blockIdx.x;
@@ -285,91 +289,90 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a) {
   const int g = lane >> 4, r16 = lane & 15;
   const int V = a.vocab, d = a.d;
   const int v0 = vb * HS_ROWS;
-  const bf16 *W = (const bf16 *)a.w;
-  // loader: vector q = tid + 256 i holds tile row q >> 5, physical chunk q & 31
-  int goff[HS_VEC];
+  const char *wblk = reinterpret_cast<const char *>((const bf16 *)a.w + (long)v0 * d);
+  // copy j of wave w fills LDS vectors 64 (4 j + w) + lane: tile row
+  // 2 (4 j + w) + lane / 32, physical chunk lane % 32
+  uint32_t goff[HS_COPIES];
 #pragma unroll
-  for (int i = 0; i < HS_VEC; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    const int row = q >> 5, pc = q & 31;
-    goff[i] = (min(v0 + row, V - 1) - v0) * d + 8 * (pc ^ hs_swz(row));
+  for (int j = 0; j < HS_COPIES; ++j) {
+    const int row = 2 * (4 * j + wave) + (lane >> 5), pc = lane & 31;
+    goff[j] = (uint32_t)((min(v0 + row, V - 1) - v0) * d * 2 + 16 * (pc ^ hs_swz(row)));
   }
-  const bf16 *wblk = W + (long)v0 * d;
-  bf16x8 st[HS_VEC];
-  auto gload = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < HS_VEC; ++i)
-      st[i] = *reinterpret_cast<const bf16x8 *>(wblk + (long)s * HS_K + goff[i]);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < HS_VEC; ++i)
-      *reinterpret_cast<bf16x8 *>(&wsm[buf][(threadIdx.x + 256 * i) * 8]) = st[i];
-  };
   // A-operand rows of this wave's tile pair (permuted vocabulary order)
   int arow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) arow[t] = 32 * wave + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-  const bf16 *xp[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = min(16 * t + r16, a.rows - 1);
-    const long hrow = (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq;
-    xp[t] = (const bf16 *)a.hidden + hrow * d + 8 * g;
-  }
-  f32x4 acc[2][MT];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < MT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r = min(r16, a.rows - 1);
+  const bf16 *xp = (const bf16 *)a.hidden +
+                   ((long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq) * d + 8 * g;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const int nst = d / HS_K;
   // each block starts its k walk at a different stage, so concurrent blocks
   // do not sweep the same column offset of their rows at the same time
   const int rot = (vb * 5) % nst;
   auto kst = [&](int s) { return s + rot < nst ? s + rot : s + rot - nst; };
-  gload(kst(0));
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) gload(kst(s + 1));
-    const bf16 *ws = wsm[cur];
+  auto issue = [&](int s, int buf) {
+    const char *src = wblk + (long)kst(s) * HS_K * 2;
+    const uint32_t l = lds_u32(&wsm[buf][0]) + wave * 1024;
+#pragma unroll
+    for (int j = 0; j < HS_COPIES; ++j) dma16(src, goff[j], l + j * 4096);
+  };
+  auto xload = [&](int s, bf16x8 (&xf)[HS_K / 32]) {
+#pragma unroll
+    for (int kk = 0; kk < HS_K / 32; ++kk)
+      xf[kk] = *reinterpret_cast<const bf16x8 *>(xp + (long)kst(s) * HS_K + kk * 32);
+  };
+  auto compute = [&](int buf, const bf16x8 (&xf)[HS_K / 32]) {
+    const bf16 *ws = wsm[buf];
 #pragma unroll
     for (int kk = 0; kk < HS_K / 32; ++kk) {
-      bf16x8 fa[2], fb[MT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        fa[t] = *reinterpret_cast<const bf16x8 *>(
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
             ws + arow[t] * HS_K + 8 * ((kk * 4 + g) ^ hs_swz(arow[t])));
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8 *>(xp[j] + (long)kst(s) * HS_K + kk * 32);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < MT; ++j) acc[t][j] = Mma<bf16>::run(fa[t], fb[j], acc[t][j]);
+        acc[t] = Mma<bf16>::run(fa, xf[kk], acc[t]);
+      }
     }
-    if (s + 1 < nst) lstore(cur ^ 1);
+  };
+  bf16x8 xa[HS_K / 32], xb[HS_K / 32];
+  issue(0, 0);
+  xload(0, xa);
+  wait_vmcnt<0>();
+  __syncthreads();
+  // stage s is multiplied out of buffer s & 1 with register set (s & 1 ? xb
+  // : xa) while stage s + 1 is copied into the other buffer and set
+  for (int s = 0; s < nst; s += 2) {
+    if (s + 1 < nst) {
+      issue(s + 1, 1);
+      xload(s + 1, xb);
+    }
+    compute(0, xa);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (s + 1 >= nst) break;
+    if (s + 2 < nst) {
+      issue(s + 2, 0);
+      xload(s + 2, xa);
+    }
+    compute(1, xb);
+    wait_vmcnt<0>();
     __syncthreads();
   }
   // epilogue: per row, the wave's 32 ids, then the four waves in LDS
-  RowStat(*red)[MT * 16] = reinterpret_cast<RowStat(*)[MT * 16]>(&wsm[0][0]);
+  RowStat(*red)[16] = reinterpret_cast<RowStat(*)[16]>(&wsm[0][0]);
   const int vw = v0 + 32 * wave;
+  float zz[1][8];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float zz[1][8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zz[0][e] = acc[e >> 2][mt][e & 3];
-    RowStat st2 = lane_rowstat<1>(a, 16 * mt + r16, vw, g, zz);
-    if (g == 0) red[wave][16 * mt + r16] = st2;
-  }
+  for (int e = 0; e < 8; ++e) zz[0][e] = acc[e >> 2][e & 3];
+  RowStat st2 = lane_rowstat<1>(a, r16, vw, g, zz);
+  if (g == 0) red[wave][r16] = st2;
   __syncthreads();
-  for (int i = threadIdx.x; i < MT * 16; i += blockDim.x) {
-    if (i >= a.rows) continue;
-    RowStat st2 = red[0][i];
+  if (threadIdx.x < 16 && threadIdx.x < a.rows) {
+    const int i = threadIdx.x;
+    RowStat t = red[0][i];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) st2 = rowstat_merge(st2, red[w][i]);
-    a.part[(long)i * a.nvb + vb] = to_partial(st2);
+    for (int w = 1; w < 4; ++w) t = rowstat_merge(t, red[w][i]);
+    a.part[(long)i * a.nvb + vb] = to_partial(t);
   }
 }
 
@@ -450,21 +453,22 @@ static void launch_rows(const HeadArgs &a, hipStream_t st) {
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
-  // the LDS kernel addresses a block's hidden rows with 32-bit byte offsets
-  constexpr int BM = 32 * HEAD_MW;
+  // up to 16 rows stream the weight in 512-byte row slices; more rows go
+  // through the tile engine, with a row tile fitted to the row count (the
+  // LDS kernel addresses a block's hidden rows with 32-bit byte offsets)
+  const int mw = a.rows <= 32 ? 1 : a.rows <= 64 ? 2 : HEAD_MW;
+  const int BM = 32 * mw;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
-  if (a.dtype == 1 && a.rows > 64 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
+  if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
+    a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
+    hipLaunchKernelGGL(lm_head_stream_kernel, dim3(a.nvb), dim3(256), 0, st, a);
+  } else if (a.dtype == 1 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
     a.nvb = (a.vocab + HEAD_VB_LDS - 1) / HEAD_VB_LDS;
     const int nmb = (a.rows + BM - 1) / BM;
     const int nvb8 = (a.nvb + NXCD - 1) / NXCD * NXCD;
-    hipLaunchKernelGGL(lm_head_lds_kernel, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
-  } else if (a.dtype == 1 && a.d % HS_K == 0) {
-    a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
-    const dim3 grid(a.nvb);
-    if (a.rows <= 16) hipLaunchKernelGGL(lm_head_stream_kernel<1>, grid, dim3(256), 0, st, a);
-    else if (a.rows <= 32) hipLaunchKernelGGL(lm_head_stream_kernel<2>, grid, dim3(256), 0, st, a);
-    else if (a.rows <= 48) hipLaunchKernelGGL(lm_head_stream_kernel<3>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(lm_head_stream_kernel<4>, grid, dim3(256), 0, st, a);
+    if (mw == 1) hipLaunchKernelGGL(lm_head_lds_kernel<1>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
+    else if (mw == 2) hipLaunchKernelGGL(lm_head_lds_kernel<2>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
+    else hipLaunchKernelGGL(lm_head_lds_kernel<HEAD_MW>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;
     if (a.dtype == 1) launch_rows<bf16>(a, st);
