@@ -9,11 +9,13 @@ zsel, lse and stored logits must agree to the fp32 accumulation bound
 2.5e-4 * sum_k |h_k w_k| (recursive-summation bound for 4096 terms), which for
 these inputs is ~1e-4 absolute; the near-tie count is reported.
 
-Shapes: the tiny fp32 workload (V 1024, d 256, gamma 7 rows), a ragged bf16
-case (V 5003, d 512, rows in blocks of 15 with a stride of 16), and the full
-8B-shaped head (V 151936, d 4096) at the row counts of the greedy bs-1 (15
-rows, argmax), bs-32 rejection-sampling (480 rows, Gumbel, logits stored;
-sampled rows checked) and multi-copy (144 rows, shared Gumbel) workloads.
+Shapes: the tiny fp32 workload (V 1024, d 256, gamma 7 rows), ragged bf16
+cases (V 5003, d 512, rows in blocks of 15 with a stride of 16) at 11, 30,
+37 and 45 rows (one case per kernel row band: <= 16, <= 32, <= 64), and the
+full 8B-shaped head (V 151936, d 4096) at the row counts of the greedy bs-1
+(15 rows, argmax), bs-4 (60 rows), bs-32 rejection-sampling (480 rows,
+Gumbel, logits stored; sampled rows checked) and multi-copy (144 rows,
+shared Gumbel) workloads.
 """
 
 import numpy as np
@@ -114,6 +116,22 @@ def test_ragged_bf16_gumbel_strided_rows():
 
 def test_ragged_bf16_argmax():
     _run_case(5003, 512, "bf16", 45, 15, 16, bd.HEAD_ARGMAX)
+
+
+def test_ragged_bf16_gumbel_up_to_32_rows():
+    # 17..32 rows: the 32-row tile of the tile engine
+    _run_case(5003, 512, "bf16", 30, 15, 16, bd.HEAD_GUMBEL, keep_logits=True)
+
+
+def test_ragged_bf16_stream_up_to_16_rows():
+    # <= 16 rows: the weight-streaming kernel, with a partial last vocabulary block
+    _run_case(5003, 512, "bf16", 11, 11, 16, bd.HEAD_GUMBEL, T=1.3, keep_logits=True)
+
+
+def test_q8b_bs4_rows():
+    # 60 rows (4 sequences x 15 slots): the 64-row tile at full vocabulary
+    n, _, _ = _run_case(151936, 4096, "bf16", 60, 15, 16, bd.HEAD_ARGMAX, sample=12)
+    assert n <= 1
 
 
 def test_q8b_greedy_bs1_rows():
