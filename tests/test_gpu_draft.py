@@ -127,6 +127,20 @@ def test_small_bf16_ragged(ctx):
     assert flags.cpu().tolist() == [0, 0, 0]
 
 
+@pytest.mark.parametrize("hq,hkv,dh", [(8, 1, 128), (16, 1, 128), (8, 2, 64), (8, 1, 64)])
+def test_small_bf16_head_geometries(hq, hkv, dh):
+    # one case per attention kernel shape: two wave sets of 8 heads (1024
+    # threads), one wave set of 16 heads, head_dim 64 through the direct-copy
+    # ring (groups of 4) and through registers (groups of 8)
+    ctx = [37, 300, 1029]
+    cfg = configs.small_bf16(n_q_heads=hq, n_kv_heads=hkv, head_dim=dh, ctx=ctx)
+    dev, w, dr, kv = _setup(cfg, 1152)
+    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
+    want = _oracle(cfg, to_np(w), kv, tok, ctx)
+    _compare(cfg, to_np(w), out, want, f"heads {hq}/{hkv} dh {dh}")
+    assert flags.cpu().tolist() == [0, 0, 0]
+
+
 def test_small_bf16_multicopy():
     cfg = configs.small_bf16(ctx=[200, 513, 7], n_copies=3)
     dev, w, dr, kv = _setup(cfg, 640)
