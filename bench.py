@@ -219,18 +219,26 @@ def main():
     head_s = per_call["head"] * 1e-3
     head_bound = "mfma" if alg["head"]["flops"] / alg["head"]["bytes"] > \
         MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    # the LM-head kernel that runs at this row count (see launch_lm_head)
+    if cfg["dtype"] != "bf16":
+        head_kernel = "lm_head_kernel<float>"
+    else:
+        head_kernel = ("lm_head_stream_kernel" if cyc.rows <= 16 else
+                       "lm_head_lds_kernel<%d>" % (1 if cyc.rows <= 32 else 2 if cyc.rows <= 64 else 4))
+    head_kernel += " (+lm_combine_kernel)"
     traffic = None
     if args.workload == "q8b_bs32_rs":
         traffic = _profiled_traffic("lm_head_lds_kernel",
-                                    ["lm_head.hip", "mma_tile.hpp", "common.hpp", "kernels.hpp"])
+                                    ["lm_head.hip", "mma_tile.hpp", "dma.hpp", "common.hpp",
+                                     "kernels.hpp"])
     if head_bound == "mfma":
         ach = alg["head"]["flops"] / head_s / 1e12
-        roof = dict(kernel="lm_head_kernel (+lm_combine)", bound="mfma", achieved=round(ach, 2),
+        roof = dict(kernel=head_kernel, bound="mfma", achieved=round(ach, 2),
                     peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                     traffic=traffic, avg_us=round(per_call["head"] * 1e3, 2))
     else:
         ach = alg["head"]["bytes"] / head_s / 1e9
-        roof = dict(kernel="lm_head_kernel (+lm_combine)", bound="hbm", achieved=round(ach, 1),
+        roof = dict(kernel=head_kernel, bound="hbm", achieved=round(ach, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
                     traffic=traffic, avg_us=round(per_call["head"] * 1e3, 2))
 
