@@ -609,15 +609,38 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int S = a.eff_ctx[b];
   const int nvalid = max(1, (S + a.split - 1) / a.split);
   const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B + s;  // record of split sp: rec0 + sp*B
+  // splits in groups of 8 with predicated loads, so a group's loads are in
+  // flight together; the accumulation order is the split order
+  constexpr int G = 8;
   float M = -INFINITY;
-  for (int sp = 0; sp < nvalid; ++sp) M = fmaxf(M, a.mlpart[(rec0 + (long)sp * a.B) * 2]);
+  for (int sp0 = 0; sp0 < nvalid; sp0 += G) {
+    float mv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      mv[i] = sp0 + i < nvalid ? a.mlpart[(rec0 + (long)(sp0 + i) * a.B) * 2] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < G; ++i) M = fmaxf(M, mv[i]);
+  }
   float L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nvalid; ++sp) {
-    const long r = rec0 + (long)sp * a.B;
-    const float w = exp2f(a.mlpart[r * 2] - M);
-    L += w * a.mlpart[r * 2 + 1];
-    o += w * *reinterpret_cast<const f32x4 *>(a.opart + r * dh + d);
+  for (int sp0 = 0; sp0 < nvalid; sp0 += G) {
+    float mv[G], lv[G];
+    f32x4 ov[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const long r = rec0 + (long)(sp0 + i) * a.B;
+      const bool ok = sp0 + i < nvalid;
+      mv[i] = ok ? a.mlpart[r * 2] : -INFINITY;
+      lv[i] = ok ? a.mlpart[r * 2 + 1] : 0.f;
+      ov[i] = ok ? *reinterpret_cast<const f32x4 *>(a.opart + r * dh + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (sp0 + i >= nvalid) break;
+      const float w = exp2f(mv[i] - M);
+      L += w * lv[i];
+      o += w * ov[i];
+    }
   }
   const float inv = 1.0f / L;
   T *dst = (T *)a.out + ((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d;

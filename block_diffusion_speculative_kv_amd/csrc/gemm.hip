@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   constexpr int BN = 32 * NW, BM = 32 * MW;
   __shared__ LdsSmem sm;
   int nb, mb;
-  xcd_block(blockIdx.x, nmb, &nb, &mb);
+  xcd_block(blockIdx.x, nmb, (nnb + 7) >> 3, &nb, &mb);
   if (nb >= nnb) return;
   const int s0 = blockIdx.y * st_per_split;
   const int s1 = min(s0 + st_per_split, nst);

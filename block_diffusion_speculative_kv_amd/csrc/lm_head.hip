@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   constexpr int BN = 32 * NW, BM = 32 * MW;
   __shared__ TileSmem<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> sm;
   int vb, rb;
-  xcd_block(blockIdx.x, nmb, &vb, &rb);
+  xcd_block(blockIdx.x, nmb, (a.nvb + 7) >> 3, &vb, &rb);
   if (vb >= a.nvb) return;
   const int v0 = vb * BN, r0 = rb * BM;
   const int V = a.vocab, d = a.d;

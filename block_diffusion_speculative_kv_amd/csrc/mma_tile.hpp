@@ -175,13 +175,22 @@ __device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW, KT, NSW, NSX> &sm
   __syncthreads();  // every wave is done with the rings: the caller may reuse them
 }
 
-// XCD-aware placement: workgroup L runs on XCD L mod 8.  The m-blocks of one
-// n-block get consecutive slots on the same XCD, so they stream the same
-// weight tile through one L2 at about the same time.
-__device__ __forceinline__ void xcd_block(int L, int nmb, int *nb, int *mb) {
-  const int xcd = L & 7, slot = L >> 3;
-  *nb = (slot / nmb) * 8 + xcd;
-  *mb = slot % nmb;
+// XCD-aware placement: workgroup L runs on XCD L mod 8, which takes every
+// eighth n-block (nn of them).  Within an XCD, slots go in groups of up to
+// 8 m-blocks x all its n-blocks, m fastest: the workgroups that run together
+// on one XCD cover at most 8 m-blocks and a few n-blocks, so both the weight
+// tiles and the activation tiles they stream are shared through that XCD's
+// L2.  With up to 8 m-blocks (every draft shape and the LM head) this is
+// simply all m-blocks of one n-block in consecutive slots.
+__device__ __forceinline__ void xcd_block(int L, int nmb, int nn, int *nb, int *mb) {
+  constexpr int GM = 8;
+  const int xcd = L & 7, s = L >> 3;
+  const int per_group = GM * nn;
+  const int first = (s / per_group) * GM;
+  const int gsz = min(nmb - first, GM);
+  const int r = s % per_group;
+  *mb = first + r % gsz;
+  *nb = (r / gsz) * 8 + xcd;
 }
 
 }  // namespace dstill
