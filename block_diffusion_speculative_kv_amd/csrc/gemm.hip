@@ -8,11 +8,13 @@
 // summed in a fixed order by the consumer (the fused epilogue kernels), which
 // keeps results deterministic.
 //
-// Two kernels: with up to 64 rows the projection streams its weight once
-// (HBM-bound) and every MFMA operand fragment is loaded straight from global
-// memory into registers by the streaming loop of common.hpp (groups of
-// k-steps in flight); with more rows (bf16) the 128 x 128 LDS-tiled main loop
-// of mma_tile.hpp re-uses each staged weight tile across 128 rows.
+// Two kernels.  bf16 products whose depth is a multiple of 64 run on the
+// tile engine of mma_tile.hpp (gemm_lds_partial): 128 output features x 32,
+// 64 or 128 rows per workgroup, operands streamed HBM -> LDS by direct copies
+// (the weight three stages ahead), each staged weight tile re-used across the
+// workgroup's rows.  fp32 products and other depths load every MFMA operand
+// fragment straight from global memory into registers by the streaming loop
+// of common.hpp (gemm_nt_partial).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mma_tile.hpp"
@@ -63,21 +65,27 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
   }
 }
 
-// LDS-tiled path: 128 x 128 blocks, k-split over stages of 64.
-constexpr int LDS_NW = 4, LDS_MW = 4;
-// k per stage; W and X ring depths (80 KB: two workgroups per CU)
+// LDS-tiled path: 128 x 32 MW blocks (MW = 4 from 65 rows, else 1 or 2), k-split
+// over stages of 64.
+constexpr int LDS_NW = 4;
+// k per stage; W and X ring depths (56-80 KB: two workgroups per CU)
 constexpr int LDS_KT = 64, LDS_NSW = 3, LDS_NSX = 2;
-using LdsSmem = TileSmem<LDS_NW, LDS_MW, LDS_KT, LDS_NSW, LDS_NSX>;
-constexpr int LDS_PER_CU = 160 * 1024 / (int)sizeof(LdsSmem);  // workgroups per compute unit
+template <int MW>
+using LdsSmem = TileSmem<LDS_NW, MW, LDS_KT, LDS_NSW, LDS_NSX>;
+constexpr int LDS_PER_CU = 2;  // workgroups per compute unit (LDS and registers)
+static_assert(2 * sizeof(LdsSmem<4>) <= 160 * 1024, "two workgroups per CU");
 
+static int lds_mw(int M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
+
+template <int MW>
 __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
                                                         const bf16 *__restrict__ W, long ldw,
                                                         float *__restrict__ out, int M, int N,
                                                         int nst, int st_per_split, int nnb,
                                                         int nmb) {
-  constexpr int NW = LDS_NW, MW = LDS_MW;
+  constexpr int NW = LDS_NW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
-  __shared__ LdsSmem sm;
+  __shared__ LdsSmem<MW> sm;
   int nb, mb;
   xcd_block(blockIdx.x, nmb, (nnb + 7) >> 3, &nb, &mb);
   if (nb >= nnb) return;
@@ -106,11 +114,14 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   }
 }
 
-static bool use_lds(int M, int K, int dtype) { return dtype == 1 && M > 64 && K % LDS_KT == 0; }
+// every bf16 product whose depth is a whole number of stages takes the LDS
+// path (its direct-copy rings stream the weight faster than register loads
+// at any row count); fp32 and other depths take gemm_nt_partial
+static bool use_lds(int K, int dtype) { return dtype == 1 && K % LDS_KT == 0; }
 
 static void lds_geometry(int M, int N, int K, int ncu, int *nnb, int *nmb, int *nst,
                          int *splits, int *per) {
-  constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
+  const int BN = 32 * LDS_NW, BM = 32 * lds_mw(M);
   *nnb = (N + BN - 1) / BN;
   *nmb = (M + BM - 1) / BM;
   *nst = K / LDS_KT;
@@ -154,7 +165,7 @@ static void launch_tile(const GemmArgs &a, hipStream_t st) {
 // Chooses the wave tile from M and the number of k-splits; returns the split
 // count the output buffer must hold.
 int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
-  if (use_lds(M, K, dtype)) {
+  if (use_lds(K, dtype)) {
     int nnb, nmb, nst, splits, per;
     lds_geometry(M, N, K, num_cu, &nnb, &nmb, &nst, &splits, &per);
     return splits;
@@ -195,14 +206,22 @@ static void launch_typed(const GemmArgs &a, hipStream_t st) {
 }
 
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
-  if (use_lds(a.M, a.K, a.dtype)) {
-    constexpr int BN = 32 * LDS_NW, BM = 32 * LDS_MW;
+  if (use_lds(a.K, a.dtype)) {
+    const int mw = lds_mw(a.M);
+    const int BN = 32 * LDS_NW, BM = 32 * mw;
     const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
     const int per = (nst + a.splits - 1) / a.splits;
     const int nnb8 = (nnb + 7) / 8 * 8;
-    hipLaunchKernelGGL(gemm_lds_partial, dim3(nnb8 * nmb, a.splits), dim3(256), 0, st,
-                       (const bf16 *)a.X, a.ldx, (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst,
-                       per, nnb, nmb);
+    const dim3 grid(nnb8 * nmb, a.splits);
+    if (mw == 1)
+      hipLaunchKernelGGL(gemm_lds_partial<1>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
+    else if (mw == 2)
+      hipLaunchKernelGGL(gemm_lds_partial<2>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
+    else
+      hipLaunchKernelGGL(gemm_lds_partial<4>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
     return;
   }
   if (a.dtype == 1) launch_typed<bf16>(a, st);
