@@ -185,14 +185,26 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 // ---------------------------------------------------------------------------
 struct u64x4 { uint64_t w[4]; };
 
+// Full 64 x 64 -> 128-bit product of a constant and x, from four 32 x 32 ->
+// 64-bit partial products (each one v_mad_u64_u32): both halves at once.
+__device__ __forceinline__ void mulhilo64(uint64_t m, uint64_t x, uint64_t &lo, uint64_t &hi) {
+  const uint64_t ml = (uint32_t)m, mh = m >> 32, xl = (uint32_t)x, xh = x >> 32;
+  const uint64_t p0 = ml * xl;                    // bits 0..63
+  const uint64_t p1 = ml * xh + (p0 >> 32);       // bits 32..95, cannot overflow
+  const uint64_t p2 = mh * xl + (uint32_t)p1;     // bits 32..95, cannot overflow
+  lo = (p2 << 32) | (uint32_t)p0;
+  hi = mh * xh + (p1 >> 32) + (p2 >> 32);
+}
+
 __device__ __forceinline__ u64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
                                                uint64_t c3, uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
-    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    uint64_t lo0, hi0, lo1, hi1;
+    mulhilo64(M0, c0, lo0, hi0);
+    mulhilo64(M1, c2, lo1, hi1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += W0; k1 += W1;

@@ -38,7 +38,7 @@ namespace dstill {
 template <int NW, int MW, int KT, int NSW, int NSX>
 struct TileSmem {
   static_assert(KT == 64 || KT == 32, "stage depth");
-  static_assert(NSX == 2 && (NSW == 2 || NSW == 3), "ring depths");
+  static_assert(NSX == 2 && NSW >= 2 && NSW <= 6, "ring depths");
   static constexpr int BN = 32 * NW, BM = 32 * MW;
   bf16 w[NSW][BN * KT];
   bf16 x[NSX][BM * KT];
@@ -155,15 +155,23 @@ __device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW, KT, NSW, NSX> &sm
         for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
     }
   };
-  // Issue order: W0, X0, (W1 if NSW = 3); then per stage s, after its wait:
-  // X(s + 1), W(s + NSW - 1).  So when stage s is waited for, the only copies
-  // issued after X(s) are W(s + 1) (NSW = 3, if it exists), and W(s) was
-  // issued before X(s) (NSW = 3) or right after it (NSW = 2).
+  // Issue order: W0, X0, W1 .. W(NSW - 2); then per stage s, after its wait:
+  // X(s + 1), W(s + NSW - 1).  When stage s is waited for, the copies issued
+  // after X(s) are W(1 .. NSW - 2) at s = 0, and W(s + NSW - 2) later (those
+  // that exist); W(s) itself was issued before X(s), except with NSW = 2,
+  // where it follows X(s) and nothing may stay outstanding.
   ld.issue_w(sm, 0);
   ld.issue_x(sm, 0);
-  if (NSW == 3 && nst > 1) ld.issue_w(sm, 1);
+#pragma unroll
+  for (int p = 1; p <= NSW - 2; ++p)
+    if (p < nst) ld.issue_w(sm, p);
   for (int s = 0; s < nst; ++s) {
-    if (NSW == 3 && s + 1 < nst) wait_vmcnt<NCW>();
+    int later = 0;  // W stages allowed to stay in flight
+    if (NSW > 2) later = s == 0 ? min(NSW - 2, nst - 1) : (s + NSW - 2 < nst ? 1 : 0);
+    if (NSW >= 6 && later >= 4) wait_vmcnt<4 * NCW>();
+    else if (NSW >= 5 && later >= 3) wait_vmcnt<3 * NCW>();
+    else if (NSW >= 4 && later >= 2) wait_vmcnt<2 * NCW>();
+    else if (NSW >= 3 && later >= 1) wait_vmcnt<NCW>();
     else wait_vmcnt<0>();
     // every wave's copies of stage s are visible after the barrier, and the
     // buffers refilled next (last read at stage s - 1) are free
