@@ -375,8 +375,15 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     // gate|up, SwiGLU, down
     g.X = w.u; g.ldx = d; g.W = L.w_gate_up; g.ldw = d; g.N = 2 * c.mlp; g.K = d;
     g.splits = gemm_plan_splits(R, 2 * c.mlp, d, c.dtype, ncu);
-    launch_gemm(g, st);
-    launch_swiglu(c.dtype, w.parts, g.splits, R, c.mlp, w.act, st);
+    if (gemm_can_fuse_swiglu(R, c.mlp, d, c.dtype, ncu)) {
+      g.splits = 1;
+      g.swiglu_act = w.act; g.mlp = c.mlp;  // SwiGLU in the product's epilogue
+      launch_gemm(g, st);
+      g.swiglu_act = nullptr; g.mlp = 0;
+    } else {
+      launch_gemm(g, st);
+      launch_swiglu(c.dtype, w.parts, g.splits, R, c.mlp, w.act, st);
+    }
     g.X = w.act; g.ldx = c.mlp; g.W = L.w_down; g.ldw = c.mlp; g.N = d; g.K = c.mlp;
     g.splits = gemm_plan_splits(R, d, c.mlp, c.dtype, ncu);
     launch_gemm(g, st);

@@ -77,12 +77,18 @@ static_assert(2 * sizeof(LdsSmem<4>) <= 160 * 1024, "two workgroups per CU");
 
 static int lds_mw(int M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
 
+// act != nullptr selects the fused SwiGLU epilogue (one split): n-block nb
+// covers features f0 = 64 nb .. f0 + 63, and tile row r (wave r / 64, in-wave
+// row r % 64) is gate row f0 + 32 (r / 64) + r % 32 for r % 64 < 32, else the
+// matching up row mlp + f0 + 32 (r / 64) + r % 32; so a lane's tiles i and
+// i + 2 hold the gate and up sums of the same 4 features of the same row.
 template <int MW>
 __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
                                                         const bf16 *__restrict__ W, long ldw,
                                                         float *__restrict__ out, int M, int N,
                                                         int nst, int st_per_split, int nnb,
-                                                        int nmb) {
+                                                        int nmb, bf16 *__restrict__ act,
+                                                        int mlp) {
   constexpr int NW = LDS_NW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
   __shared__ LdsSmem<MW> sm;
@@ -91,16 +97,42 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   if (nb >= nnb) return;
   const int s0 = blockIdx.y * st_per_split;
   const int s1 = min(s0 + st_per_split, nst);
-  const int n0 = nb * BN, m0 = mb * BM;
+  const int m0 = mb * BM;
+  const bool fused = act != nullptr;
+  const int n0 = fused ? nb * (BN / 2) : nb * BN;
   TileLoader<NW, MW, LDS_KT, LDS_NSW, LDS_NSX> ld;
-  ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
-          X + (long)m0 * ldx, [&](int r) { return (min(m0 + r, M - 1) - m0) * (int)ldx; },
-          (long)s0 * LDS_KT);
+  auto xrow = [&](int r) { return (min(m0 + r, M - 1) - m0) * (int)ldx; };
+  if (fused)
+    ld.init(W + (long)n0 * ldw,
+            [&](int r) { return (((r & 32) ? mlp : 0) + 32 * (r >> 6) + (r & 31)) * (int)ldw; },
+            X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
+  else
+    ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
+            X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
   f32x4 acc[NW][MW];
   tile_mainloop<NW, MW, LDS_KT, LDS_NSW, LDS_NSX, false>(sm, ld, s1 - s0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int wn = wave & 1, wm = wave >> 1;
+  if (fused) {
+#pragma unroll
+    for (int i = 0; i < NW / 2; ++i) {
+      const int f = n0 + 32 * wn + 16 * i + 4 * g;
+#pragma unroll
+      for (int j = 0; j < MW; ++j) {
+        const int m = m0 + wm * 16 * MW + 16 * j + r16;
+        if (m >= M) continue;
+        bf16 v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gt = acc[i][j][e], up = acc[i + 2][j][e];
+          v[e] = from_f32<bf16>(gt / (1.0f + expf(-gt)) * up);
+        }
+        *reinterpret_cast<uint2 *>(act + (long)m * mlp + f) = *reinterpret_cast<const uint2 *>(v);
+      }
+    }
+    return;
+  }
   float *o = out + (long)blockIdx.y * M * N;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -162,6 +194,12 @@ static void launch_tile(const GemmArgs &a, hipStream_t st) {
                      (const T *)a.X, a.ldx, (const T *)a.W, a.ldw, a.out, a.M, a.N, nks, per);
 }
 
+bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu) {
+  if (!use_lds(K, dtype) || mlp % 64 != 0 || M <= 0) return false;
+  const long tiles = (long)(mlp / 64) * ((M + 32 * lds_mw(M) - 1) / (32 * lds_mw(M)));
+  return tiles >= num_cu;
+}
+
 // Chooses the wave tile from M and the number of k-splits; returns the split
 // count the output buffer must hold.
 int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
@@ -206,6 +244,23 @@ static void launch_typed(const GemmArgs &a, hipStream_t st) {
 }
 
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
+  if (a.swiglu_act) {
+    // fused gate|up + SwiGLU: 64 features (128 weight rows) per n-block
+    const int mw = lds_mw(a.M), BM = 32 * mw;
+    const int nnb = a.mlp / 64, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
+    const dim3 grid((nnb + 7) / 8 * 8 * nmb, 1);
+    bf16 *act = (bf16 *)a.swiglu_act;
+    if (mw == 1)
+      hipLaunchKernelGGL(gemm_lds_partial<1>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
+    else if (mw == 2)
+      hipLaunchKernelGGL(gemm_lds_partial<2>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
+    else
+      hipLaunchKernelGGL(gemm_lds_partial<4>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
+    return;
+  }
   if (use_lds(a.K, a.dtype)) {
     const int mw = lds_mw(a.M);
     const int BN = 32 * LDS_NW, BM = 32 * mw;
@@ -215,13 +270,16 @@ void launch_gemm(const GemmArgs &a, hipStream_t st) {
     const dim3 grid(nnb8 * nmb, a.splits);
     if (mw == 1)
       hipLaunchKernelGGL(gemm_lds_partial<1>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
+                         0);
     else if (mw == 2)
       hipLaunchKernelGGL(gemm_lds_partial<2>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
+                         0);
     else
       hipLaunchKernelGGL(gemm_lds_partial<4>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb);
+                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
+                         0);
     return;
   }
   if (a.dtype == 1) launch_typed<bf16>(a, st);

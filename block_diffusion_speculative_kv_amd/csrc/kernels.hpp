@@ -16,7 +16,16 @@ struct GemmArgs {
   long ldw;
   float *out;     // [splits][M][N] fp32 partial sums
   int M, N, K, splits, dtype;
+  // Fused SwiGLU (bf16, one split, mlp a multiple of 64): W is gate rows
+  // [0, mlp) then up rows [mlp, 2 mlp) (N = 2 mlp) and the product is written
+  // as act[M][mlp] = bf16(silu(gate) * up) instead of partial sums.
+  void *swiglu_act = nullptr;
+  int mlp = 0;
 };
+// Whether a gate|up product of these sizes takes the fused SwiGLU epilogue:
+// bf16, mlp a multiple of 64, and one split already gives every compute unit
+// a workgroup (the fusion saves the partial plane and the separate pass).
+bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu);
 void gemm_pick_tile(int M, int *ntw, int *mtw);
 int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu);
 void launch_gemm(const GemmArgs &a, hipStream_t st);

@@ -141,6 +141,18 @@ def test_small_bf16_head_geometries(hq, hkv, dh):
     assert flags.cpu().tolist() == [0, 0, 0]
 
 
+def test_small_bf16_batch32_fused_swiglu():
+    # 512 rows and mlp 5632 (352 tiles): the gate|up product runs unsplit,
+    # with SwiGLU in its epilogue
+    ctx = [int(x) for x in np.random.default_rng(5).integers(0, 160, 32)]
+    cfg = configs.small_bf16(bs=32, ctx=ctx, mlp=5632)
+    dev, w, dr, kv = _setup(cfg, 192)
+    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
+    want = _oracle(cfg, to_np(w), kv, tok, ctx)
+    _compare(cfg, to_np(w), out, want, "batch 32")
+    assert flags.cpu().tolist() == [0] * 32
+
+
 def test_small_bf16_multicopy():
     cfg = configs.small_bf16(ctx=[200, 513, 7], n_copies=3)
     dev, w, dr, kv = _setup(cfg, 640)
