@@ -84,7 +84,7 @@ __device__ __forceinline__ RowStat rowstat_shfl_xor(const RowStat &a, int o) {
 // starting at vw + 32p + 8g.  Writes the logits if asked, draws the Gumbel
 // noise (one Philox block per 8 ids), and returns the lane's statistics
 // merged over the wave's four lane groups.
-template <int NP>
+template <int NP, bool STORE = true>
 __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw, int g,
                                                 float (&zz)[NP][8]) {
   const int V = a.vocab;
@@ -129,7 +129,7 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
         st.m = fmaxf(st.m, z * invT);
       }
     }
-    if (a.logits && rvalid) {
+    if (STORE && a.logits && rvalid) {
       float *lp = a.logits + (long)r * V + v0;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -243,8 +243,16 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   f32x4 acc[NW][MW];
   tile_mainloop<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX, true>(sm, ld, d / HEAD_KT, acc);
 
-  // the main loop ended with a barrier: its LDS is free for the row records
-  RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm.w[0][0]);
+  // The main loop ended with a barrier: its LDS is free.  The first 8 KB take
+  // the per-wave row records; stored logits are staged behind them as a
+  // [BM][BN + 4] fp32 tile and written back as whole 512-byte row runs (a
+  // lane's own values are 8 ids of one row, 16 rows per instruction).
+  constexpr int LGS = BN + 4;  // staged row stride (floats): 16-row writes hit distinct banks
+  static_assert(2 * BM * (int)sizeof(RowStat) <= 8192, "row records");
+  static_assert(8192 + BM * LGS * 4 <= (int)sizeof(sm), "logits staging");
+  RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm);
+  float *lg = reinterpret_cast<float *>(reinterpret_cast<char *>(&sm) + 8192);
+  const bool stage = a.logits != nullptr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int wn = wave & 1, wm = wave >> 1;
@@ -257,10 +265,33 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
     for (int p = 0; p < NW / 2; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][mt][e & 3];
-    RowStat st = lane_rowstat<NW / 2>(a, r0 + rl, vw, g, zz);
+    if (stage) {
+#pragma unroll
+      for (int p = 0; p < NW / 2; ++p) {
+        float *dst = lg + rl * LGS + wn * 16 * NW + 32 * p + 8 * g;
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{zz[p][0], zz[p][1], zz[p][2], zz[p][3]};
+        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{zz[p][4], zz[p][5], zz[p][6], zz[p][7]};
+      }
+    }
+    RowStat st = lane_rowstat<NW / 2, false>(a, r0 + rl, vw, g, zz);
     if (g == 0) red[wn][rl] = st;
   }
   __syncthreads();
+  if (stage) {
+    for (int i = threadIdx.x; i < BM * (BN / 4); i += blockDim.x) {
+      const int rl = i / (BN / 4), v = v0 + 4 * (i % (BN / 4)), r = r0 + rl;
+      if (r >= a.rows || v >= V) continue;
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(lg + rl * LGS + (v - v0));
+      float *dst = a.logits + (long)r * V + v;
+      if (v + 4 <= V && (V & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(dst) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v + e < V) dst[e] = x[e];
+      }
+    }
+  }
   for (int i = threadIdx.x; i < BM; i += blockDim.x) {
     const int r = r0 + i;
     if (r >= a.rows) continue;
