@@ -133,15 +133,32 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
     }
     return;
   }
+  // A lane holds 4 consecutive features of one row, so direct stores would
+  // touch 16 rows x 64 bytes per instruction: the tile goes through the idle
+  // ring as [BM][BN + 4] fp32 and leaves as whole 512-byte row runs.
+  constexpr int OS = BN + 4;  // staged row stride (floats)
+  static_assert(BM * OS * 4 <= (int)sizeof(LdsSmem<MW>), "partial staging");
+  float *ot = reinterpret_cast<float *>(&sm);
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int j = 0; j < MW; ++j)
+      *reinterpret_cast<f32x4 *>(ot + (wm * 16 * MW + 16 * j + r16) * OS + wn * 16 * NW + 16 * i +
+                                 4 * g) = acc[i][j];
+  __syncthreads();
   float *o = out + (long)blockIdx.y * M * N;
+  for (int idx = threadIdx.x; idx < BM * (BN / 4); idx += blockDim.x) {
+    const int rl = idx / (BN / 4), nl = 4 * (idx % (BN / 4));
+    const int m = m0 + rl, n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(ot + rl * OS + nl);
+    float *dst = o + (long)m * N + n;
+    if ((N & 3) == 0) {
+      *reinterpret_cast<f32x4 *>(dst) = x;
+    } else {
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int n = n0 + wn * 16 * NW + 16 * i + 4 * g;
-    if (n >= N) continue;
-#pragma unroll
-    for (int j = 0; j < MW; ++j) {
-      const int m = m0 + wm * 16 * MW + 16 * j + r16;
-      if (m < M) *reinterpret_cast<f32x4 *>(o + (long)m * N + n) = acc[i][j];
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) dst[e] = x[e];
     }
   }
 }
