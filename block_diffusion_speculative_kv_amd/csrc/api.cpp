@@ -107,7 +107,7 @@ AttnPlan attn_plan(int max_ctx, int pairs) {
 // Workspace of one block_draft call.
 struct DraftWs {
   int32_t *eff_ctx, *tok;
-  float *h, *parts, *opart, *mlpart, *ssp;
+  float *h, *parts, *opart, *mlpart, *ssp, *rope;
   void *u, *q, *kb, *vb, *attn, *act;
 };
 size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int ncu, void *ws,
@@ -120,6 +120,7 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
   w.tok = cv.take<int32_t>(R);
   w.h = cv.take<float>((size_t)R * d);
   w.ssp = cv.take<float>((size_t)R * ((d + 1023) / 1024));
+  w.rope = cv.take<float>((size_t)R * c.head_dim);  // [R][dh/2] (cos, sin)
   w.u = cv.take<char>((size_t)R * d * eb);
   w.q = cv.take<char>((size_t)R * qd * eb);
   w.kb = cv.take<char>((size_t)R * kvd * eb);
@@ -136,7 +137,7 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
 
 struct InjectWs {
   void *ht;
-  float *parts, *xtmp, *ssp;
+  float *parts, *xtmp, *ssp, *rope;
 };
 size_t inject_ws(const dstill_config &c, int n, int ncu, void *ws, InjectWs *out) {
   Carver cv(ws);
@@ -144,6 +145,7 @@ size_t inject_ws(const dstill_config &c, int n, int ncu, void *ws, InjectWs *out
   w.ht = cv.take<char>((size_t)n * c.hidden * elem_bytes(c.dtype));
   w.xtmp = cv.take<float>((size_t)n * c.hidden);
   w.ssp = cv.take<float>((size_t)n * ((c.hidden + 1023) / 1024));
+  w.rope = cv.take<float>((size_t)n * c.head_dim);  // [n][dh/2] (cos, sin)
   w.parts = cv.take<float>(gemm_parts_floats(c, n, ncu));
   if (out) *out = w;
   return cv.off;
@@ -289,6 +291,7 @@ int dstill_inject_kv(const dstill_handle *h, const void *feats, const int32_t *s
   const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   const int eb = elem_bytes(c.dtype);
 
+  launch_rope_table(nullptr, 1, 1, pos, n, c.head_dim, c.rope_theta, w.rope, st);
   GemmArgs g;
   g.dtype = c.dtype;
   g.X = feats; g.ldx = F; g.W = h->w.w_fuse; g.ldw = F; g.out = w.parts;
@@ -307,7 +310,7 @@ int dstill_inject_kv(const dstill_handle *h, const void *feats, const int32_t *s
     k.splits = gemm_plan_splits(n, 2 * kvd, d, c.dtype, ncu);
     launch_gemm(k, st);
     launch_inject_post(c.dtype, w.parts, k.splits, n, c.n_kv_heads, c.head_dim, seq_id, pos,
-                       L.k_norm, c.qk_norm, c.rms_eps, c.rope_theta, kv->k[l], kv->v[l],
+                       L.k_norm, c.qk_norm, c.rms_eps, w.rope, kv->k[l], kv->v[l],
                        kv->max_batch, kv->cap, st);
   }
   return hip_check("inject_kv launch");
@@ -342,6 +345,8 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
   launch_draft_prep(block_tokens, ctx_len, bs, n_copies * block, c.vocab, ctx_limit, w.eff_ctx,
                     w.tok, flags, st);
   launch_embed(c.dtype, h->w.embed, w.tok, R, d, w.h, st);
+  launch_rope_table(w.eff_ctx, n_copies * block, block, nullptr, R, c.head_dim, c.rope_theta,
+                    w.rope, st);
   // pre-attention norm of layer 0; later layers get it fused after the MLP
   launch_norm_rows(c.dtype, nullptr, 0, R, d, w.h, 0, h->layers[0].attn_norm, c.rms_eps, w.u, d,
                    nullptr, w.ssp, st);
@@ -355,7 +360,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     launch_gemm(g, st);
     launch_qkv_post(c.dtype, w.parts, g.splits, R, c.n_q_heads, c.n_kv_heads, c.head_dim,
                     w.eff_ctx, n_copies * block, block, L.q_norm, L.k_norm, c.qk_norm, c.rms_eps,
-                    c.rope_theta, w.q, w.kb, w.vb, st);
+                    w.rope, w.q, w.kb, w.vb, st);
     AttnArgs a;
     a.dtype = c.dtype;
     a.q = w.q; a.kb = w.kb; a.vb = w.vb; a.kc = kv->k[l]; a.vc = kv->v[l];

@@ -42,15 +42,19 @@ void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d
 void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
                       int write_resid, const void *gain, float eps, void *out, long out_stride,
                       float *xtmp, float *ssp, hipStream_t st);
+// (cos, sin) of the rotary pairs of n rows, [n][dh/2] float2: row r sits at
+// pos[r] (injection) or, with pos null, at eff_ctx[r / rows_per_seq] + r % block.
+void launch_rope_table(const int32_t *eff_ctx, int rows_per_seq, int block, const int32_t *pos,
+                       int n, int dh, float theta, float *tab, hipStream_t st);
 void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, int hkv, int dh,
                      const int32_t *eff_ctx, int rows_per_seq, int block, const void *q_norm,
-                     const void *k_norm, int qk_norm, float eps, float theta, void *q, void *kb,
-                     void *vb, hipStream_t st);
+                     const void *k_norm, int qk_norm, float eps, const float *rope, void *q,
+                     void *kb, void *vb, hipStream_t st);
 void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, void *act,
                    hipStream_t st);
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
                         const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
-                        float eps, float theta, void *kc, void *vc, int max_batch, int cap,
+                        float eps, const float *rope, void *kc, void *vc, int max_batch, int cap,
                         hipStream_t st);
 
 // ---- block attention over injected context (attn.hip) --------------------

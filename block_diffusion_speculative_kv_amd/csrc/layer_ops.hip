@@ -142,25 +142,45 @@ void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, f
                        (const float *)gain, eps, (float *)out, out_stride);
 }
 
-// ---- per-head RMSNorm + rotary embedding -------------------------------------
-// One wave handles one (row, head); lane p owns the rotary pairs
-// (p, p + dh/2) and (p + 64, p + 64 + dh/2) (dh <= 256).
-__device__ __forceinline__ void rope_pair(float &x1, float &x2, int p, int dh, int pos,
-                                          float theta) {
+// ---- rotary table: (cos, sin) of every rotary pair of every row ------------
+// angle = pos * theta^(-2p/dh), in fp64, rounded to fp32 once; every head of
+// a row reads the same row of the table.
+__global__ __launch_bounds__(64) void rope_table_kernel(const int32_t *__restrict__ eff_ctx,
+                                                        int rows_per_seq, int block,
+                                                        const int32_t *__restrict__ pos, int dh,
+                                                        float theta, float2 *__restrict__ tab) {
+  const int r = blockIdx.x, half = dh / 2;
+  const int p = blockIdx.y * 64 + threadIdx.x;
+  if (p >= half) return;
+  const int ps = pos ? max(pos[r], 0) : eff_ctx[r / rows_per_seq] + r % block;
   const double inv = exp(-2.0 * (double)p / (double)dh * log((double)theta));
   double sn, cs;
-  sincos((double)pos * inv, &sn, &cs);
-  const float c = (float)cs, s = (float)sn;
-  const float y1 = x1 * c - x2 * s;
-  const float y2 = x2 * c + x1 * s;
+  sincos((double)ps * inv, &sn, &cs);
+  tab[(long)r * half + p] = make_float2((float)cs, (float)sn);
+}
+
+void launch_rope_table(const int32_t *eff_ctx, int rows_per_seq, int block, const int32_t *pos,
+                       int n, int dh, float theta, float *tab, hipStream_t st) {
+  if (n == 0) return;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(n, (dh / 2 + 63) / 64), dim3(64), 0, st, eff_ctx,
+                     rows_per_seq, block, pos, dh, theta, (float2 *)tab);
+}
+
+// ---- per-head RMSNorm + rotary embedding -------------------------------------
+// One wave handles one (row, head); lane p owns the rotary pairs
+// (p, p + dh/2) and (p + 64, p + 64 + dh/2) (dh <= 256); cs is the row's
+// rotary table.
+__device__ __forceinline__ void rope_pair(float &x1, float &x2, float2 cs) {
+  const float y1 = x1 * cs.x - x2 * cs.y;
+  const float y2 = x2 * cs.x + x1 * cs.y;
   x1 = y1;
   x2 = y2;
 }
 
 template <typename T>
 __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh, bool norm,
-                                               const T *g, float eps, bool rope, int pos,
-                                               float theta) {
+                                               const T *g, float eps,
+                                               const float2 *__restrict__ cs) {
   const int lane = threadIdx.x & 63, half = dh / 2;
   if (norm) {
     float ss = 0.f;
@@ -177,12 +197,10 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
       }
     }
   }
-  if (rope) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = lane + 64 * i;
-      if (p < half) rope_pair(x1[i], x2[i], p, dh, pos, theta);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) rope_pair(x1[i], x2[i], cs[p]);
   }
 }
 
@@ -191,10 +209,9 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(
     const float *__restrict__ parts, int nsplit, int R, int hq, int hkv, int dh,
     const int32_t *__restrict__ eff_ctx, int rows_per_seq, int block,
     const T *__restrict__ q_norm, const T *__restrict__ k_norm, int qk_norm, float eps,
-    float theta, T *__restrict__ q, T *__restrict__ kb, T *__restrict__ vb) {
+    const float2 *__restrict__ rope, T *__restrict__ q, T *__restrict__ kb, T *__restrict__ vb) {
   const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
   const int half = dh / 2, ncol = (hq + 2 * hkv) * dh;
-  const int pos = eff_ctx[r / rows_per_seq] + r % block;
   const bool is_q = head < hq, is_k = !is_q && head < hq + hkv;
   float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
 #pragma unroll
@@ -222,7 +239,7 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(
     return;
   }
   T *dst = is_q ? q + (long)r * hq * dh + head * dh : kb + (long)r * hkv * dh + (head - hq) * dh;
-  head_norm_rope<T>(x1, x2, dh, qk_norm != 0, is_q ? q_norm : k_norm, eps, true, pos, theta);
+  head_norm_rope<T>(x1, x2, dh, qk_norm != 0, is_q ? q_norm : k_norm, eps, rope + (long)r * half);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
@@ -235,18 +252,18 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(
 
 void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, int hkv, int dh,
                      const int32_t *eff_ctx, int rows_per_seq, int block, const void *q_norm,
-                     const void *k_norm, int qk_norm, float eps, float theta, void *q, void *kb,
-                     void *vb, hipStream_t st) {
+                     const void *k_norm, int qk_norm, float eps, const float *rope, void *q,
+                     void *kb, void *vb, hipStream_t st) {
   if (R == 0) return;
   dim3 grid(R, hq + 2 * hkv);
   if (dtype == 1)
     hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
                        eff_ctx, rows_per_seq, block, (const bf16 *)q_norm, (const bf16 *)k_norm,
-                       qk_norm, eps, theta, (bf16 *)q, (bf16 *)kb, (bf16 *)vb);
+                       qk_norm, eps, (const float2 *)rope, (bf16 *)q, (bf16 *)kb, (bf16 *)vb);
   else
     hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
                        eff_ctx, rows_per_seq, block, (const float *)q_norm, (const float *)k_norm,
-                       qk_norm, eps, theta, (float *)q, (float *)kb, (float *)vb);
+                       qk_norm, eps, (const float2 *)rope, (float *)q, (float *)kb, (float *)vb);
 }
 
 // ---- SwiGLU gate ------------------------------------------------------------
@@ -284,8 +301,8 @@ template <typename T>
 __global__ __launch_bounds__(64) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos,
-    const T *__restrict__ k_norm, int qk_norm, float eps, float theta, T *__restrict__ kc,
-    T *__restrict__ vc, int max_batch, int cap) {
+    const T *__restrict__ k_norm, int qk_norm, float eps, const float2 *__restrict__ rope,
+    T *__restrict__ kc, T *__restrict__ vc, int max_batch, int cap) {
   const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
   const int sq = seq[r], ps = pos[r];
   if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(64) void inject_post_kernel(
   const long stride = is_k ? 1 : 64;
   T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
                 : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
-  if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, true, ps, theta);
+  if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, rope + (long)r * half);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
@@ -322,18 +339,18 @@ __global__ __launch_bounds__(64) void inject_post_kernel(
 
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
                         const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
-                        float eps, float theta, void *kc, void *vc, int max_batch, int cap,
+                        float eps, const float *rope, void *kc, void *vc, int max_batch, int cap,
                         hipStream_t st) {
   if (n == 0) return;
   dim3 grid(n, 2 * hkv);
   if (dtype == 1)
     hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, (const bf16 *)k_norm, qk_norm, eps, theta, (bf16 *)kc,
-                       (bf16 *)vc, max_batch, cap);
+                       seq, pos, (const bf16 *)k_norm, qk_norm, eps, (const float2 *)rope,
+                       (bf16 *)kc, (bf16 *)vc, max_batch, cap);
   else
     hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, (const float *)k_norm, qk_norm, eps, theta, (float *)kc,
-                       (float *)vc, max_batch, cap);
+                       seq, pos, (const float *)k_norm, qk_norm, eps, (const float2 *)rope,
+                       (float *)kc, (float *)vc, max_batch, cap);
 }
 
 }  // namespace dstill
