@@ -106,7 +106,7 @@ AttnPlan attn_plan(int max_ctx, int pairs) {
 
 // Workspace of one block_draft call.
 struct DraftWs {
-  int32_t *eff_ctx, *tok;
+  int32_t *eff_ctx, *tok, *wlist;
   float *h, *parts, *opart, *mlpart, *ssp, *rope;
   void *u, *q, *kb, *vb, *attn, *act;
 };
@@ -118,6 +118,7 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
   DraftWs w;
   w.eff_ctx = cv.take<int32_t>(bs);
   w.tok = cv.take<int32_t>(R);
+  w.wlist = cv.take<int32_t>((size_t)ap.nsplit * bs * C * c.n_kv_heads);
   w.h = cv.take<float>((size_t)R * d);
   w.ssp = cv.take<float>((size_t)R * ((d + 1023) / 1024));
   w.rope = cv.take<float>((size_t)R * c.head_dim);  // [R][dh/2] (cos, sin)
@@ -350,6 +351,17 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
   // pre-attention norm of layer 0; later layers get it fused after the MLP
   launch_norm_rows(c.dtype, nullptr, 0, R, d, w.h, 0, h->layers[0].attn_norm, c.rms_eps, w.u, d,
                    nullptr, w.ssp, st);
+  AttnArgs a;
+  a.dtype = c.dtype;
+  a.q = w.q; a.kb = w.kb; a.vb = w.vb;
+  a.eff_ctx = w.eff_ctx;
+  a.bs = bs; a.C = n_copies; a.B = block;
+  a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.dh = c.head_dim; a.cap = kv->cap;
+  a.split = ap.split; a.nsplit = ap.nsplit;
+  a.scale = 1.0f / sqrtf((float)c.head_dim);
+  a.opart = w.opart; a.mlpart = w.mlpart; a.out = w.attn;
+  launch_attention_worklist(a, w.wlist, st);
+  a.worklist = w.wlist;
   for (int l = 0; l < c.n_layers; ++l) {
     const dstill_layer_weights &L = h->layers[l];
     GemmArgs g;
@@ -361,15 +373,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     launch_qkv_post(c.dtype, w.parts, g.splits, R, c.n_q_heads, c.n_kv_heads, c.head_dim,
                     w.eff_ctx, n_copies * block, block, L.q_norm, L.k_norm, c.qk_norm, c.rms_eps,
                     w.rope, w.q, w.kb, w.vb, st);
-    AttnArgs a;
-    a.dtype = c.dtype;
-    a.q = w.q; a.kb = w.kb; a.vb = w.vb; a.kc = kv->k[l]; a.vc = kv->v[l];
-    a.eff_ctx = w.eff_ctx;
-    a.bs = bs; a.C = n_copies; a.B = block;
-    a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.dh = c.head_dim; a.cap = kv->cap;
-    a.split = ap.split; a.nsplit = ap.nsplit;
-    a.scale = 1.0f / sqrtf((float)c.head_dim);
-    a.opart = w.opart; a.mlpart = w.mlpart; a.out = w.attn;
+    a.kc = kv->k[l]; a.vc = kv->v[l];
     launch_attention(a, st);
     // O projection, then h += o and the pre-MLP norm
     g.X = w.attn; g.ldx = qd; g.W = L.wo; g.ldw = qd; g.N = d; g.K = qd;

@@ -163,19 +163,48 @@ __device__ __forceinline__ void rescale(WS &ws, float cmax, float c) {
   }
 }
 
-// Workgroup -> (split, kv head, sequence-copy).  The grid is one-dimensional
-// with the split index varying slowest: consecutive workgroups, which the
-// dispatcher deals round-robin to the 8 XCDs, are different (sequence, head)
-// pairs of the same split, so every XCD gets an even share of long and
-// short contexts (with the split fastest, XCD k would run every split k,
-// and the late splits of ragged contexts are mostly empty), and the busy
-// low splits are dispatched first.
+// Workgroup -> (split, kv head, sequence-copy).  Items are numbered with the
+// split index slowest, item = sp * pairs + bc * hkv + h; the workgroups take
+// them in the order of a work list sorted by decreasing chunk count (built
+// once per call by attn_worklist_kernel), so full splits start first and the
+// short last splits of each context fill the tail.  Consecutive workgroups go
+// round-robin to the 8 XCDs, so each XCD gets an even share of the work.
 __device__ __forceinline__ void split_coords(const AttnArgs &a, int *sp, int *h, int *bc) {
   const int pairs = a.hkv * a.bs * a.C;
-  const int L = blockIdx.x;
+  const int L = a.worklist ? a.worklist[blockIdx.x] : (int)blockIdx.x;
   *sp = L / pairs;
   *h = (L % pairs) % a.hkv;
   *bc = (L % pairs) / a.hkv;
+}
+
+// Counting sort of the items by decreasing number of 64-key context chunks
+// (split 0 counts one more for the block keys; empty splits go last).  One
+// workgroup; the order within a count is whatever the atomics give, which
+// changes nothing but the schedule.
+__global__ __launch_bounds__(1024) void attn_worklist_kernel(AttnArgs a, int *__restrict__ list) {
+  constexpr int NB = 130;  // counts 0 .. 129 (split <= 128 chunks, + the block chunk)
+  __shared__ int hist[NB], base[NB];
+  const int pairs = a.hkv * a.bs * a.C, n = a.nsplit * pairs;
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  auto count = [&](int L) {
+    const int sp = L / pairs, bc = (L % pairs) / a.hkv;
+    const int S = a.eff_ctx[bc / a.C];
+    const int k0 = sp * a.split, k1 = min(k0 + a.split, S);
+    const int c = k1 > k0 ? (k1 - k0 + ATT_KC - 1) / ATT_KC : 0;
+    return min(c + (sp == 0 ? 1 : 0), NB - 1);
+  };
+  for (int L = threadIdx.x; L < n; L += blockDim.x) atomicAdd(&hist[count(L)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int c = NB - 1; c >= 0; --c) {
+      base[c] = acc;
+      acc += hist[c];
+    }
+  }
+  __syncthreads();
+  for (int L = threadIdx.x; L < n; L += blockDim.x) list[atomicAdd(&base[count(L)], 1)] = L;
 }
 
 // One wave's pass over a staged chunk holding `nk` valid keys (1..64), with
@@ -695,6 +724,11 @@ static void launch_typed(const AttnArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(attn_combine_kernel<T>,
                      dim3(a.bs * a.C, a.hq, (a.B + rows_per_wg - 1) / rows_per_wg), dim3(128), 0,
                      st, a);
+}
+
+void launch_attention_worklist(const AttnArgs &a, int *list, hipStream_t st) {
+  if (a.bs * a.C == 0) return;
+  hipLaunchKernelGGL(attn_worklist_kernel, dim3(1), dim3(1024), 0, st, a, list);
 }
 
 void launch_attention(const AttnArgs &a, hipStream_t st) {

@@ -73,7 +73,11 @@ struct AttnArgs {
   float *opart;        // [bs*C][hq][nsplit][B][dh]
   float *mlpart;       // [bs*C][hq][nsplit][B][2]  (running max in log2 units, sum)
   void *out;           // [bs*C*B, hq*dh]
+  const int *worklist = nullptr;  // optional [nsplit * hkv * bs*C] item order
 };
+// Item order for launch_attention, longest first (one small kernel; depends
+// only on eff_ctx and the split plan, so one list serves every layer).
+void launch_attention_worklist(const AttnArgs &a, int *list, hipStream_t st);
 void launch_attention(const AttnArgs &a, hipStream_t st);
 
 // ---- LM head with fused vocabulary reduction (lm_head.hip) -----------------
