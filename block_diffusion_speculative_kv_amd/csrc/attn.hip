@@ -605,21 +605,41 @@ __global__ __launch_bounds__(NTHR) void attn_split_dma_kernel(AttnArgs a) {
     for (int dt = 0; dt < DH / 16; ++dt)
       st.o[dt] = a0 * st.o[dt] + a1 * *reinterpret_cast<const f32x4 *>(xs + 4 * dt);
     st.m = mm;
+  } else {
+    __syncthreads();  // every wave is done with the ring before it stages records
   }
   if (!active) return;
 
   st.l += __shfl_xor(st.l, 16, WAVE);
   st.l += __shfl_xor(st.l, 32, WAVE);
-  if (r16 < a.B) {
-    const long rec = (((long)bc * a.hq + head) * a.nsplit + sp) * a.B + r16;
-    float *op = a.opart + rec * DH;
+  // The head's B records are one contiguous run of B * DH floats; a lane holds
+  // 4 dims of one row, so the wave stages O as [16][DH + 4] floats in LDS
+  // (within the region it used for the merge, or its own ring share) and
+  // writes the run with 16-byte stores across consecutive dims.
+  constexpr int OS = DH + 4, REGION = 64 * (DH / 4 + 4);  // floats: staged tile, wave's region
+  static_assert(16 * OS <= REGION, "staging fits the wave's merge region");
+  constexpr int STAGED_WAVES = KSPLIT == 2 ? NTHR / 128 : NTHR / 64;
+  constexpr bool STAGE = STAGED_WAVES * REGION * 4 <= (int)sizeof(AttnRing<DH>);
+  const long rec0 = (((long)bc * a.hq + head) * a.nsplit + sp) * a.B;
+  float *op = a.opart + rec0 * DH;
+  if constexpr (STAGE) {
+    float *ost = reinterpret_cast<float *>(&sm) + (long)(KSPLIT == 2 ? wave % group : wave) * REGION;
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt)
-      *reinterpret_cast<f32x4 *>(op + dt * 16 + 4 * g) = st.o[dt];
-    if (g == 0) {
-      a.mlpart[rec * 2] = st.m * c_log2;
-      a.mlpart[rec * 2 + 1] = st.l;
+      *reinterpret_cast<f32x4 *>(ost + r16 * OS + dt * 16 + 4 * g) = st.o[dt];
+    for (int i = lane; i < a.B * (DH / 4); i += 64) {
+      const int row = i / (DH / 4), c4 = 4 * (i % (DH / 4));
+      *reinterpret_cast<f32x4 *>(op + (long)row * DH + c4) =
+          *reinterpret_cast<const f32x4 *>(ost + row * OS + c4);
     }
+  } else if (r16 < a.B) {
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<f32x4 *>(op + (long)r16 * DH + dt * 16 + 4 * g) = st.o[dt];
+  }
+  if (r16 < a.B && g == 0) {
+    a.mlpart[(rec0 + r16) * 2] = st.m * c_log2;
+    a.mlpart[(rec0 + r16) * 2 + 1] = st.l;
   }
 }
 
