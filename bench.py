@@ -223,8 +223,10 @@ def main():
     if cfg["dtype"] != "bf16":
         head_kernel = "lm_head_kernel<float>"
     else:
-        head_kernel = ("lm_head_stream_kernel" if cyc.rows <= 16 else
-                       "lm_head_lds_kernel<%d>" % (1 if cyc.rows <= 32 else 2 if cyc.rows <= 64 else 4))
+        r = cyc.rows
+        head_kernel = ("lm_head_stream_kernel" if r <= 16 else
+                       "lm_head_lds_kernel<%d,%d>" % ((2, 1) if r <= 32 else (2, 2) if r <= 64
+                                                      else (2, 5) if r <= 160 else (4, 4)))
     head_kernel += " (+lm_combine_kernel)"
     traffic = None
     if args.workload == "q8b_bs32_rs":

@@ -36,14 +36,12 @@
 namespace dstill {
 
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
-constexpr int HEAD_NW = 4, HEAD_MW = 4;  // LDS path: 128 ids x 128 rows per workgroup
-constexpr int HEAD_VB_LDS = 32 * HEAD_NW;
 // LDS path: k per stage; W and X ring depths (80 KB: two workgroups per CU)
 constexpr int HEAD_KT = 64, HEAD_NSW = 3, HEAD_NSX = 2;
 constexpr int NXCD = 8;
 
 // Smallest vocabulary block of any path: sizes the partial-record workspace.
-int head_vocab_block() { return HEAD_VB_LDS; }
+int head_vocab_block() { return 64; }  // the smallest block any path uses
 
 struct RowStat {
   ArgTop2 arg;
@@ -219,13 +217,13 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
   }
 }
 
-// LDS-tiled variant (bf16): 128 vocabulary ids x 32 * MW rows per
-// workgroup.  MW = 4 at batch scale; MW = 1 or 2 for up to 32 or 64 rows,
-// where each weight tile has a single reader and the direct-copy ring keeps
-// two stages of it in flight per workgroup.
-template <int MW>
+// LDS-tiled variant (bf16): 32 * NW vocabulary ids x 32 * MW rows per
+// workgroup.  128 x 128 at batch scale.  Up to 160 rows the tile takes every
+// row (each weight tile has a single reader) and 64 ids, which keeps two
+// workgroups per compute unit and gives twice as many workgroups, so the
+// last round of a launch is small next to the others.
+template <int NW, int MW>
 __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
-  constexpr int NW = HEAD_NW;
   constexpr int BN = 32 * NW, BM = 32 * MW;
   __shared__ TileSmem<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> sm;
   int vb, rb;
@@ -243,15 +241,15 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   f32x4 acc[NW][MW];
   tile_mainloop<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX, true>(sm, ld, d / HEAD_KT, acc);
 
-  // The main loop ended with a barrier: its LDS is free.  The first 8 KB take
-  // the per-wave row records; stored logits are staged behind them as a
+  // The main loop ended with a barrier: its LDS is free.  The first RED bytes
+  // take the per-wave row records; stored logits are staged behind them as a
   // [BM][BN + 4] fp32 tile and written back as whole 512-byte row runs (a
   // lane's own values are 8 ids of one row, 16 rows per instruction).
   constexpr int LGS = BN + 4;  // staged row stride (floats): 16-row writes hit distinct banks
-  static_assert(2 * BM * (int)sizeof(RowStat) <= 8192, "row records");
-  static_assert(8192 + BM * LGS * 4 <= (int)sizeof(sm), "logits staging");
+  constexpr int RED = (2 * BM * (int)sizeof(RowStat) + 255) & ~255;  // row-record bytes
+  static_assert(RED + BM * LGS * 4 <= (int)sizeof(sm), "logits staging");
   RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm);
-  float *lg = reinterpret_cast<float *>(reinterpret_cast<char *>(&sm) + 8192);
+  float *lg = reinterpret_cast<float *>(reinterpret_cast<char *>(&sm) + RED);
   const bool stage = a.logits != nullptr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -485,21 +483,25 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
   // up to 16 rows stream the weight in 512-byte row slices; more rows go
-  // through the tile engine, with a row tile fitted to the row count (the
-  // LDS kernel addresses a block's hidden rows with 32-bit byte offsets)
-  const int mw = a.rows <= 32 ? 1 : a.rows <= 64 ? 2 : HEAD_MW;
-  const int BM = 32 * mw;
+  // through the tile engine, with a tile fitted to the row count (the LDS
+  // kernel addresses a block's hidden rows with 32-bit byte offsets)
+  int nw = 2, mw = 5;
+  if (a.rows <= 32) mw = 1;
+  else if (a.rows <= 64) mw = 2;
+  else if (a.rows > 160) nw = 4, mw = 4;
+  const int BM = 32 * mw, BN = 32 * nw;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
   if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
     a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
     hipLaunchKernelGGL(lm_head_stream_kernel, dim3(a.nvb), dim3(256), 0, st, a);
   } else if (a.dtype == 1 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
-    a.nvb = (a.vocab + HEAD_VB_LDS - 1) / HEAD_VB_LDS;
+    a.nvb = (a.vocab + BN - 1) / BN;
     const int nmb = (a.rows + BM - 1) / BM;
-    const int nvb8 = (a.nvb + NXCD - 1) / NXCD * NXCD;
-    if (mw == 1) hipLaunchKernelGGL(lm_head_lds_kernel<1>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
-    else if (mw == 2) hipLaunchKernelGGL(lm_head_lds_kernel<2>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
-    else hipLaunchKernelGGL(lm_head_lds_kernel<HEAD_MW>, dim3(nvb8 * nmb), dim3(256), 0, st, a, nmb);
+    const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nmb);
+    if (mw == 1) hipLaunchKernelGGL((lm_head_lds_kernel<2, 1>), grid, dim3(256), 0, st, a, nmb);
+    else if (mw == 2) hipLaunchKernelGGL((lm_head_lds_kernel<2, 2>), grid, dim3(256), 0, st, a, nmb);
+    else if (mw == 5) hipLaunchKernelGGL((lm_head_lds_kernel<2, 5>), grid, dim3(256), 0, st, a, nmb);
+    else hipLaunchKernelGGL((lm_head_lds_kernel<4, 4>), grid, dim3(256), 0, st, a, nmb);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;
     if (a.dtype == 1) launch_rows<bf16>(a, st);
