@@ -5,7 +5,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace dstill {
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N - 1, expanded at compile
+// time: register arrays indexed by i stay in registers however large the
+// body (a plain loop the compiler declines to unroll would index them
+// dynamically and move them to scratch memory).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -10,11 +10,11 @@
 //
 // Two kernels.  bf16 products whose depth is a multiple of 64 run on the
 // tile engine of mma_tile.hpp (gemm_lds_partial): 128 output features x 32,
-// 64 or 128 rows per workgroup, operands streamed HBM -> LDS by direct copies
-// (the weight three stages ahead), each staged weight tile re-used across the
-// workgroup's rows.  fp32 products and other depths load every MFMA operand
-// fragment straight from global memory into registers by the streaming loop
-// of common.hpp (gemm_nt_partial).
+// 64 or 128 rows per workgroup, or 256 x 256 from 2048 rows, operands
+// streamed HBM -> LDS by direct copies ahead of the multiply, each staged
+// weight tile re-used across the workgroup's rows.  fp32 products and other
+// depths load every MFMA operand fragment straight from global memory into
+// registers by the streaming loop of common.hpp (gemm_nt_partial).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mma_tile.hpp"
@@ -65,33 +65,47 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
   }
 }
 
-// LDS-tiled path: 128 x 32 MW blocks (MW = 4 from 65 rows, else 1 or 2), k-split
-// over stages of 64.
-constexpr int LDS_NW = 4;
-// k per stage; W and X ring depths (56-80 KB: two workgroups per CU)
-constexpr int LDS_KT = 64, LDS_NSW = 3, LDS_NSX = 2;
+// LDS-tiled path, k in stages of 64.  Below 2048 rows: 128 features x 32 MW
+// rows (MW = 4 from 65 rows, else 1 or 2), 2 x 2 waves, two workgroups per
+// compute unit.  From 2048 rows: 256 x 256, 2 x 4 waves, one workgroup per
+// compute unit: half the bytes copied into LDS per product term.
+constexpr int LDS_KT = 64;
 template <int MW>
-using LdsSmem = TileSmem<LDS_NW, MW, LDS_KT, LDS_NSW, LDS_NSX>;
-constexpr int LDS_PER_CU = 2;  // workgroups per compute unit (LDS and registers)
-static_assert(2 * sizeof(LdsSmem<4>) <= 160 * 1024, "two workgroups per CU");
+using SmallTile = TileEngine<2, 2, 4, MW, LDS_KT, 3, 2>;
+using BigTile = TileEngine<2, 4, 8, 4, LDS_KT, 2, 2>;
+static_assert(2 * sizeof(SmallTile<4>::Smem) <= 160 * 1024, "two workgroups per CU");
+static_assert(sizeof(BigTile::Smem) <= 160 * 1024, "one workgroup per CU");
+constexpr int BIG_MIN_ROWS = 2048;
 
 static int lds_mw(int M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
 
+// Wave rows (groups of 16 MW rows) staged per pass of the partial store: the
+// most that fit the idle rings as a [rows][BN + 4] fp32 tile.
+template <class E>
+constexpr int stage_wave_rows() {
+  int w = E::WM;
+  while (w > 1 && (E::WM % w != 0 ||
+                   (long)w * 16 * E::MW * (E::BN + 4) * 4 > (long)sizeof(typename E::Smem)))
+    --w;
+  return w;
+}
+
 // act != nullptr selects the fused SwiGLU epilogue (one split): n-block nb
-// covers features f0 = 64 nb .. f0 + 63, and tile row r (wave r / 64, in-wave
-// row r % 64) is gate row f0 + 32 (r / 64) + r % 32 for r % 64 < 32, else the
-// matching up row mlp + f0 + 32 (r / 64) + r % 32; so a lane's tiles i and
-// i + 2 hold the gate and up sums of the same 4 features of the same row.
-template <int MW>
-__global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
-                                                        const bf16 *__restrict__ W, long ldw,
-                                                        float *__restrict__ out, int M, int N,
-                                                        int nst, int st_per_split, int nnb,
-                                                        int nmb, bf16 *__restrict__ act,
-                                                        int mlp) {
-  constexpr int NW = LDS_NW;
-  constexpr int BN = 32 * NW, BM = 32 * MW;
-  __shared__ LdsSmem<MW> sm;
+// covers features f0 = (BN / 2) nb .. f0 + BN / 2 - 1.  With wave bands of
+// WB = 16 NW weight rows, tile row r (band r / WB, in-band row q = r % WB) is
+// gate row f0 + (WB / 2)(r / WB) + q for q < WB / 2, else the matching up row
+// mlp + f0 + (WB / 2)(r / WB) + q - WB / 2; so a lane's tiles i and i + NW / 2
+// hold the gate and up sums of the same 4 features of the same row.
+template <class E>
+__global__ __launch_bounds__(E::NT) void gemm_lds_partial(const bf16 *__restrict__ X, long ldx,
+                                                          const bf16 *__restrict__ W, long ldw,
+                                                          float *__restrict__ out, int M, int N,
+                                                          int nst, int st_per_split, int nnb,
+                                                          int nmb, bf16 *__restrict__ act,
+                                                          int mlp) {
+  constexpr int NW = E::NW, MW = E::MW, BN = E::BN, BM = E::BM;
+  constexpr int WB = 16 * NW, HB = WB / 2;
+  __shared__ typename E::Smem sm;
   int nb, mb;
   xcd_block(blockIdx.x, nmb, (nnb + 7) >> 3, &nb, &mb);
   if (nb >= nnb) return;
@@ -100,24 +114,27 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   const int m0 = mb * BM;
   const bool fused = act != nullptr;
   const int n0 = fused ? nb * (BN / 2) : nb * BN;
-  TileLoader<NW, MW, LDS_KT, LDS_NSW, LDS_NSX> ld;
+  typename E::Loader ld;
   auto xrow = [&](int r) { return (min(m0 + r, M - 1) - m0) * (int)ldx; };
   if (fused)
     ld.init(W + (long)n0 * ldw,
-            [&](int r) { return (((r & 32) ? mlp : 0) + 32 * (r >> 6) + (r & 31)) * (int)ldw; },
+            [&](int r) {
+              const int q = r % WB;
+              return ((q >= HB ? mlp : 0) + HB * (r / WB) + q % HB) * (int)ldw;
+            },
             X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
   else
     ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
             X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
   f32x4 acc[NW][MW];
-  tile_mainloop<NW, MW, LDS_KT, LDS_NSW, LDS_NSX, false>(sm, ld, s1 - s0, acc);
+  E::template mainloop<false>(sm, ld, s1 - s0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % E::WN, wm = wave / E::WN;
   if (fused) {
 #pragma unroll
     for (int i = 0; i < NW / 2; ++i) {
-      const int f = n0 + 32 * wn + 16 * i + 4 * g;
+      const int f = n0 + HB * wn + 16 * i + 4 * g;
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
         const int m = m0 + wm * 16 * MW + 16 * j + r16;
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
         bf16 v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float gt = acc[i][j][e], up = acc[i + 2][j][e];
+          const float gt = acc[i][j][e], up = acc[i + NW / 2][j][e];
           v[e] = from_f32<bf16>(gt / (1.0f + expf(-gt)) * up);
         }
         *reinterpret_cast<uint2 *>(act + (long)m * mlp + f) = *reinterpret_cast<const uint2 *>(v);
@@ -135,31 +152,39 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
   }
   // A lane holds 4 consecutive features of one row, so direct stores would
   // touch 16 rows x 64 bytes per instruction: the tile goes through the idle
-  // ring as [BM][BN + 4] fp32 and leaves as whole 512-byte row runs.
+  // rings as [rows][BN + 4] fp32, WPP wave rows at a time, and leaves as
+  // whole row runs.
   constexpr int OS = BN + 4;  // staged row stride (floats)
-  static_assert(BM * OS * 4 <= (int)sizeof(LdsSmem<MW>), "partial staging");
+  constexpr int WPP = stage_wave_rows<E>(), RP = WPP * 16 * MW;
+  static_assert(RP * OS * 4 <= (int)sizeof(typename E::Smem), "partial staging");
   float *ot = reinterpret_cast<float *>(&sm);
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-#pragma unroll
-    for (int j = 0; j < MW; ++j)
-      *reinterpret_cast<f32x4 *>(ot + (wm * 16 * MW + 16 * j + r16) * OS + wn * 16 * NW + 16 * i +
-                                 4 * g) = acc[i][j];
-  __syncthreads();
   float *o = out + (long)blockIdx.y * M * N;
-  for (int idx = threadIdx.x; idx < BM * (BN / 4); idx += blockDim.x) {
-    const int rl = idx / (BN / 4), nl = 4 * (idx % (BN / 4));
-    const int m = m0 + rl, n = n0 + nl;
-    if (m >= M || n >= N) continue;
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(ot + rl * OS + nl);
-    float *dst = o + (long)m * N + n;
-    if ((N & 3) == 0) {
-      *reinterpret_cast<f32x4 *>(dst) = x;
-    } else {
+#pragma unroll 1
+  for (int p = 0; p < E::WM / WPP; ++p) {
+    if (wm / WPP == p) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < N) dst[e] = x[e];
+      for (int i = 0; i < NW; ++i)
+#pragma unroll
+        for (int j = 0; j < MW; ++j)
+          *reinterpret_cast<f32x4 *>(ot + ((wm % WPP) * 16 * MW + 16 * j + r16) * OS +
+                                     wn * 16 * NW + 16 * i + 4 * g) = acc[i][j];
     }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < RP * (BN / 4); idx += E::NT) {
+      const int rl = idx / (BN / 4), nl = 4 * (idx % (BN / 4));
+      const int m = m0 + p * RP + rl, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(ot + rl * OS + nl);
+      float *dst = o + (long)m * N + n;
+      if ((N & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(dst) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = x[e];
+      }
+    }
+    if (p + 1 < E::WM / WPP) __syncthreads();
   }
 }
 
@@ -168,32 +193,41 @@ __global__ __launch_bounds__(256) void gemm_lds_partial(const bf16 *__restrict__
 // at any row count); fp32 and other depths take gemm_nt_partial
 static bool use_lds(int K, int dtype) { return dtype == 1 && K % LDS_KT == 0; }
 
-static void lds_geometry(int M, int N, int K, int ncu, int *nnb, int *nmb, int *nst,
-                         int *splits, int *per) {
-  const int BN = 32 * LDS_NW, BM = 32 * lds_mw(M);
-  *nnb = (N + BN - 1) / BN;
-  *nmb = (M + BM - 1) / BM;
-  *nst = K / LDS_KT;
-  const long tiles = (long)*nnb * *nmb;
-  // Workgroups run in rounds of ncu x LDS_PER_CU.  Estimated time of a
-  // split count s: rounds x (stages per workgroup x ~0.3 us per 64-deep
-  // stage, shared by the workgroups of a compute unit, + ~1 us of pipeline
-  // fill), plus the fp32 partial plane each split writes and the consumer
-  // reads back (~6 TB/s).  The smallest s within 3% of the best wins.
+struct LdsPlan {
+  bool big;
+  int BN, BM, nnb, nmb, nst, splits, per;
+};
+
+static LdsPlan lds_geometry(int M, int N, int K, int ncu) {
+  LdsPlan p;
+  p.big = M >= BIG_MIN_ROWS;
+  p.BN = p.big ? BigTile::BN : SmallTile<4>::BN;
+  p.BM = p.big ? BigTile::BM : 32 * lds_mw(M);
+  p.nnb = (N + p.BN - 1) / p.BN;
+  p.nmb = (M + p.BM - 1) / p.BM;
+  p.nst = K / LDS_KT;
+  const long tiles = (long)p.nnb * p.nmb;
+  // Workgroups run in rounds of ncu x (2 small or 1 large) slots.  Estimated
+  // time of a split count s: rounds x (stages per workgroup x ~0.6 us per
+  // 64-deep stage of a round of small tiles, ~1.5 times that for large ones,
+  // + ~1 us of pipeline fill), plus the fp32 partial plane each split writes
+  // and the consumer reads back (~6 TB/s).  The smallest s within 3% of the
+  // best wins.
+  const long slots = (long)ncu * (p.big ? 1 : 2);
+  const double stage_us = p.big ? 0.9 : 0.6;
   auto est = [&](int s) {
-    const int per = (*nst + s - 1) / s;
-    const long slots = (long)ncu * LDS_PER_CU;
+    const int per = (p.nst + s - 1) / s;
     const long rounds = (tiles * s + slots - 1) / slots;
-    return (double)rounds * (per * 0.3 * LDS_KT / 64 * LDS_PER_CU + 1.0) +
-           (double)s * M * N * 8.0 / 6e6;
+    return (double)rounds * (per * stage_us + 1.0) + (double)s * M * N * 8.0 / 6e6;
   };
-  const int smax = max(1, min(16, *nst / 2));
+  const int smax = max(1, min(16, p.nst / 2));
   double best = est(1);
   for (int s = 2; s <= smax; ++s) best = fmin(best, est(s));
   int s = 1;
   while (est(s) > best * 1.03) ++s;
-  *per = (*nst + s - 1) / s;
-  *splits = (*nst + *per - 1) / *per;
+  p.per = (p.nst + s - 1) / s;
+  p.splits = (p.nst + p.per - 1) / p.per;
+  return p;
 }
 
 // Host-side plan: wave tile of NTW x MTW 16x16 tiles, 4 waves along N, and a
@@ -212,7 +246,7 @@ static void launch_tile(const GemmArgs &a, hipStream_t st) {
 }
 
 bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu) {
-  if (!use_lds(K, dtype) || mlp % 64 != 0 || M <= 0) return false;
+  if (!use_lds(K, dtype) || mlp % 64 != 0 || M <= 0 || M >= BIG_MIN_ROWS) return false;
   const long tiles = (long)(mlp / 64) * ((M + 32 * lds_mw(M) - 1) / (32 * lds_mw(M)));
   return tiles >= num_cu;
 }
@@ -220,11 +254,7 @@ bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu) {
 // Chooses the wave tile from M and the number of k-splits; returns the split
 // count the output buffer must hold.
 int gemm_plan_splits(int M, int N, int K, int dtype, int num_cu) {
-  if (use_lds(K, dtype)) {
-    int nnb, nmb, nst, splits, per;
-    lds_geometry(M, N, K, num_cu, &nnb, &nmb, &nst, &splits, &per);
-    return splits;
-  }
+  if (use_lds(K, dtype)) return lds_geometry(M, N, K, num_cu).splits;
   const int KW = dtype == 1 ? 32 : 16;
   const int nks = K / KW;
   int ntw, mtw;
@@ -260,43 +290,38 @@ static void launch_typed(const GemmArgs &a, hipStream_t st) {
   else launch_tile<T, 4, 4>(a, st);
 }
 
+template <class E>
+static void launch_lds(const GemmArgs &a, int nnb, int nmb, int per, int splits, bf16 *act,
+                       hipStream_t st) {
+  const dim3 grid((nnb + 7) / 8 * 8 * nmb, splits);
+  hipLaunchKernelGGL((gemm_lds_partial<E>), grid, dim3(E::NT), 0, st, (const bf16 *)a.X, a.ldx,
+                     (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, a.K / LDS_KT, per, nnb, nmb, act,
+                     a.mlp);
+}
+
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.swiglu_act) {
-    // fused gate|up + SwiGLU: 64 features (128 weight rows) per n-block
+    // fused gate|up + SwiGLU (small tiles only): 64 features (128 weight rows)
+    // per n-block
     const int mw = lds_mw(a.M), BM = 32 * mw;
     const int nnb = a.mlp / 64, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
-    const dim3 grid((nnb + 7) / 8 * 8 * nmb, 1);
     bf16 *act = (bf16 *)a.swiglu_act;
-    if (mw == 1)
-      hipLaunchKernelGGL(gemm_lds_partial<1>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
-    else if (mw == 2)
-      hipLaunchKernelGGL(gemm_lds_partial<2>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
-    else
-      hipLaunchKernelGGL(gemm_lds_partial<4>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, nst, nnb, nmb, act, a.mlp);
+    if (mw == 1) launch_lds<SmallTile<1>>(a, nnb, nmb, nst, 1, act, st);
+    else if (mw == 2) launch_lds<SmallTile<2>>(a, nnb, nmb, nst, 1, act, st);
+    else launch_lds<SmallTile<4>>(a, nnb, nmb, nst, 1, act, st);
     return;
   }
   if (use_lds(a.K, a.dtype)) {
+    // the tile depends on M alone (the plan that chose a.splits used it too)
+    const bool big = a.M >= BIG_MIN_ROWS;
     const int mw = lds_mw(a.M);
-    const int BN = 32 * LDS_NW, BM = 32 * mw;
+    const int BN = big ? BigTile::BN : SmallTile<4>::BN, BM = big ? BigTile::BM : 32 * mw;
     const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
     const int per = (nst + a.splits - 1) / a.splits;
-    const int nnb8 = (nnb + 7) / 8 * 8;
-    const dim3 grid(nnb8 * nmb, a.splits);
-    if (mw == 1)
-      hipLaunchKernelGGL(gemm_lds_partial<1>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
-                         0);
-    else if (mw == 2)
-      hipLaunchKernelGGL(gemm_lds_partial<2>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
-                         0);
-    else
-      hipLaunchKernelGGL(gemm_lds_partial<4>, grid, dim3(256), 0, st, (const bf16 *)a.X, a.ldx,
-                         (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, nst, per, nnb, nmb, nullptr,
-                         0);
+    if (big) launch_lds<BigTile>(a, nnb, nmb, per, a.splits, nullptr, st);
+    else if (mw == 1) launch_lds<SmallTile<1>>(a, nnb, nmb, per, a.splits, nullptr, st);
+    else if (mw == 2) launch_lds<SmallTile<2>>(a, nnb, nmb, per, a.splits, nullptr, st);
+    else launch_lds<SmallTile<4>>(a, nnb, nmb, per, a.splits, nullptr, st);
     return;
   }
   if (a.dtype == 1) launch_typed<bf16>(a, st);

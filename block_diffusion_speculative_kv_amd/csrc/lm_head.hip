@@ -36,8 +36,14 @@
 namespace dstill {
 
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
-// LDS path: k per stage; W and X ring depths (80 KB: two workgroups per CU)
-constexpr int HEAD_KT = 64, HEAD_NSW = 3, HEAD_NSX = 2;
+constexpr int HEAD_KT = 64;   // LDS path: k per stage
+// LDS-path tiles (vocabulary ids x rows), 2 x 2 waves, two workgroups per CU:
+// 64 x 32, 64 x 64 and 64 x 160 for up to 160 rows, 128 x 128 beyond.  (A
+// 256 x 256 tile with one workgroup per CU copies half the bytes into LDS
+// but leaves the matrix cores idle during its sampling epilogue, which the
+// second workgroup of a CU otherwise overlaps: no faster at 480 rows.)
+template <int NW, int MW>
+using HeadTile = TileEngine<2, 2, NW, MW, HEAD_KT, 3, 2>;
 constexpr int NXCD = 8;
 
 // Smallest vocabulary block of any path: sizes the partial-record workspace.
@@ -217,15 +223,18 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
   }
 }
 
-// LDS-tiled variant (bf16): 32 * NW vocabulary ids x 32 * MW rows per
-// workgroup.  128 x 128 at batch scale.  Up to 160 rows the tile takes every
-// row (each weight tile has a single reader) and 64 ids, which keeps two
-// workgroups per compute unit and gives twice as many workgroups, so the
-// last round of a launch is small next to the others.
-template <int NW, int MW>
-__global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
-  constexpr int BN = 32 * NW, BM = 32 * MW;
-  __shared__ TileSmem<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> sm;
+// LDS-tiled variant (bf16): BN vocabulary ids x BM rows per workgroup on the
+// tile engine E.  Up to 160 rows the tile takes every row (each weight tile
+// has a single reader) and 64 ids, which gives many workgroups, so the last
+// round of a launch is small next to the others.  At batch scale 128 x 128
+// re-uses each staged weight tile across 128 rows.
+template <class E>
+constexpr int head_stage_wave_rows();
+
+template <class E>
+__global__ __launch_bounds__(E::NT) void lm_head_lds_kernel(HeadArgs a, int nmb) {
+  constexpr int NW = E::NW, MW = E::MW, BN = E::BN, BM = E::BM;
+  __shared__ typename E::Smem sm;
   int vb, rb;
   xcd_block(blockIdx.x, nmb, (a.nvb + 7) >> 3, &vb, &rb);
   if (vb >= a.nvb) return;
@@ -233,68 +242,99 @@ __global__ __launch_bounds__(256) void lm_head_lds_kernel(HeadArgs a, int nmb) {
   const int V = a.vocab, d = a.d;
   const bf16 *W = (const bf16 *)a.w;
   const bf16 *H = (const bf16 *)a.hidden;
-  TileLoader<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX> ld;
+  typename E::Loader ld;
   auto hrow = [&](int r) { return (r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq; };
   const int h0 = hrow(r0);
   ld.init(W + (long)v0 * d, [&](int i) { return (min(v0 + i, V - 1) - v0) * d; },
           H + (long)h0 * d, [&](int i) { return (hrow(min(r0 + i, a.rows - 1)) - h0) * d; }, 0);
   f32x4 acc[NW][MW];
-  tile_mainloop<NW, MW, HEAD_KT, HEAD_NSW, HEAD_NSX, true>(sm, ld, d / HEAD_KT, acc);
+  E::template mainloop<true>(sm, ld, d / HEAD_KT, acc);
 
   // The main loop ended with a barrier: its LDS is free.  The first RED bytes
-  // take the per-wave row records; stored logits are staged behind them as a
-  // [BM][BN + 4] fp32 tile and written back as whole 512-byte row runs (a
-  // lane's own values are 8 ids of one row, 16 rows per instruction).
+  // take the per-wave row records; stored logits are staged behind them as
+  // [rows][BN + 4] fp32 tiles, WPP wave rows at a time, and written back as
+  // whole row runs (a lane's own values are 8 ids of one row, 16 rows per
+  // instruction).
   constexpr int LGS = BN + 4;  // staged row stride (floats): 16-row writes hit distinct banks
-  constexpr int RED = (2 * BM * (int)sizeof(RowStat) + 255) & ~255;  // row-record bytes
-  static_assert(RED + BM * LGS * 4 <= (int)sizeof(sm), "logits staging");
+  constexpr int RED = (E::WN * BM * (int)sizeof(RowStat) + 255) & ~255;  // row-record bytes
+  constexpr int WPP = head_stage_wave_rows<E>(), RP = WPP * 16 * MW;
+  static_assert(RED + RP * LGS * 4 <= (int)sizeof(typename E::Smem), "logits staging");
   RowStat(*red)[BM] = reinterpret_cast<RowStat(*)[BM]>(&sm);
   float *lg = reinterpret_cast<float *>(reinterpret_cast<char *>(&sm) + RED);
-  const bool stage = a.logits != nullptr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % E::WN, wm = wave / E::WN;
   const int vw = v0 + wn * 16 * NW;
-#pragma unroll
-  for (int mt = 0; mt < MW; ++mt) {
-    const int rl = wm * 16 * MW + 16 * mt + r16;
-    float zz[NW / 2][8];
+  // lane's values of m-tile mt: 8 consecutive ids vw + 32 p + 8 g .. + 7
+  auto lane_vals = [&](int mt, float (&zz)[NW / 2][8]) {
 #pragma unroll
     for (int p = 0; p < NW / 2; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][mt][e & 3];
-    if (stage) {
-#pragma unroll
-      for (int p = 0; p < NW / 2; ++p) {
-        float *dst = lg + rl * LGS + wn * 16 * NW + 32 * p + 8 * g;
-        *reinterpret_cast<f32x4 *>(dst) = f32x4{zz[p][0], zz[p][1], zz[p][2], zz[p][3]};
-        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{zz[p][4], zz[p][5], zz[p][6], zz[p][7]};
-      }
-    }
+  };
+  static_for<MW>([&](auto MT) {
+    constexpr int mt = decltype(MT)::value;
+    const int rl = wm * 16 * MW + 16 * mt + r16;
+    float zz[NW / 2][8];
+    lane_vals(mt, zz);
     RowStat st = lane_rowstat<NW / 2, false>(a, r0 + rl, vw, g, zz);
     if (g == 0) red[wn][rl] = st;
-  }
-  __syncthreads();
-  if (stage) {
-    for (int i = threadIdx.x; i < BM * (BN / 4); i += blockDim.x) {
-      const int rl = i / (BN / 4), v = v0 + 4 * (i % (BN / 4)), r = r0 + rl;
-      if (r >= a.rows || v >= V) continue;
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(lg + rl * LGS + (v - v0));
-      float *dst = a.logits + (long)r * V + v;
-      if (v + 4 <= V && (V & 3) == 0) {
-        *reinterpret_cast<f32x4 *>(dst) = x;
-      } else {
+  });
+  if (a.logits != nullptr) {
+#pragma unroll 1
+    for (int p = 0; p < E::WM / WPP; ++p) {
+      if (wm / WPP == p) {
+        static_for<MW>([&](auto MT) {
+          constexpr int mt = decltype(MT)::value;
+          float zz[NW / 2][8];
+          lane_vals(mt, zz);
+          const int rs = (wm % WPP) * 16 * MW + 16 * mt + r16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (v + e < V) dst[e] = x[e];
+          for (int q = 0; q < NW / 2; ++q) {
+            float *dst = lg + rs * LGS + wn * 16 * NW + 32 * q + 8 * g;
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{zz[q][0], zz[q][1], zz[q][2], zz[q][3]};
+            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{zz[q][4], zz[q][5], zz[q][6], zz[q][7]};
+          }
+        });
       }
+      __syncthreads();
+      for (int i = threadIdx.x; i < RP * (BN / 4); i += E::NT) {
+        const int rl = i / (BN / 4), v = v0 + 4 * (i % (BN / 4)), r = r0 + p * RP + rl;
+        if (r >= a.rows || v >= V) continue;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(lg + rl * LGS + (v - v0));
+        float *dst = a.logits + (long)r * V + v;
+        if (v + 4 <= V && (V & 3) == 0) {
+          *reinterpret_cast<f32x4 *>(dst) = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < V) dst[e] = x[e];
+        }
+      }
+      if (p + 1 < E::WM / WPP) __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < BM; i += blockDim.x) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < BM; i += E::NT) {
     const int r = r0 + i;
     if (r >= a.rows) continue;
-    a.part[(long)r * a.nvb + vb] = to_partial(rowstat_merge(red[0][i], red[1][i]));
+    RowStat st = red[0][i];
+#pragma unroll
+    for (int w = 1; w < E::WN; ++w) st = rowstat_merge(st, red[w][i]);
+    a.part[(long)r * a.nvb + vb] = to_partial(st);
   }
+}
+
+// Wave rows staged per pass of the logits store: the most that fit behind
+// the row records.
+template <class E>
+constexpr int head_stage_wave_rows() {
+  const long red = ((long)E::WN * E::BM * sizeof(RowStat) + 255) & ~255L;
+  int w = E::WM;
+  while (w > 1 && (E::WM % w != 0 ||
+                   red + (long)w * 16 * E::MW * (E::BN + 4) * 4 > (long)sizeof(typename E::Smem)))
+    --w;
+  return w;
 }
 
 // Weight-streaming variant for up to 16 rows (bf16, one row tile): the
@@ -479,17 +519,21 @@ static void launch_rows(const HeadArgs &a, hipStream_t st) {
   else launch_typed<T, 4>(a, st);
 }
 
+template <class E>
+static void launch_head_tile(const HeadArgs &a, dim3 grid, int nmb, hipStream_t st) {
+  hipLaunchKernelGGL((lm_head_lds_kernel<E>), grid, dim3(E::NT), 0, st, a, nmb);
+}
+
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
   // up to 16 rows stream the weight in 512-byte row slices; more rows go
   // through the tile engine, with a tile fitted to the row count (the LDS
   // kernel addresses a block's hidden rows with 32-bit byte offsets)
-  int nw = 2, mw = 5;
-  if (a.rows <= 32) mw = 1;
-  else if (a.rows <= 64) mw = 2;
-  else if (a.rows > 160) nw = 4, mw = 4;
-  const int BM = 32 * mw, BN = 32 * nw;
+  int BN = 64, BM = 160;
+  if (a.rows <= 32) BM = 32;
+  else if (a.rows <= 64) BM = 64;
+  else if (a.rows > 160) BN = 128, BM = 128;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
   if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
     a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
@@ -498,10 +542,10 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
     a.nvb = (a.vocab + BN - 1) / BN;
     const int nmb = (a.rows + BM - 1) / BM;
     const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nmb);
-    if (mw == 1) hipLaunchKernelGGL((lm_head_lds_kernel<2, 1>), grid, dim3(256), 0, st, a, nmb);
-    else if (mw == 2) hipLaunchKernelGGL((lm_head_lds_kernel<2, 2>), grid, dim3(256), 0, st, a, nmb);
-    else if (mw == 5) hipLaunchKernelGGL((lm_head_lds_kernel<2, 5>), grid, dim3(256), 0, st, a, nmb);
-    else hipLaunchKernelGGL((lm_head_lds_kernel<4, 4>), grid, dim3(256), 0, st, a, nmb);
+    if (BM == 32) launch_head_tile<HeadTile<2, 1>>(a, grid, nmb, st);
+    else if (BM == 64) launch_head_tile<HeadTile<2, 2>>(a, grid, nmb, st);
+    else if (BM == 160) launch_head_tile<HeadTile<2, 5>>(a, grid, nmb, st);
+    else launch_head_tile<HeadTile<4, 4>>(a, grid, nmb, st);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;
     if (a.dtype == 1) launch_rows<bf16>(a, st);

@@ -1,16 +1,17 @@
 // LDS-tiled bf16 MFMA main loop shared by the dense projections with many
 // rows and by the LM head at batch scale.
 //
-// A workgroup of 4 waves (2 x 2) computes a BN x BM block of C = W . X^T,
+// A workgroup of WN x WM waves computes a BN x BM block of C = W . X^T,
 // W [N, K] the weight (MFMA A operand, output features), X [M, K] the
 // activations (MFMA B operand, rows); each wave owns NW x MW 16x16 tiles.
 // k advances in stages of KT through rings of LDS buffers filled by direct
 // global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
-// the instruction's LDS base + 16 * lane), issued ahead of the multiply: the copies need no registers and no LDS write
-// instructions, and the only wait is one vmcnt + barrier per stage.  The
-// loads are issued from inline assembly with an explicit vmcnt, because the
-// compiler, which cannot tell the ring buffers apart, would otherwise wait
-// for every outstanding copy before each LDS read.
+// the instruction's LDS base + 16 * lane), issued ahead of the multiply: the
+// copies need no registers and no LDS write instructions, and the only wait
+// is one vmcnt + barrier per stage.  The loads are issued from inline
+// assembly with an explicit vmcnt, because the compiler, which cannot tell
+// the ring buffers apart, would otherwise wait for every outstanding copy
+// before each LDS read.
 //
 // LDS rows are KT * 2 bytes (unpadded); 16-byte chunk c of row r sits at
 // chunk c ^ tile_swz(r), so the 16 rows of one fragment read (contiguous
@@ -29,21 +30,6 @@
 
 namespace dstill {
 
-// KT: k per LDS stage (64 or 32).  W stages sit in a ring of NSW buffers,
-// X stages in a ring of NSX: the weight, streamed once from HBM, is fetched
-// NSW - 1 stages ahead of the multiply, the activations (re-read by every
-// weight block, mostly from L2) NSX - 1 stages ahead.  A row of a stage is
-// KT * 2 bytes, CPR = KT / 8 chunks of 16 bytes; one copy instruction (64
-// lanes x 16 bytes) fills RPI = 1024 / (KT * 2) rows.
-template <int NW, int MW, int KT, int NSW, int NSX>
-struct TileSmem {
-  static_assert(KT == 64 || KT == 32, "stage depth");
-  static_assert(NSX == 2 && NSW >= 2 && NSW <= 6, "ring depths");
-  static constexpr int BN = 32 * NW, BM = 32 * MW;
-  bf16 w[NSW][BN * KT];
-  bf16 x[NSX][BM * KT];
-};
-
 // Chunk swizzle.  KT = 64 (8 chunks, 2 rows per 256-byte bank window): bits
 // (r1, r3, r2 ^ r4); KT = 32 (4 chunks, 4 rows per window): bits (r2 ^ r4,
 // r3).  Over 16 contiguous rows (r0..r3 vary) and over the permuted rows of
@@ -55,133 +41,164 @@ __device__ __forceinline__ int tile_swz(int r) {
   return (((r >> 2) ^ (r >> 4)) & 1) | ((r >> 2) & 2);
 }
 
-// Copier for one workgroup's W and X tiles.  Per stage, each wave issues
-// NCW copies of W and NCX of X; copy i of wave w fills row group 4i + w (RPI
-// rows), lane L loading row RPI * group + L / CPR, logical chunk
-// (L % CPR) ^ tile_swz(row).  Each matrix is addressed from one wave-uniform
-// base (the block's first row, advanced by whole stages) plus a 32-bit
-// per-lane byte offset.
-template <int NW, int MW, int KT, int NSW, int NSX>
-struct TileLoader {
-  static constexpr int CPR = KT / 8, RPI = 64 / CPR;
-  static constexpr int NCW = 32 * NW / RPI / 4, NCX = 32 * MW / RPI / 4;
-  static constexpr int OPS = NCW + NCX;  // copies per wave per stage
-  const char *wbase, *xbase;
-  uint32_t woff[NCW], xoff[NCX];
-
-  // wrow(r) / xrow(r): element offset of tile row r from wb / xb (already
-  // clamped to a valid row; twice it must fit in 32 bits); k0: first k of
-  // this workgroup's range.
-  template <typename WRow, typename XRow>
-  __device__ __forceinline__ void init(const bf16 *wb, WRow wrow, const bf16 *xb, XRow xrow,
-                                       long k0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    wbase = reinterpret_cast<const char *>(wb + k0);
-    xbase = reinterpret_cast<const char *>(xb + k0);
-#pragma unroll
-    for (int i = 0; i < NCW; ++i) {
-      const int r = RPI * (4 * i + wave) + lane / CPR;
-      woff[i] = (uint32_t)wrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < NCX; ++i) {
-      const int r = RPI * (4 * i + wave) + lane / CPR;
-      xoff[i] = (uint32_t)xrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
-    }
-  }
-  __device__ __forceinline__ void issue_w(TileSmem<NW, MW, KT, NSW, NSX> &sm, int stage) const {
-    const char *wb = wbase + (long)stage * KT * 2;
-    const uint32_t wl = lds_u32(&sm.w[stage % NSW][0]) + (threadIdx.x >> 6) * 1024;
-#pragma unroll
-    for (int i = 0; i < NCW; ++i) dma16(wb, woff[i], wl + i * 4096);
-  }
-  __device__ __forceinline__ void issue_x(TileSmem<NW, MW, KT, NSW, NSX> &sm, int stage) const {
-    const char *xb = xbase + (long)stage * KT * 2;
-    const uint32_t xl = lds_u32(&sm.x[stage % NSX][0]) + (threadIdx.x >> 6) * 1024;
-#pragma unroll
-    for (int i = 0; i < NCX; ++i) dma16(xb, xoff[i], xl + i * 4096);
-  }
-};
-
-// Row (within the workgroup's BN rows) that lane r16 feeds for tile i.
-template <int NW, bool PERM>
-__device__ __forceinline__ int tile_a_row(int wn, int i, int r16) {
-  if (PERM) return wn * 16 * NW + 32 * (i >> 1) + 8 * (r16 >> 2) + 4 * (i & 1) + (r16 & 3);
-  return wn * 16 * NW + 16 * i + r16;
-}
-
 // Byte offset of lane (g, r16)'s 16-byte k-chunk 4 kk + g of LDS row r.
 template <int KT>
 __device__ __forceinline__ int tile_frag_off(int r, int kk, int g) {
   return r * (KT * 2) + (((4 * kk + g) ^ tile_swz<KT>(r)) * 16);
 }
 
-template <int NW, int MW, int KT, int NSW, int NSX, bool PERM>
-__device__ __forceinline__ void tile_mainloop(TileSmem<NW, MW, KT, NSW, NSX> &sm,
-                                              const TileLoader<NW, MW, KT, NSW, NSX> &ld, int nst,
-                                              f32x4 (&acc)[NW][MW]) {
-  constexpr int NCW = TileLoader<NW, MW, KT, NSW, NSX>::NCW;
-  constexpr int NKK = KT / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;
+// One tile configuration: WN x WM waves, each owning NW x MW 16x16 output
+// tiles, so a workgroup computes BN = 16 NW WN output features x BM = 16 MW
+// WM rows.  KT: k per LDS stage (64 or 32).  W stages sit in a ring of NSW
+// buffers, X stages in a ring of NSX: the weight, streamed once from HBM, is
+// fetched NSW - 1 stages ahead of the multiply, the activations (re-read by
+// every weight block, mostly from L2) NSX - 1 stages ahead.  A row of a stage
+// is KT * 2 bytes, CPR = KT / 8 chunks of 16 bytes; one copy instruction (64
+// lanes x 16 bytes) fills RPI = 1024 / (KT * 2) rows.
+//
+// 2 x 2 waves with 128 x 128 tiles keep two workgroups on a compute unit;
+// 2 x 4 waves with 256 x 256 tiles take one compute unit each and halve the
+// bytes copied into LDS per product term, which is what bounds the smaller
+// tile once the rows are many.
+template <int WN_, int WM_, int NW_, int MW_, int KT_, int NSW_, int NSX_>
+struct TileEngine {
+  static constexpr int WN = WN_, WM = WM_, NW = NW_, MW = MW_, KT = KT_, NSW = NSW_, NSX = NSX_;
+  static constexpr int NWAVES = WN * WM, NT = 64 * NWAVES;
+  static constexpr int BN = 16 * NW * WN, BM = 16 * MW * WM;
+  static constexpr int CPR = KT / 8, RPI = 64 / CPR;
+  // copies per stage (TW, TX) and per wave (NCW, NCX): every wave takes the
+  // same number of W copies; X copies may fall short by one on the last waves
+  static constexpr int TW = BN / RPI, TX = BM / RPI;
+  static constexpr int NCW = TW / NWAVES, NCX = (TX + NWAVES - 1) / NWAVES;
+  static_assert(KT == 64 || KT == 32, "stage depth");
+  static_assert(NSX == 2 && NSW >= 2 && NSW <= 4, "ring depths");
+  static_assert(TW * RPI == BN && TX * RPI == BM && NCW * NWAVES == TW, "whole copies");
+
+  struct Smem {
+    bf16 w[NSW][BN * KT];
+    bf16 x[NSX][BM * KT];
+  };
+
+  // Copier for one workgroup's W and X tiles.  Copy i of wave w fills row
+  // group NWAVES i + w (RPI rows; X copies only while the group exists), lane
+  // L loading row RPI * group + L / CPR, logical chunk (L % CPR) ^
+  // tile_swz(row).  A wave's X copies are issued before any W copy the wait
+  // may leave in flight, so one issuing fewer of them waits no less.  Each matrix is addressed from
+  // one wave-uniform base (the block's first row, advanced by whole stages)
+  // plus a 32-bit per-lane byte offset.
+  struct Loader {
+    const char *wbase, *xbase;
+    uint32_t woff[NCW], xoff[NCX];
+
+    // wrow(r) / xrow(r): element offset of tile row r from wb / xb (already
+    // clamped to a valid row; twice it must fit in 32 bits); k0: first k of
+    // this workgroup's range.
+    template <typename WRow, typename XRow>
+    __device__ __forceinline__ void init(const bf16 *wb, WRow wrow, const bf16 *xb, XRow xrow,
+                                         long k0) {
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      wbase = reinterpret_cast<const char *>(wb + k0);
+      xbase = reinterpret_cast<const char *>(xb + k0);
 #pragma unroll
-  for (int i = 0; i < NW; ++i)
+      for (int i = 0; i < NCW; ++i) {
+        const int r = RPI * (NWAVES * i + wave) + lane / CPR;
+        woff[i] = (uint32_t)wrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
+      }
 #pragma unroll
-    for (int j = 0; j < MW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nst <= 0) return;
-  int aoff[NW][NKK], boff[MW][NKK];
+      for (int i = 0; i < NCX; ++i) {
+        const int r = min(RPI * (NWAVES * i + wave) + lane / CPR, BM - 1);
+        xoff[i] = (uint32_t)xrow(r) * 2u + (uint32_t)(((lane % CPR) ^ tile_swz<KT>(r)) * 16);
+      }
+    }
+    __device__ __forceinline__ void issue_w(Smem &sm, int stage) const {
+      const char *wb = wbase + (long)stage * KT * 2;
+      const uint32_t wl = lds_u32(&sm.w[stage % NSW][0]) + (threadIdx.x >> 6) * 1024;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+      for (int i = 0; i < NCW; ++i) dma16(wb, woff[i], wl + i * 1024 * NWAVES);
+    }
+    __device__ __forceinline__ void issue_x(Smem &sm, int stage) const {
+      const char *xb = xbase + (long)stage * KT * 2;
+      const uint32_t xl = lds_u32(&sm.x[stage % NSX][0]) + (threadIdx.x >> 6) * 1024;
 #pragma unroll
-    for (int i = 0; i < NW; ++i)
-      aoff[i][kk] = tile_frag_off<KT>(tile_a_row<NW, PERM>(wn, i, r16), kk, g);
-#pragma unroll
-    for (int j = 0; j < MW; ++j) boff[j][kk] = tile_frag_off<KT>(wm * 16 * MW + 16 * j + r16, kk, g);
-  }
-  auto compute = [&](int s) {
-    const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
-    const char *xs = reinterpret_cast<const char *>(&sm.x[s % NSX][0]);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 a[NW], b[MW];
-#pragma unroll
-      for (int i = 0; i < NW; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
-#pragma unroll
-      for (int j = 0; j < MW; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
-#pragma unroll
-      for (int i = 0; i < NW; ++i)
-#pragma unroll
-        for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < NCX; ++i)
+        if (TX % NWAVES == 0 || NWAVES * i + (int)(threadIdx.x >> 6) < TX)
+          dma16(xb, xoff[i], xl + i * 1024 * NWAVES);
     }
   };
-  // Issue order: W0, X0, W1 .. W(NSW - 2); then per stage s, after its wait:
-  // X(s + 1), W(s + NSW - 1).  When stage s is waited for, the copies issued
-  // after X(s) are W(1 .. NSW - 2) at s = 0, and W(s + NSW - 2) later (those
-  // that exist); W(s) itself was issued before X(s), except with NSW = 2,
-  // where it follows X(s) and nothing may stay outstanding.
-  ld.issue_w(sm, 0);
-  ld.issue_x(sm, 0);
-#pragma unroll
-  for (int p = 1; p <= NSW - 2; ++p)
-    if (p < nst) ld.issue_w(sm, p);
-  for (int s = 0; s < nst; ++s) {
-    int later = 0;  // W stages allowed to stay in flight
-    if (NSW > 2) later = s == 0 ? min(NSW - 2, nst - 1) : (s + NSW - 2 < nst ? 1 : 0);
-    if (NSW >= 6 && later >= 4) wait_vmcnt<4 * NCW>();
-    else if (NSW >= 5 && later >= 3) wait_vmcnt<3 * NCW>();
-    else if (NSW >= 4 && later >= 2) wait_vmcnt<2 * NCW>();
-    else if (NSW >= 3 && later >= 1) wait_vmcnt<NCW>();
-    else wait_vmcnt<0>();
-    // every wave's copies of stage s are visible after the barrier, and the
-    // buffers refilled next (last read at stage s - 1) are free
-    __syncthreads();
-    if (s + 1 < nst) ld.issue_x(sm, s + 1);
-    if (s + NSW - 1 < nst) ld.issue_w(sm, s + NSW - 1);
-    compute(s);
+
+  // Row (within the workgroup's BN rows) that lane r16 of wave column wn feeds
+  // for tile i.  PERM: inside each pair of tiles, A-operand row 4q + e of tile
+  // 2p + s is feature 32p + 8q + 4s + e of the wave's band.
+  template <bool PERM>
+  __device__ __forceinline__ static int a_row(int wn, int i, int r16) {
+    if (PERM) return wn * 16 * NW + 32 * (i >> 1) + 8 * (r16 >> 2) + 4 * (i & 1) + (r16 & 3);
+    return wn * 16 * NW + 16 * i + r16;
   }
-  __syncthreads();  // every wave is done with the rings: the caller may reuse them
-}
+
+  template <bool PERM>
+  __device__ __forceinline__ static void mainloop(Smem &sm, const Loader &ld, int nst,
+                                                  f32x4 (&acc)[NW][MW]) {
+    constexpr int NKK = KT / 32;
+    static_assert(!PERM || NW % 2 == 0, "permuted rows pair the tiles");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int wn = wave % WN, wm = wave / WN;
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int j = 0; j < MW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nst <= 0) return;
+    int aoff[NW][NKK], boff[MW][NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) aoff[i][kk] = tile_frag_off<KT>(a_row<PERM>(wn, i, r16), kk, g);
+#pragma unroll
+      for (int j = 0; j < MW; ++j)
+        boff[j][kk] = tile_frag_off<KT>(wm * 16 * MW + 16 * j + r16, kk, g);
+    }
+    auto compute = [&](int s) {
+      const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
+      const char *xs = reinterpret_cast<const char *>(&sm.x[s % NSX][0]);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        bf16x8 a[NW], b[MW];
+#pragma unroll
+        for (int i = 0; i < NW; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
+#pragma unroll
+        for (int j = 0; j < MW; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+#pragma unroll
+          for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
+      }
+    };
+    // Issue order: W0, X0, W1 .. W(NSW - 2); then per stage s, after its
+    // wait: X(s + 1), W(s + NSW - 1).  When stage s is waited for, the copies
+    // issued after X(s) are W(1 .. NSW - 2) at s = 0, and W(s + NSW - 2)
+    // later (those that exist); W(s) itself was issued before X(s), except
+    // with NSW = 2, where it follows X(s) and nothing may stay outstanding.
+    ld.issue_w(sm, 0);
+    ld.issue_x(sm, 0);
+#pragma unroll
+    for (int p = 1; p <= NSW - 2; ++p)
+      if (p < nst) ld.issue_w(sm, p);
+    for (int s = 0; s < nst; ++s) {
+      int later = 0;  // W stages allowed to stay in flight
+      if (NSW > 2) later = s == 0 ? min(NSW - 2, nst - 1) : (s + NSW - 2 < nst ? 1 : 0);
+      if (NSW >= 4 && later >= 2) wait_vmcnt<2 * NCW>();
+      else if (NSW >= 3 && later >= 1) wait_vmcnt<NCW>();
+      else wait_vmcnt<0>();
+      // every wave's copies of stage s are visible after the barrier, and the
+      // buffers refilled next (last read at stage s - 1) are free
+      __syncthreads();
+      if (s + 1 < nst) ld.issue_x(sm, s + 1);
+      if (s + NSW - 1 < nst) ld.issue_w(sm, s + NSW - 1);
+      compute(s);
+    }
+    __syncthreads();  // every wave is done with the rings: the caller may reuse them
+  }
+};
 
 // XCD-aware placement: workgroup L runs on XCD L mod 8, which takes every
 // eighth n-block (nn of them).  Within an XCD, slots go in groups of up to
