@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
 constexpr int LDS_KT = 64;
 template <int MW>
 using SmallTile = TileEngine<2, 2, 4, MW, LDS_KT, 3, 2>;
-using BigTile = TileEngine<2, 4, 8, 4, LDS_KT, 2, 2>;
+using BigTile = TileEngine<2, 4, 8, 4, LDS_KT, 3, 2>;
 static_assert(2 * sizeof(SmallTile<4>::Smem) <= 160 * 1024, "two workgroups per CU");
 static_assert(sizeof(BigTile::Smem) <= 160 * 1024, "one workgroup per CU");
 constexpr int BIG_MIN_ROWS = 2048;

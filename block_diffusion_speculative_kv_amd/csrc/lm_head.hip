@@ -37,13 +37,13 @@ namespace dstill {
 
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
 constexpr int HEAD_KT = 64;   // LDS path: k per stage
-// LDS-path tiles (vocabulary ids x rows), 2 x 2 waves, two workgroups per CU:
-// 64 x 32, 64 x 64 and 64 x 160 for up to 160 rows, 128 x 128 beyond.  (A
-// 256 x 256 tile with one workgroup per CU copies half the bytes into LDS
-// but leaves the matrix cores idle during its sampling epilogue, which the
-// second workgroup of a CU otherwise overlaps: no faster at 480 rows.)
+// LDS-path tiles (vocabulary ids x rows): 64 x 32, 64 x 64 and 64 x 160 for
+// up to 160 rows (2 x 2 waves, two workgroups per CU); 256 x 256 beyond (2 x 4
+// waves, one workgroup per CU, the weight three stages ahead in all of LDS),
+// which copies half the bytes into LDS per product term.
 template <int NW, int MW>
 using HeadTile = TileEngine<2, 2, NW, MW, HEAD_KT, 3, 2>;
+using HeadBigTile = TileEngine<2, 4, 8, 4, HEAD_KT, 3, 2>;
 constexpr int NXCD = 8;
 
 // Smallest vocabulary block of any path: sizes the partial-record workspace.
@@ -226,8 +226,8 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
 // LDS-tiled variant (bf16): BN vocabulary ids x BM rows per workgroup on the
 // tile engine E.  Up to 160 rows the tile takes every row (each weight tile
 // has a single reader) and 64 ids, which gives many workgroups, so the last
-// round of a launch is small next to the others.  At batch scale 128 x 128
-// re-uses each staged weight tile across 128 rows.
+// round of a launch is small next to the others.  At batch scale 256 x 256
+// re-uses each staged weight tile across 256 rows.
 template <class E>
 constexpr int head_stage_wave_rows();
 
@@ -533,7 +533,7 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   int BN = 64, BM = 160;
   if (a.rows <= 32) BM = 32;
   else if (a.rows <= 64) BM = 64;
-  else if (a.rows > 160) BN = 128, BM = 128;
+  else if (a.rows > 160) BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
   if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
     a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
@@ -545,7 +545,7 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
     if (BM == 32) launch_head_tile<HeadTile<2, 1>>(a, grid, nmb, st);
     else if (BM == 64) launch_head_tile<HeadTile<2, 2>>(a, grid, nmb, st);
     else if (BM == 160) launch_head_tile<HeadTile<2, 5>>(a, grid, nmb, st);
-    else launch_head_tile<HeadTile<4, 4>>(a, grid, nmb, st);
+    else launch_head_tile<HeadBigTile>(a, grid, nmb, st);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;
     if (a.dtype == 1) launch_rows<bf16>(a, st);
