@@ -227,7 +227,7 @@ def main():
         head_kernel = ("lm_head_stream_kernel" if r <= 16 else
                        "lm_head_lds_kernel (%d ids x %d rows tile)" % (
                            (64, 32) if r <= 32 else (64, 64) if r <= 64
-                           else (64, 160) if r <= 160 else (256, 256)))
+                           else (128, 160) if r <= 160 else (256, 256)))
     head_kernel += " (+lm_combine_kernel)"
     traffic = None
     if args.workload == "q8b_bs32_rs":

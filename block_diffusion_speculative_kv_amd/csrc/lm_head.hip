@@ -37,12 +37,14 @@ namespace dstill {
 
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
 constexpr int HEAD_KT = 64;   // LDS path: k per stage
-// LDS-path tiles (vocabulary ids x rows): 64 x 32, 64 x 64 and 64 x 160 for
-// up to 160 rows (2 x 2 waves, two workgroups per CU); 256 x 256 beyond (2 x 4
-// waves, one workgroup per CU, the weight three stages ahead in all of LDS),
-// which copies half the bytes into LDS per product term.
+// LDS-path tiles (vocabulary ids x rows): 64 x 32 and 64 x 64 up to 64 rows,
+// 128 x 160 up to 160 rows (2 x 2 waves, two workgroups per CU; the 160-row
+// tile with a two-deep weight ring to fit); 256 x 256 beyond (2 x 4 waves, one
+// workgroup per CU, the weight three stages ahead in all of LDS), which
+// copies half the bytes into LDS per product term.
 template <int NW, int MW>
 using HeadTile = TileEngine<2, 2, NW, MW, HEAD_KT, 3, 2>;
+using HeadMidTile = TileEngine<2, 2, 4, 5, HEAD_KT, 2, 2>;
 using HeadBigTile = TileEngine<2, 4, 8, 4, HEAD_KT, 3, 2>;
 constexpr int NXCD = 8;
 
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(256) void lm_head_kernel(HeadArgs a, int nrb) {
 
 // LDS-tiled variant (bf16): BN vocabulary ids x BM rows per workgroup on the
 // tile engine E.  Up to 160 rows the tile takes every row (each weight tile
-// has a single reader) and 64 ids, which gives many workgroups, so the last
-// round of a launch is small next to the others.  At batch scale 256 x 256
+// has a single reader) and 64 or 128 ids, which gives many workgroups, so the
+// last round of a launch is small next to the others.  At batch scale 256 x 256
 // re-uses each staged weight tile across 256 rows.
 template <class E>
 constexpr int head_stage_wave_rows();
@@ -530,9 +532,9 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   // up to 16 rows stream the weight in 512-byte row slices; more rows go
   // through the tile engine, with a tile fitted to the row count (the LDS
   // kernel addresses a block's hidden rows with 32-bit byte offsets)
-  int BN = 64, BM = 160;
-  if (a.rows <= 32) BM = 32;
-  else if (a.rows <= 64) BM = 64;
+  int BN = HeadMidTile::BN, BM = HeadMidTile::BM;
+  if (a.rows <= 32) BN = 64, BM = 32;
+  else if (a.rows <= 64) BN = 64, BM = 64;
   else if (a.rows > 160) BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
   if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
@@ -544,7 +546,7 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
     const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nmb);
     if (BM == 32) launch_head_tile<HeadTile<2, 1>>(a, grid, nmb, st);
     else if (BM == 64) launch_head_tile<HeadTile<2, 2>>(a, grid, nmb, st);
-    else if (BM == 160) launch_head_tile<HeadTile<2, 5>>(a, grid, nmb, st);
+    else if (BM == 160) launch_head_tile<HeadMidTile>(a, grid, nmb, st);
     else launch_head_tile<HeadBigTile>(a, grid, nmb, st);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;

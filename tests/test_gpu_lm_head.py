@@ -11,11 +11,11 @@ these inputs is ~1e-4 absolute; the near-tie count is reported.
 
 Shapes: the tiny fp32 workload (V 1024, d 256, gamma 7 rows), ragged bf16
 cases (V 5003, d 512, rows in blocks of 15 with a stride of 16) at 11, 30,
-37 and 45 rows (one case per kernel row band: <= 16, <= 32, <= 64), and the
-full 8B-shaped head (V 151936, d 4096) at the row counts of the greedy bs-1
-(15 rows, argmax), bs-4 (60 rows), bs-32 rejection-sampling (480 rows,
-Gumbel, logits stored; sampled rows checked) and multi-copy (144 rows,
-shared Gumbel) workloads.
+37, 45, 100 and 300 rows (one case per kernel row band: <= 16, <= 32, <= 64,
+<= 160, two row blocks of the largest tile), and the full 8B-shaped head (V
+151936, d 4096) at the row counts of the greedy bs-1 (15 rows, argmax), bs-4
+(60 rows), bs-32 rejection-sampling (480 rows, Gumbel, logits stored; sampled
+rows checked) and multi-copy (144 rows, shared Gumbel) workloads.
 """
 
 import numpy as np
@@ -126,6 +126,16 @@ def test_ragged_bf16_gumbel_up_to_32_rows():
 def test_ragged_bf16_stream_up_to_16_rows():
     # <= 16 rows: the weight-streaming kernel, with a partial last vocabulary block
     _run_case(5003, 512, "bf16", 11, 11, 16, bd.HEAD_GUMBEL, T=1.3, keep_logits=True)
+
+
+def test_ragged_bf16_gumbel_up_to_160_rows():
+    # 65..160 rows: the 128 x 160 tile, partial last vocabulary block
+    _run_case(5003, 512, "bf16", 100, 15, 16, bd.HEAD_GUMBEL, T=0.9, keep_logits=True)
+
+
+def test_ragged_bf16_argmax_two_row_blocks():
+    # > 160 rows: the 256 x 256 tile over two row blocks (the second partial)
+    _run_case(5003, 512, "bf16", 300, 15, 16, bd.HEAD_ARGMAX, keep_logits=True)
 
 
 def test_q8b_bs4_rows():
