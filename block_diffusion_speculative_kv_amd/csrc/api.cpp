@@ -89,18 +89,25 @@ size_t gemm_parts_floats(const dstill_config &c, int M, int ncu) {
 struct AttnPlan {
   int split, nsplit;
 };
-AttnPlan attn_plan(int max_ctx, int pairs) {
-  // about 1536 splits of the longest context over all (sequence, kv head)
-  // pairs: ~3 rounds of two workgroups per compute unit, long enough that
-  // each workgroup's start and end costs are small next to its streaming
-  const long want = ((long)max_ctx * pairs + 1535) / 1536;
+// Split of the context keys among attention workgroups, which run two per
+// compute unit (slots = 2 ncu).  With ns splits of max_ctx keys per (sequence,
+// kv head) pair there are ns * pairs workgroups, and ns = slots / pairs fills
+// one round exactly.  When that leaves fewer than four splits per pair (many
+// pairs), contexts of different lengths leave one round unbalanced, so ns is
+// taken 1.5 times larger and the longest-first work list evens it out.  (On
+// the 8B-shaped drafter this beat fixed split lengths: one round for 32 pairs
+// of 32K keys and for 72 pairs of 4K, 1.5 rounds for 256 pairs of 1K-8K.)
+AttnPlan attn_plan(int max_ctx, int pairs, int ncu) {
+  const long slots = 2L * ncu;
+  long ns = std::max<long>(1, slots / pairs);
+  if (ns < 4) ns = std::max<long>(1, 3 * slots / (2 * pairs));
+  long split = ((long)max_ctx + ns - 1) / ns;
   // at most 128 splits (the merge kernel stages one weight per split)
   const long floor_split = std::max<long>(128, ((long)max_ctx + 127) / 128);
-  int split = (int)std::max<long>(floor_split, (want + 63) / 64 * 64);
-  split = (split + 63) / 64 * 64;
+  split = (std::max(split, floor_split) + 63) / 64 * 64;
   AttnPlan p;
-  p.split = split;
-  p.nsplit = std::max(1, (max_ctx + split - 1) / split);
+  p.split = (int)split;
+  p.nsplit = std::max(1, (int)(((long)max_ctx + split - 1) / split));
   return p;
 }
 
@@ -253,11 +260,13 @@ int dstill_workspace_bytes(const dstill_handle *h, const dstill_limits *lim, siz
   const int B = c.max_block;
   for (int bs = 1; bs <= lim->max_batch; ++bs)
     for (int C = 1; C <= std::max(1, lim->max_copies); ++C) {
-      const AttnPlan ap = attn_plan(std::max(1, lim->max_ctx), bs * C * c.n_kv_heads);
-      // a call with a smaller max_ctx plans more, shorter splits: bound the count
+      const int pairs = bs * C * c.n_kv_heads;
+      const AttnPlan ap = attn_plan(std::max(1, lim->max_ctx), pairs, ncu);
+      // a call with a smaller max_ctx may plan more, shorter splits (never
+      // more than 3 ncu / pairs + 1): bound the count
       AttnPlan bound = ap;
       bound.nsplit = std::max(ap.nsplit, std::min((std::max(1, lim->max_ctx) + 127) / 128,
-                                                  2048 / (bs * C * c.n_kv_heads) + 2));
+                                                  3 * ncu / pairs + 2));
       best = std::max(best, draft_ws(c, bs, C, B, bound, ncu, nullptr, nullptr));
       // fewer rows per block give other k-split choices
       for (int b2 = 1; b2 < B; ++b2)
@@ -334,7 +343,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
   if (!ws) return fail(DSTILL_EINVAL, "ws is null");
   const int ncu = num_cu();
   const int ctx_limit = std::min(max_ctx, kv->cap);
-  const AttnPlan ap = attn_plan(std::max(1, ctx_limit), bs * n_copies * c.n_kv_heads);
+  const AttnPlan ap = attn_plan(std::max(1, ctx_limit), bs * n_copies * c.n_kv_heads, ncu);
   const size_t need = draft_ws(c, bs, n_copies, block, ap, ncu, nullptr, nullptr);
   if (ws_bytes < need) return fail(DSTILL_EWORKSPACE, "block_draft needs %zu workspace bytes", need);
   DraftWs w;
