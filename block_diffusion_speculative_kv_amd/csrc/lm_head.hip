@@ -340,97 +340,104 @@ constexpr int head_stage_wave_rows() {
 }
 
 // Weight-streaming variant for up to 16 rows (bf16, one row tile): the
-// weight tile of 128 vocabulary rows streams through a two-stage LDS ring in
-// k-stages of 256 (512 contiguous bytes of every row per stage, 64 KB),
-// filled by direct global->LDS copies one stage ahead; the hidden row
-// fragments of the next stage are loaded into the other of two register sets
-// meanwhile.  LDS rows are unpadded and XOR-swizzled per 16-byte chunk, so
-// the 16 rows one fragment read touches (in the permuted vocabulary order)
-// fall on distinct banks.
-constexpr int HS_K = 256;       // k per stage
+// weight tile of 128 vocabulary rows streams through a ring of HS_NS LDS
+// stages of k = 128 (256 contiguous bytes of every row, 32 KB), filled by
+// direct global->LDS copies HS_NS - 1 stages ahead, so about 96 KB per
+// compute unit stay in flight however short each stage's multiply.  The 16
+// hidden rows' slice of the stage (4 KB) rides in the same ring.  LDS rows
+// are unpadded and XOR-swizzled per 16-byte chunk, so the 16 rows one
+// fragment read touches (in the permuted vocabulary order) fall on distinct
+// banks.
+constexpr int HS_K = 128;       // k per stage
+constexpr int HS_NS = 4;        // ring stages
 constexpr int HS_ROWS = 128;    // vocabulary rows per workgroup (32 per wave)
-constexpr int HS_COPIES = HS_ROWS * HS_K * 2 / 1024 / 4;  // direct copies per wave per stage
+constexpr int HS_WC = HS_ROWS * HS_K * 2 / 1024 / 4;  // weight copies per wave per stage
+constexpr int HS_OPS = HS_WC + 1;                      // + one hidden-slice copy
+
+struct HsStage {
+  bf16 w[HS_ROWS * HS_K];
+  bf16 x[16 * HS_K];
+};
 
 __device__ __forceinline__ int hs_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
 
 __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a) {
-  __shared__ bf16 wsm[2][HS_ROWS * HS_K];
+  __shared__ HsStage ring[HS_NS];
   const int vb = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int V = a.vocab, d = a.d;
   const int v0 = vb * HS_ROWS;
   const char *wblk = reinterpret_cast<const char *>((const bf16 *)a.w + (long)v0 * d);
-  // copy j of wave w fills LDS vectors 64 (4 j + w) + lane: tile row
-  // 2 (4 j + w) + lane / 32, physical chunk lane % 32
-  uint32_t goff[HS_COPIES];
+  const char *xblk = reinterpret_cast<const char *>(a.hidden);
+  // weight copy j of wave w fills LDS vectors 64 (4 j + w) + lane: tile row
+  // 4 (4 j + w) + lane / 16, physical chunk lane % 16; the hidden copy of
+  // wave w fills rows 4 w + lane / 16 of the stage's 16 x 128 slice
+  uint32_t goff[HS_WC];
 #pragma unroll
-  for (int j = 0; j < HS_COPIES; ++j) {
-    const int row = 2 * (4 * j + wave) + (lane >> 5), pc = lane & 31;
+  for (int j = 0; j < HS_WC; ++j) {
+    const int row = 4 * (4 * j + wave) + (lane >> 4), pc = lane & 15;
     goff[j] = (uint32_t)((min(v0 + row, V - 1) - v0) * d * 2 + 16 * (pc ^ hs_swz(row)));
+  }
+  uint32_t xoff;
+  {
+    const int row = 4 * wave + (lane >> 4), pc = lane & 15;
+    const int r = min(row, a.rows - 1);
+    const long hr = (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq;
+    xoff = (uint32_t)(hr * d * 2 + 16 * (pc ^ row));
   }
   // A-operand rows of this wave's tile pair (permuted vocabulary order)
   int arow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) arow[t] = 32 * wave + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-  const int r = min(r16, a.rows - 1);
-  const bf16 *xp = (const bf16 *)a.hidden +
-                   ((long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq) * d + 8 * g;
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const int nst = d / HS_K;
   // each block starts its k walk at a different stage, so concurrent blocks
   // do not sweep the same column offset of their rows at the same time
   const int rot = (vb * 5) % nst;
   auto kst = [&](int s) { return s + rot < nst ? s + rot : s + rot - nst; };
-  auto issue = [&](int s, int buf) {
-    const char *src = wblk + (long)kst(s) * HS_K * 2;
-    const uint32_t l = lds_u32(&wsm[buf][0]) + wave * 1024;
+  auto issue = [&](int s) {
+    const long k0 = (long)kst(s) * HS_K * 2;
+    HsStage &st = ring[s % HS_NS];
+    const uint32_t wl = lds_u32(&st.w[0]) + wave * 1024;
 #pragma unroll
-    for (int j = 0; j < HS_COPIES; ++j) dma16(src, goff[j], l + j * 4096);
+    for (int j = 0; j < HS_WC; ++j) dma16(wblk + k0, goff[j], wl + j * 4096);
+    dma16(xblk + k0, xoff, lds_u32(&st.x[0]) + wave * 1024);
   };
-  auto xload = [&](int s, bf16x8 (&xf)[HS_K / 32]) {
-#pragma unroll
-    for (int kk = 0; kk < HS_K / 32; ++kk)
-      xf[kk] = *reinterpret_cast<const bf16x8 *>(xp + (long)kst(s) * HS_K + kk * 32);
-  };
-  auto compute = [&](int buf, const bf16x8 (&xf)[HS_K / 32]) {
-    const bf16 *ws = wsm[buf];
+  auto compute = [&](const HsStage &st) {
+    const char *ws = reinterpret_cast<const char *>(&st.w[0]);
+    const char *xs = reinterpret_cast<const char *>(&st.x[0]);
 #pragma unroll
     for (int kk = 0; kk < HS_K / 32; ++kk) {
+      const bf16x8 xf =
+          *reinterpret_cast<const bf16x8 *>(xs + r16 * HS_K * 2 + 16 * ((kk * 4 + g) ^ r16));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
-            ws + arow[t] * HS_K + 8 * ((kk * 4 + g) ^ hs_swz(arow[t])));
-        acc[t] = Mma<bf16>::run(fa, xf[kk], acc[t]);
+            ws + arow[t] * HS_K * 2 + 16 * ((kk * 4 + g) ^ hs_swz(arow[t])));
+        acc[t] = Mma<bf16>::run(fa, xf, acc[t]);
       }
     }
   };
-  bf16x8 xa[HS_K / 32], xb[HS_K / 32];
-  issue(0, 0);
-  xload(0, xa);
-  wait_vmcnt<0>();
-  __syncthreads();
-  // stage s is multiplied out of buffer s & 1 with register set (s & 1 ? xb
-  // : xa) while stage s + 1 is copied into the other buffer and set
-  for (int s = 0; s < nst; s += 2) {
-    if (s + 1 < nst) {
-      issue(s + 1, 1);
-      xload(s + 1, xb);
-    }
-    compute(0, xa);
-    wait_vmcnt<0>();
+#pragma unroll
+  for (int p = 0; p < HS_NS - 1; ++p)
+    if (p < nst) issue(p);
+  for (int s = 0; s < nst; ++s) {
+    // stage s has landed once at most the copies of the stages after it (up
+    // to HS_NS - 2 of them) are outstanding
+    const int ahead = min(nst - 1 - s, HS_NS - 2);
+    if (ahead >= 2) wait_vmcnt<2 * HS_OPS>();
+    else if (ahead == 1) wait_vmcnt<HS_OPS>();
+    else wait_vmcnt<0>();
+    // every wave's copies of stage s are visible, and the buffer refilled
+    // next (read at stage s - 1) is free
     __syncthreads();
-    if (s + 1 >= nst) break;
-    if (s + 2 < nst) {
-      issue(s + 2, 0);
-      xload(s + 2, xa);
-    }
-    compute(1, xb);
-    wait_vmcnt<0>();
-    __syncthreads();
+    if (s + HS_NS - 1 < nst) issue(s + HS_NS - 1);
+    compute(ring[s % HS_NS]);
   }
+  __syncthreads();
   // epilogue: per row, the wave's 32 ids, then the four waves in LDS
-  RowStat(*red)[16] = reinterpret_cast<RowStat(*)[16]>(&wsm[0][0]);
+  RowStat(*red)[16] = reinterpret_cast<RowStat(*)[16]>(&ring[0]);
   const int vw = v0 + 32 * wave;
   float zz[1][8];
 #pragma unroll
