@@ -454,62 +454,84 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a) {
   }
 }
 
-// One wave per row merges the row's vocabulary-block records.
-__global__ __launch_bounds__(64) void lm_combine_kernel(HeadArgs a) {
-  const int r = blockIdx.x, lane = threadIdx.x;
+// One workgroup per row merges the row's vocabulary-block records in two
+// passes over them: the top-2 / zmax / largest block maximum M, then the
+// fp64 sum of s_i exp(m_i - M) (one exponential per record, no dependent
+// chain).  Each thread takes records tid, tid + COMB_T, ... in order, then
+// the waves reduce by a fixed butterfly and the four wave results merge in
+// wave order: deterministic.
+constexpr int COMB_T = 256;
+
+__device__ __forceinline__ void arg_merge(ArgTop2 &arg, float &zbest, const ArgTop2 &o, float zb) {
+  const bool bw = o.best > arg.best || (o.best == arg.best && o.idx < arg.idx);
+  if (bw) zbest = zb;
+  arg = top2_merge(arg, o);
+}
+
+__global__ __launch_bounds__(COMB_T) void lm_combine_kernel(HeadArgs a) {
+  constexpr int NWV = COMB_T / 64;
+  __shared__ ArgTop2 s_arg[NWV];
+  __shared__ float s_zb[NWV], s_zmax[NWV], s_m[NWV];
+  __shared__ double s_s[NWV];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const HeadPartial *p = a.part + (long)r * a.nvb;
   ArgTop2 arg;
   arg.best = -INFINITY;
   arg.second = -INFINITY;
   arg.idx = 0x7fffffff;
   float zbest = 0.f, zmax = -INFINITY, m = -INFINITY;
-  double s = 0.0;
-  const HeadPartial *p = a.part + (long)r * a.nvb;
-  for (int i = lane; i < a.nvb; i += WAVE) {
+  for (int i = tid; i < a.nvb; i += COMB_T) {
     const HeadPartial h = p[i];
     ArgTop2 o;
     o.best = h.best;
     o.second = h.second;
     o.idx = h.idx;
-    const bool bw = o.best > arg.best || (o.best == arg.best && o.idx < arg.idx);
-    if (bw) zbest = h.zbest;
-    arg = top2_merge(arg, o);
+    arg_merge(arg, zbest, o, h.zbest);
     zmax = fmaxf(zmax, h.zmax);
-    if (h.m != -INFINITY) {
-      if (m == -INFINITY) { m = h.m; s = h.s; }
-      else {
-        const float M = fmaxf(m, h.m);
-        s = s * exp((double)m - M) + (double)h.s * exp((double)h.m - M);
-        m = M;
-      }
-    }
+    m = fmaxf(m, h.m);
   }
   for (int o = 32; o > 0; o >>= 1) {
     ArgTop2 b;
     b.best = __shfl_xor(arg.best, o, WAVE);
     b.second = __shfl_xor(arg.second, o, WAVE);
     b.idx = __shfl_xor(arg.idx, o, WAVE);
-    const float zb2 = __shfl_xor(zbest, o, WAVE);
-    const bool bw = b.best > arg.best || (b.best == arg.best && b.idx < arg.idx);
-    if (bw) zbest = zb2;
-    arg = top2_merge(arg, b);
+    arg_merge(arg, zbest, b, __shfl_xor(zbest, o, WAVE));
     zmax = fmaxf(zmax, __shfl_xor(zmax, o, WAVE));
-    const float m2 = __shfl_xor(m, o, WAVE);
-    const double s2 = __shfl_xor(s, o, WAVE);
-    if (m2 != -INFINITY) {
-      if (m == -INFINITY) { m = m2; s = s2; }
-      else {
-        const float M = fmaxf(m, m2);
-        s = s * exp((double)m - M) + s2 * exp((double)m2 - M);
-        m = M;
-      }
-    }
+    m = fmaxf(m, __shfl_xor(m, o, WAVE));
   }
   if (lane == 0) {
-    a.ids[r] = arg.idx;
-    if (a.zmax) a.zmax[r] = zmax;
-    if (a.lse) a.lse[r] = (float)((double)m + log(s));
-    if (a.zsel) a.zsel[r] = zbest;
-    if (a.gap) a.gap[r] = arg.best - arg.second;
+    s_arg[wave] = arg;
+    s_zb[wave] = zbest;
+    s_zmax[wave] = zmax;
+    s_m[wave] = m;
+  }
+  __syncthreads();
+  float M = s_m[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_m[w]);
+  double s = 0.0;
+  if (M != -INFINITY)
+    for (int i = tid; i < a.nvb; i += COMB_T) {
+      const float mi = p[i].m, si = p[i].s;
+      if (mi != -INFINITY) s += (double)si * exp((double)mi - (double)M);
+    }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, WAVE);
+  if (lane == 0) s_s[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    ArgTop2 g = s_arg[0];
+    float zb = s_zb[0], zm = s_zmax[0];
+    double S = s_s[0];
+    for (int w = 1; w < NWV; ++w) {
+      arg_merge(g, zb, s_arg[w], s_zb[w]);
+      zm = fmaxf(zm, s_zmax[w]);
+      S += s_s[w];
+    }
+    a.ids[r] = g.idx;
+    if (a.zmax) a.zmax[r] = zm;
+    if (a.lse) a.lse[r] = (float)((double)M + log(S));
+    if (a.zsel) a.zsel[r] = zb;
+    if (a.gap) a.gap[r] = g.best - g.second;
   }
 }
 
@@ -560,7 +582,7 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
     if (a.dtype == 1) launch_rows<bf16>(a, st);
     else launch_rows<float>(a, st);
   }
-  hipLaunchKernelGGL(lm_combine_kernel, dim3(a.rows), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(lm_combine_kernel, dim3(a.rows), dim3(COMB_T), 0, st, a);
 }
 
 }  // namespace dstill
