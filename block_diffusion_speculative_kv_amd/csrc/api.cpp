@@ -77,7 +77,9 @@ size_t gemm_parts_floats(const dstill_config &c, int M, int ncu) {
                                  {2 * c.mlp, d},
                                  {d, c.mlp},
                                  {d, F},
-                                 {2 * c.n_kv_heads * c.head_dim, d}};
+                                 {2 * c.n_kv_heads * c.head_dim, d},
+                                 {2 * c.n_kv_heads * c.head_dim *
+                                      std::min(c.n_layers, (int32_t)GEMM_MAX_GROUPS), d}};
   size_t best = 0;
   for (const P &p : ps) {
     const int s = gemm_plan_splits(M, p.N, p.K, c.dtype, ncu);
@@ -310,18 +312,32 @@ int dstill_inject_kv(const dstill_handle *h, const void *feats, const int32_t *s
   launch_gemm(g, st);
   launch_norm_rows(c.dtype, w.parts, g.splits, n, d, nullptr, 0, h->w.g_fuse, c.rms_eps, w.ht, d,
                    w.xtmp, w.ssp, st);
-  for (int l = 0; l < c.n_layers; ++l) {
-    const dstill_layer_weights &L = h->layers[l];
+  // K/V rows of the draft layers: with bf16 weights one product covers up to
+  // GEMM_MAX_GROUPS layers (each layer's W^K|W^V rows are one weight group)
+  // and one pass scatters all of them; otherwise one product per layer
+  const int per = gemm_can_group(d, c.dtype) && (2 * kvd) % 256 == 0 ? GEMM_MAX_GROUPS : 1;
+  for (int l0 = 0; l0 < c.n_layers; l0 += per) {
+    const int nl = std::min(per, c.n_layers - l0);
     GemmArgs k;
     k.dtype = c.dtype;
     k.X = w.ht; k.ldx = d;
-    k.W = (const char *)L.wqkv + (size_t)qd * d * eb;  // rows W^K then W^V
-    k.ldw = d; k.out = w.parts; k.M = n; k.N = 2 * kvd; k.K = d;
-    k.splits = gemm_plan_splits(n, 2 * kvd, d, c.dtype, ncu);
+    k.ldw = d; k.out = w.parts; k.M = n; k.N = 2 * kvd * nl; k.K = d;
+    InjectLayers il;
+    il.layers = nl;
+    for (int i = 0; i < nl; ++i) {
+      const dstill_layer_weights &L = h->layers[l0 + i];
+      const void *wkv = (const char *)L.wqkv + (size_t)qd * d * eb;  // rows W^K then W^V
+      if (per > 1) k.wg[i] = wkv;
+      else k.W = wkv;
+      il.k_norm[i] = L.k_norm;
+      il.kc[i] = kv->k[l0 + i];
+      il.vc[i] = kv->v[l0 + i];
+    }
+    if (per > 1) k.wg_rows = 2 * kvd;
+    k.splits = gemm_plan_splits(n, k.N, d, c.dtype, ncu);
     launch_gemm(k, st);
-    launch_inject_post(c.dtype, w.parts, k.splits, n, c.n_kv_heads, c.head_dim, seq_id, pos,
-                       L.k_norm, c.qk_norm, c.rms_eps, w.rope, kv->k[l], kv->v[l],
-                       kv->max_batch, kv->cap, st);
+    launch_inject_post(c.dtype, w.parts, k.splits, n, c.n_kv_heads, c.head_dim, seq_id, pos, il,
+                       c.qk_norm, c.rms_eps, w.rope, kv->max_batch, kv->cap, st);
   }
   return hip_check("inject_kv launch");
 }

@@ -90,6 +90,11 @@ constexpr int stage_wave_rows() {
   return w;
 }
 
+struct WGroups {
+  const bf16 *p[GEMM_MAX_GROUPS];
+  int rows;
+};
+
 // act != nullptr selects the fused SwiGLU epilogue (one split): n-block nb
 // covers features f0 = (BN / 2) nb .. f0 + BN / 2 - 1.  With wave bands of
 // WB = 16 NW weight rows, tile row r (band r / WB, in-band row q = r % WB) is
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(E::NT) void gemm_lds_partial(const bf16 *__restrict
                                                           float *__restrict__ out, int M, int N,
                                                           int nst, int st_per_split, int nnb,
                                                           int nmb, bf16 *__restrict__ act,
-                                                          int mlp) {
+                                                          int mlp, WGroups wgr) {
   constexpr int NW = E::NW, MW = E::MW, BN = E::BN, BM = E::BM;
   constexpr int WB = 16 * NW, HB = WB / 2;
   __shared__ typename E::Smem sm;
@@ -123,6 +128,9 @@ __global__ __launch_bounds__(E::NT) void gemm_lds_partial(const bf16 *__restrict
               return ((q >= HB ? mlp : 0) + HB * (r / WB) + q % HB) * (int)ldw;
             },
             X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
+  else if (wgr.rows > 0)  // whole tiles inside one group
+    ld.init(wgr.p[n0 / wgr.rows] + (long)(n0 % wgr.rows) * ldw,
+            [&](int r) { return r * (int)ldw; }, X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
   else
     ld.init(W + (long)n0 * ldw, [&](int r) { return (min(n0 + r, N - 1) - n0) * (int)ldw; },
             X + (long)m0 * ldx, xrow, (long)s0 * LDS_KT);
@@ -192,6 +200,7 @@ __global__ __launch_bounds__(E::NT) void gemm_lds_partial(const bf16 *__restrict
 // path (its direct-copy rings stream the weight faster than register loads
 // at any row count); fp32 and other depths take gemm_nt_partial
 static bool use_lds(int K, int dtype) { return dtype == 1 && K % LDS_KT == 0; }
+bool gemm_can_group(int K, int dtype) { return use_lds(K, dtype); }
 
 struct LdsPlan {
   bool big;
@@ -294,9 +303,12 @@ template <class E>
 static void launch_lds(const GemmArgs &a, int nnb, int nmb, int per, int splits, bf16 *act,
                        hipStream_t st) {
   const dim3 grid((nnb + 7) / 8 * 8 * nmb, splits);
+  WGroups wgr;
+  for (int g = 0; g < GEMM_MAX_GROUPS; ++g) wgr.p[g] = (const bf16 *)a.wg[g];
+  wgr.rows = a.wg_rows;
   hipLaunchKernelGGL((gemm_lds_partial<E>), grid, dim3(E::NT), 0, st, (const bf16 *)a.X, a.ldx,
                      (const bf16 *)a.W, a.ldw, a.out, a.M, a.N, a.K / LDS_KT, per, nnb, nmb, act,
-                     a.mlp);
+                     a.mlp, wgr);
 }
 
 void launch_gemm(const GemmArgs &a, hipStream_t st) {

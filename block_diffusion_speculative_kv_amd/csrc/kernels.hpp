@@ -9,6 +9,7 @@
 namespace dstill {
 
 // ---- dense projections (gemm.hip) -----------------------------------------
+constexpr int GEMM_MAX_GROUPS = 8;
 struct GemmArgs {
   const void *X;  // [M, K] activations, row stride ldx (elements)
   long ldx;
@@ -21,7 +22,15 @@ struct GemmArgs {
   // as act[M][mlp] = bf16(silu(gate) * up) instead of partial sums.
   void *swiglu_act = nullptr;
   int mlp = 0;
+  // Weight groups (bf16 LDS path only): when wg_rows > 0, output rows
+  // [g wg_rows, (g + 1) wg_rows) of W are rows 0 .. wg_rows - 1 of wg[g]
+  // (N = groups x wg_rows, wg_rows a multiple of 256), so one launch covers
+  // row blocks of several weight tensors.  W is ignored.
+  const void *wg[GEMM_MAX_GROUPS] = {};
+  int wg_rows = 0;
 };
+// Whether a product can take weight groups (bf16 with depth a multiple of 64).
+bool gemm_can_group(int K, int dtype);
 // Whether a gate|up product of these sizes takes the fused SwiGLU epilogue:
 // bf16, mlp a multiple of 64, and one split already gives every compute unit
 // a workgroup (the fusion saves the partial plane and the separate pass).
@@ -52,9 +61,16 @@ void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, i
                      void *kb, void *vb, hipStream_t st);
 void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, void *act,
                    hipStream_t st);
+// K/V of `layers` draft layers from one partial-plane set: plane columns
+// [l * 2 kvd, (l + 1) * 2 kvd) hold layer l's K then V rows (kvd = hkv dh).
+struct InjectLayers {
+  const void *k_norm[GEMM_MAX_GROUPS];
+  void *kc[GEMM_MAX_GROUPS], *vc[GEMM_MAX_GROUPS];
+  int layers;
+};
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
-                        const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
-                        float eps, const float *rope, void *kc, void *vc, int max_batch, int cap,
+                        const int32_t *seq, const int32_t *pos, const InjectLayers &il,
+                        int qk_norm, float eps, const float *rope, int max_batch, int cap,
                         hipStream_t st);
 
 // ---- block attention over injected context (attn.hip) --------------------

@@ -300,33 +300,37 @@ void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, vo
 template <typename T>
 __global__ __launch_bounds__(64) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
-    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos,
-    const T *__restrict__ k_norm, int qk_norm, float eps, const float2 *__restrict__ rope,
-    T *__restrict__ kc, T *__restrict__ vc, int max_batch, int cap) {
-  const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
+    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
+    int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap) {
+  const int r = blockIdx.x, head = blockIdx.y, layer = blockIdx.z, lane = threadIdx.x;
   const int sq = seq[r], ps = pos[r];
   if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
-  const int half = dh / 2, ncol = 2 * hkv * dh;
+  const int half = dh / 2, ncol = 2 * hkv * dh, width = il.layers * ncol;
   const bool is_k = head < hkv;
   const int h = is_k ? head : head - hkv;
+  // all loads of the split planes first (they are independent), then the sums
+  // in split order
   float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
     if (p < half) {
-      const float *src = parts + (long)r * ncol + head * dh + p;
+      const float *src = parts + (long)r * width + layer * ncol + head * dh + p;
       for (int s = 0; s < nsplit; ++s) {
-        x1[i] += src[(long)s * n * ncol];
-        x2[i] += src[(long)s * n * ncol + half];
+        x1[i] += src[(long)s * n * width];
+        x2[i] += src[(long)s * n * width + half];
       }
     }
   }
   // K cache rows are dh-vectors [cap][dh]; the V cache is stored in tiles of
   // 64 keys, d-major inside a tile: [cap/64][dh][64]
+  T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
   const long stride = is_k ? 1 : 64;
   T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
                 : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
-  if (is_k) head_norm_rope<T>(x1, x2, dh, qk_norm != 0, k_norm, eps, rope + (long)r * half);
+  if (is_k)
+    head_norm_rope<T>(x1, x2, dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
+                      rope + (long)r * half);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
@@ -338,19 +342,17 @@ __global__ __launch_bounds__(64) void inject_post_kernel(
 }
 
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
-                        const int32_t *seq, const int32_t *pos, const void *k_norm, int qk_norm,
-                        float eps, const float *rope, void *kc, void *vc, int max_batch, int cap,
+                        const int32_t *seq, const int32_t *pos, const InjectLayers &il,
+                        int qk_norm, float eps, const float *rope, int max_batch, int cap,
                         hipStream_t st) {
-  if (n == 0) return;
-  dim3 grid(n, 2 * hkv);
+  if (n == 0 || il.layers == 0) return;
+  dim3 grid(n, 2 * hkv, il.layers);
   if (dtype == 1)
     hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, (const bf16 *)k_norm, qk_norm, eps, (const float2 *)rope,
-                       (bf16 *)kc, (bf16 *)vc, max_batch, cap);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
   else
     hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, (const float *)k_norm, qk_norm, eps, (const float2 *)rope,
-                       (float *)kc, (float *)vc, max_batch, cap);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
 }
 
 }  // namespace dstill

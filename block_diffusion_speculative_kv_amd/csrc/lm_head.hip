@@ -250,7 +250,7 @@ __global__ __launch_bounds__(E::NT) void lm_head_lds_kernel(HeadArgs a, int nmb)
   ld.init(W + (long)v0 * d, [&](int i) { return (min(v0 + i, V - 1) - v0) * d; },
           H + (long)h0 * d, [&](int i) { return (hrow(min(r0 + i, a.rows - 1)) - h0) * d; }, 0);
   f32x4 acc[NW][MW];
-  E::template mainloop<true>(sm, ld, d / HEAD_KT, acc);
+  E::template mainloop<true>(sm, ld, d / E::KT, acc);
 
   // The main loop ended with a barrier: its LDS is free.  The first RED bytes
   // take the per-wave row records; stored logits are staged behind them as

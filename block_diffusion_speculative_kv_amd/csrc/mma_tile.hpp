@@ -71,7 +71,8 @@ struct TileEngine {
   static constexpr int TW = BN / RPI, TX = BM / RPI;
   static constexpr int NCW = TW / NWAVES, NCX = (TX + NWAVES - 1) / NWAVES;
   static_assert(KT == 64 || KT == 32, "stage depth");
-  static_assert(NSX == 2 && NSW >= 2 && NSW <= 4, "ring depths");
+  static_assert(NSX == 2 && NSW >= 2 && NSW <= 8, "ring depths");
+  static_assert(NCW * (NSW > 2 ? NSW - 2 : 0) < 64, "vmcnt holds the copies left in flight");
   static_assert(TW * RPI == BN && TX * RPI == BM && NCW * NWAVES == TW, "whole copies");
 
   struct Smem {
@@ -157,20 +158,41 @@ struct TileEngine {
       for (int j = 0; j < MW; ++j)
         boff[j][kk] = tile_frag_off<KT>(wm * 16 * MW + 16 * j + r16, kk, g);
     }
+    // Fragments of both k-steps of a stage live in separate registers: the
+    // first k-step's reads are issued together, the second k-step's reads are
+    // interleaved with the first k-step's multiplies, and the second k-step's
+    // multiplies follow, so the matrix pipe waits for LDS once per stage
+    // rather than before every few products.
     auto compute = [&](int s) {
       const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
       const char *xs = reinterpret_cast<const char *>(&sm.x[s % NSX][0]);
+      bf16x8 a[NKK][NW], b[NKK][MW];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        bf16x8 a[NW], b[MW];
 #pragma unroll
-        for (int i = 0; i < NW; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
+        for (int i = 0; i < NW; ++i) a[kk][i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
 #pragma unroll
-        for (int j = 0; j < MW; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
+        for (int j = 0; j < MW; ++j) b[kk][j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int i = 0; i < NW; ++i)
 #pragma unroll
-          for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[kk][i], b[kk][j], acc[i][j]);
+      // schedule: reads of k-step 0, then (one read of k-step 1, RATIO
+      // products of k-step 0) while both last, then the remaining products
+      constexpr int NF = NW + MW, NP = NW * MW;
+      if constexpr (NKK == 2) {
+        constexpr int RATIO = NP / NF > 0 ? NP / NF : 1;
+        constexpr int INTER = NF * RATIO <= NP ? NF : NP / RATIO;
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+        static_for<INTER>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, RATIO, 0);
+        });
+        if constexpr (NF > INTER) __builtin_amdgcn_sched_group_barrier(0x100, NF - INTER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NP - INTER * RATIO, 0);
       }
     };
     // Issue order: W0, X0, W1 .. W(NSW - 2); then per stage s, after its
@@ -186,9 +208,17 @@ struct TileEngine {
     for (int s = 0; s < nst; ++s) {
       int later = 0;  // W stages allowed to stay in flight
       if (NSW > 2) later = s == 0 ? min(NSW - 2, nst - 1) : (s + NSW - 2 < nst ? 1 : 0);
-      if (NSW >= 4 && later >= 2) wait_vmcnt<2 * NCW>();
-      else if (NSW >= 3 && later >= 1) wait_vmcnt<NCW>();
-      else wait_vmcnt<0>();
+      if (later == 0) {
+        wait_vmcnt<0>();
+      } else if (later == 1) {
+        wait_vmcnt<NCW>();
+      } else {
+        // only at s = 0, with stages 1 .. later issued behind X(0)
+        static_for<(NSW > 3 ? NSW - 3 : 0)>([&](auto L) {
+          constexpr int n = decltype(L)::value + 2;
+          if (later == n) wait_vmcnt<n * NCW>();
+        });
+      }
       // every wave's copies of stage s are visible after the barrier, and the
       // buffers refilled next (last read at stage s - 1) are free
       __syncthreads();

@@ -156,33 +156,45 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
     // the running max moves once per group (one fp64 rescale), the 8 terms
     // exp(y - m) <= 1 are summed in fp32 with the hardware exp2 and folded
     // into the fp64 sum once
-    for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * blockDim.x) {
-      float x[8];
-      ld8(z + v, x);
-      bool fin = true;
+    // U groups per thread are loaded before any is reduced (more loads in
+    // flight); each thread still takes its groups in increasing order.
+    constexpr int U = 4;
+    const int step = 8 * blockDim.x;
+    for (int vb = v0 + 8 * threadIdx.x; vb < v1; vb += U * step) {
+      float xs[U][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) fin = fin && isfinite(x[e]);
-      if (!fin) {  // rare: element by element, skipping (and flagging) non-finite ones
+      for (int u = 0; u < U; ++u)
+        if (vb + u * step < v1) ld8(z + vb + u * step, xs[u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) push(x[e], v + e);
-        continue;
+      for (int u = 0; u < U; ++u) {
+        const int v = vb + u * step;
+        if (v >= v1) break;
+        const float *x = xs[u];
+        bool fin = true;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fin = fin && isfinite(x[e]);
+        if (!fin) {  // rare: element by element, skipping (and flagging) non-finite ones
+#pragma unroll
+          for (int e = 0; e < 8; ++e) push(x[e], v + e);
+          continue;
+        }
+        float gm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          top2_push(arg, x[e], v + e);
+          gm = fmaxf(gm, x[e] * invT);
+        }
+        if (gm > m) {
+          s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
+          m = gm;
+        }
+        const float mc = m * 1.4426950408889634f;
+        float s8 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s8 += __builtin_amdgcn_exp2f(fmaf(x[e] * invT, 1.4426950408889634f, -mc));
+        s += (double)s8;
       }
-      float gm = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        top2_push(arg, x[e], v + e);
-        gm = fmaxf(gm, x[e] * invT);
-      }
-      if (gm > m) {
-        s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
-        m = gm;
-      }
-      const float mc = m * 1.4426950408889634f;
-      float s8 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        s8 += __builtin_amdgcn_exp2f(fmaf(x[e] * invT, 1.4426950408889634f, -mc));
-      s += (double)s8;
     }
   } else {
     for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) push(ld(z, v), v);
