@@ -263,14 +263,21 @@ struct ArgTop2 {
   float best, second;
   int idx;
 };
+// Selects rather than branches: the update runs once per logit in the
+// vocabulary sweeps, where divergent branches cost more than both sides.
 __device__ __forceinline__ void top2_push(ArgTop2 &a, float s, int i) {
-  if (s > a.best || (s == a.best && i < a.idx)) {
-    a.second = fmaxf(a.second, a.best);
-    a.best = s;
-    a.idx = i;
-  } else {
-    a.second = fmaxf(a.second, s);
-  }
+  const bool win = s > a.best || (s == a.best && i < a.idx);
+  a.second = fmaxf(a.second, win ? a.best : s);
+  a.best = win ? s : a.best;
+  a.idx = win ? i : a.idx;
+}
+// top2_push for a chain that sees its ids in increasing order and finite
+// values only: a later id wins only when strictly greater, so the runner-up
+// is max(second, min(best, s)).
+__device__ __forceinline__ void top2_push_inc(ArgTop2 &a, float s, int i) {
+  a.idx = s > a.best ? i : a.idx;
+  a.second = fmaxf(a.second, fminf(a.best, s));
+  a.best = fmaxf(a.best, s);
 }
 __device__ __forceinline__ ArgTop2 top2_merge(ArgTop2 a, ArgTop2 b) {
   if (b.best > a.best || (b.best == a.best && b.idx < a.idx)) {

@@ -123,10 +123,70 @@ __global__ __launch_bounds__(256) void norm_apply_kernel(const float *__restrict
     out[(long)r * out_stride + c + e] = from_f32<T>(v[e] * rs * to_f32(gain[c + e]));
 }
 
+// One workgroup per row, the whole row in registers (d <= 4096 CPT): the
+// split-sum, the residual write-back, the sum of squares and the scaled
+// output in a single pass, with no scratch row.  Partial planes are summed in
+// split order, as in the two-pass form.
+constexpr int NORM_ROW_T = 1024;
+template <typename T, int CPT>
+__global__ __launch_bounds__(NORM_ROW_T) void norm_row_kernel(
+    const float *__restrict__ parts, int nsplit, int M, int d, float *resid, int write_resid,
+    const T *__restrict__ gain, float eps, T *__restrict__ out, long out_stride) {
+  __shared__ float red[NORM_ROW_T / WAVE];
+  const int r = blockIdx.x;
+  f32x4 x[CPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = (i * NORM_ROW_T + threadIdx.x) * 4;
+    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < d) {
+      if (resid) x[i] = *reinterpret_cast<const f32x4 *>(resid + (long)r * d + c);
+      for (int sp = 0; sp < nsplit; ++sp)
+        x[i] += *reinterpret_cast<const f32x4 *>(parts + ((long)sp * M + r) * d + c);
+      if (resid && write_resid) *reinterpret_cast<f32x4 *>(resid + (long)r * d + c) = x[i];
+      ss += x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
+    }
+  }
+  ss = block_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = (i * NORM_ROW_T + threadIdx.x) * 4;
+    if (c >= d) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      out[(long)r * out_stride + c + e] = from_f32<T>(x[i][e] * rs * to_f32(gain[c + e]));
+  }
+}
+
+template <typename T>
+static bool launch_norm_row(const float *parts, int nsplit, int M, int d, float *resid,
+                            int write_resid, const void *gain, float eps, void *out,
+                            long out_stride, hipStream_t st) {
+  const int cpt = (d + 4 * NORM_ROW_T - 1) / (4 * NORM_ROW_T);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(M), dim3(NORM_ROW_T), 0, st, parts, nsplit, M, d, resid,
+                       write_resid, (const T *)gain, eps, (T *)out, out_stride);
+  };
+  if (cpt == 1) go(norm_row_kernel<T, 1>);
+  else if (cpt == 2) go(norm_row_kernel<T, 2>);
+  else if (cpt <= 4) go(norm_row_kernel<T, 4>);
+  else return false;
+  return true;
+}
+
 void launch_norm_rows(int dtype, const float *parts, int nsplit, int M, int d, float *resid,
                       int write_resid, const void *gain, float eps, void *out, long out_stride,
                       float *xtmp, float *ssp, hipStream_t st) {
   if (M == 0) return;
+  if (d % 4 == 0) {
+    const bool done = dtype == 1 ? launch_norm_row<bf16>(parts, nsplit, M, d, resid, write_resid,
+                                                         gain, eps, out, out_stride, st)
+                                 : launch_norm_row<float>(parts, nsplit, M, d, resid, write_resid,
+                                                          gain, eps, out, out_stride, st);
+    if (done) return;
+  }
   const int nchunk = (d + NORM_CHUNK - 1) / NORM_CHUNK;
   // where x lives for the second pass
   float *xout = (resid && write_resid) ? resid : ((nsplit > 0 || !resid) ? xtmp : nullptr);
@@ -204,14 +264,17 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
   }
 }
 
+constexpr int POST_HEADS = 4;  // heads per workgroup, one wave each
 template <typename T>
-__global__ __launch_bounds__(64) void qkv_post_kernel(
+__global__ __launch_bounds__(64 * POST_HEADS) void qkv_post_kernel(
     const float *__restrict__ parts, int nsplit, int R, int hq, int hkv, int dh,
     const int32_t *__restrict__ eff_ctx, int rows_per_seq, int block,
     const T *__restrict__ q_norm, const T *__restrict__ k_norm, int qk_norm, float eps,
     const float2 *__restrict__ rope, T *__restrict__ q, T *__restrict__ kb, T *__restrict__ vb) {
-  const int r = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
+  const int r = blockIdx.x, head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int half = dh / 2, ncol = (hq + 2 * hkv) * dh;
+  if (head >= hq + 2 * hkv) return;
   const bool is_q = head < hq, is_k = !is_q && head < hq + hkv;
   float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
 #pragma unroll
@@ -255,13 +318,13 @@ void launch_qkv_post(int dtype, const float *parts, int nsplit, int R, int hq, i
                      const void *k_norm, int qk_norm, float eps, const float *rope, void *q,
                      void *kb, void *vb, hipStream_t st) {
   if (R == 0) return;
-  dim3 grid(R, hq + 2 * hkv);
+  dim3 grid(R, (hq + 2 * hkv + POST_HEADS - 1) / POST_HEADS);
   if (dtype == 1)
-    hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
+    hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, R, hq, hkv, dh,
                        eff_ctx, rows_per_seq, block, (const bf16 *)q_norm, (const bf16 *)k_norm,
                        qk_norm, eps, (const float2 *)rope, (bf16 *)q, (bf16 *)kb, (bf16 *)vb);
   else
-    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, R, hq, hkv, dh,
+    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, R, hq, hkv, dh,
                        eff_ctx, rows_per_seq, block, (const float *)q_norm, (const float *)k_norm,
                        qk_norm, eps, (const float2 *)rope, (float *)q, (float *)kb, (float *)vb);
 }
@@ -298,13 +361,14 @@ void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, vo
 
 // ---- injected K/V: k-norm + rotary embedding, scatter into the cache --------
 template <typename T>
-__global__ __launch_bounds__(64) void inject_post_kernel(
+__global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
     int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap) {
-  const int r = blockIdx.x, head = blockIdx.y, layer = blockIdx.z, lane = threadIdx.x;
+  const int r = blockIdx.x, head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
+  const int layer = blockIdx.z, lane = threadIdx.x & 63;
   const int sq = seq[r], ps = pos[r];
-  if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
+  if (head >= 2 * hkv || sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
   const int half = dh / 2, ncol = 2 * hkv * dh, width = il.layers * ncol;
   const bool is_k = head < hkv;
   const int h = is_k ? head : head - hkv;
@@ -346,12 +410,12 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
                         int qk_norm, float eps, const float *rope, int max_batch, int cap,
                         hipStream_t st) {
   if (n == 0 || il.layers == 0) return;
-  dim3 grid(n, 2 * hkv, il.layers);
+  dim3 grid(n, (2 * hkv + POST_HEADS - 1) / POST_HEADS, il.layers);
   if (dtype == 1)
-    hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
+    hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
                        seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
   else
-    hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64), 0, st, parts, nsplit, n, hkv, dh,
+    hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
                        seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
 }
 

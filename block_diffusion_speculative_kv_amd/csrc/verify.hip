@@ -157,45 +157,68 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
     // exp(y - m) <= 1 are summed in fp32 with the hardware exp2 and folded
     // into the fp64 sum once
     // U groups per thread are loaded before any is reduced (more loads in
-    // flight); each thread still takes its groups in increasing order.
+    // flight); each thread still takes its groups in increasing order.  One
+    // top-2 per group position (8 independent chains instead of one); the
+    // top-2 merge with lowest-id ties is order-independent.  Batches whose
+    // values are all finite take a path without per-element branches.
     constexpr int U = 4;
     const int step = 8 * blockDim.x;
-    for (int vb = v0 + 8 * threadIdx.x; vb < v1; vb += U * step) {
+    ArgTop2 ag[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[e] = ArgTop2{-INFINITY, -INFINITY, 0x7fffffff};
+    // (each position chain sees its ids in increasing order: top2_push_inc)
+    const bool want_lse = a.mode != 0;  // greedy decisions use the top-2 only
+    auto group = [&](const float (&x)[8], int v) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) top2_push_inc(ag[e], x[e], v + e);
+      if (!want_lse) return;
+      float y[8], gm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = x[e] * invT;
+        gm = fmaxf(gm, y[e]);
+      }
+      if (gm > m) {
+        s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
+        m = gm;
+      }
+      const float mc = m * 1.4426950408889634f;
+      float s8 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s8 += __builtin_amdgcn_exp2f(fmaf(y[e], 1.4426950408889634f, -mc));
+      s += (double)s8;
+    };
+    // x * 0 is 0 for finite x and NaN otherwise: one multiply-add per value
+    // tells whether a batch holds a non-finite value
+    auto all_finite = [](const float *x, int n) {
+      float t = 0.f;
+      for (int e = 0; e < n; ++e) t = fmaf(x[e], 0.f, t);
+      return t == 0.f;
+    };
+    int vb = v0 + 8 * threadIdx.x;
+    for (; vb + (U - 1) * step < v1; vb += U * step) {
       float xs[U][8];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (vb + u * step < v1) ld8(z + vb + u * step, xs[u]);
+      for (int u = 0; u < U; ++u) ld8(z + vb + u * step, xs[u]);
+      if (all_finite(&xs[0][0], U * 8)) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = vb + u * step;
-        if (v >= v1) break;
-        const float *x = xs[u];
-        bool fin = true;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fin = fin && isfinite(x[e]);
-        if (!fin) {  // rare: element by element, skipping (and flagging) non-finite ones
-#pragma unroll
-          for (int e = 0; e < 8; ++e) push(x[e], v + e);
-          continue;
-        }
-        float gm = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          top2_push(arg, x[e], v + e);
-          gm = fmaxf(gm, x[e] * invT);
-        }
-        if (gm > m) {
-          s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
-          m = gm;
-        }
-        const float mc = m * 1.4426950408889634f;
-        float s8 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s8 += __builtin_amdgcn_exp2f(fmaf(x[e] * invT, 1.4426950408889634f, -mc));
-        s += (double)s8;
+        for (int u = 0; u < U; ++u) group(xs[u], vb + u * step);
+      } else {  // rare: element by element, skipping (and flagging) non-finite ones
+        for (int u = 0; u < U; ++u)
+          for (int e = 0; e < 8; ++e) push(xs[u][e], vb + u * step + e);
       }
     }
+    for (; vb < v1; vb += step) {
+      float x[8];
+      ld8(z + vb, x);
+      if (all_finite(x, 8)) {
+        group(x, vb);
+      } else {
+        for (int e = 0; e < 8; ++e) push(x[e], vb + e);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) arg = top2_merge(arg, ag[e]);
   } else {
     for (int v = v0 + threadIdx.x; v < v1; v += blockDim.x) push(ld(z, v), v);
   }
@@ -245,37 +268,62 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
 
 // ---- decision scan ---------------------------------------------------------
 template <typename TT>
-__global__ __launch_bounds__(64) void vdecide_kernel(VerifyArgs a, VerifyWs w) {
-  const int b = blockIdx.x, k = threadIdx.x;
-  const int G = a.gamma, V = a.vocab;
-  const bool rowlane = k <= G;
-  // merge this lane's row
-  ArgTop2 arg;
-  arg.best = -INFINITY;
-  arg.second = -INFINITY;
-  arg.idx = 0x7fffffff;
-  int bad = 0;
-  double lse = 0.0;
-  if (rowlane) {
-    const long row = (long)b * (G + 1) + k;
+__global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w) {
+  struct RowRes {
+    ArgTop2 arg;
+    int bad;
+    double lse;
+  };
+  __shared__ RowRes res[64];
+  const int b = blockIdx.x, G = a.gamma, V = a.vocab;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  // Row merge, one wave per target row, lanes over the row's vocabulary
+  // splits: top-2 and flags by wave reduction, then the log-sum-exp as
+  // M + log(sum_j s_j exp(m_j - M)) with M the largest split maximum.
+  for (int kr = wave; kr <= G; kr += nw) {
+    const long row = (long)b * (G + 1) + kr;
+    ArgTop2 arg{-INFINITY, -INFINITY, 0x7fffffff};
     float m = -INFINITY;
-    double s = 0.0;
-    for (int sp = 0; sp < a.nsplit; ++sp) {
+    double sv = 0.0;
+    int bad = 0;
+    for (int sp = lane; sp < a.nsplit; sp += WAVE) {
       const VRowPart p = w.rowpart[row * a.nsplit + sp];
-      ArgTop2 y{p.best, p.second, p.idx};
-      arg = top2_merge(arg, y);
+      arg = top2_merge(arg, ArgTop2{p.best, p.second, p.idx});
       bad |= p.bad;
       if (p.m != -INFINITY) {
-        if (m == -INFINITY) { m = p.m; s = p.s; }
+        if (m == -INFINITY) { m = p.m; sv = p.s; }
         else {
           const float M = fmaxf(m, p.m);
-          s = s * exp((double)m - M) + p.s * exp((double)p.m - M);
+          sv = sv * exp((double)m - M) + p.s * exp((double)p.m - M);
           m = M;
         }
       }
     }
-    lse = (double)m + log(s);
-    w.lse_t[row] = lse;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      arg = top2_shfl_xor(arg, o);
+      bad |= __shfl_xor(bad, o, WAVE);
+    }
+    const float M = wave_max(m);
+    const double part = m == -INFINITY ? 0.0 : sv * exp((double)m - (double)M);
+    const double S = wave_sum(part);
+    if (lane == 0) {
+      const double lse = (double)M + log(S);
+      res[kr] = RowRes{arg, bad, lse};
+      w.lse_t[row] = lse;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int k = lane;
+  const bool rowlane = k <= G;
+  ArgTop2 arg{-INFINITY, -INFINITY, 0x7fffffff};
+  int bad = 0;
+  double lse = 0.0;
+  if (rowlane) {
+    arg = res[k].arg;
+    bad = res[k].bad;
+    lse = res[k].lse;
   }
   int y = 0, yraw = 0;
   if (k < G) {
@@ -403,19 +451,29 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
 }
 
 __global__ __launch_bounds__(64) void vfinish_kernel(VerifyArgs a, VerifyWs w) {
-  const int b = blockIdx.x;
-  if (threadIdx.x != 0) return;
+  const int b = blockIdx.x, lane = threadIdx.x;
   const int G = a.gamma;
   const int ks = w.kstar[b];
+  // lanes over the split records, merged by wave reduction (the top-2 merge
+  // with lowest-id ties gives the same result in any order)
   D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
   int any_r = 0, bad = 0;
-  for (int sp = 0; sp < a.nsamp; ++sp) {
+  for (int sp = lane; sp < a.nsamp; sp += WAVE) {
     const VSampPart p = w.samp[(long)b * a.nsamp + sp];
     rr = d2_merge(rr, D2{p.best_r, p.second_r, p.idx_r});
     pp = d2_merge(pp, D2{p.best_p, p.second_p, p.idx_p});
     any_r |= p.any_r;
     bad |= p.bad;
   }
+  for (int o = 32; o > 0; o >>= 1) {
+    rr = d2_merge(rr, D2{__shfl_xor(rr.best, o, WAVE), __shfl_xor(rr.second, o, WAVE),
+                         __shfl_xor(rr.idx, o, WAVE)});
+    pp = d2_merge(pp, D2{__shfl_xor(pp.best, o, WAVE), __shfl_xor(pp.second, o, WAVE),
+                         __shfl_xor(pp.idx, o, WAVE)});
+    any_r |= __shfl_xor(any_r, o, WAVE);
+    bad |= __shfl_xor(bad, o, WAVE);
+  }
+  if (lane != 0) return;
   uint32_t f = 0;
   int tok;
   double gap;
@@ -438,7 +496,8 @@ static void launch_typed(const VerifyArgs &a, hipStream_t st) {
   VerifyWs w = carve(a.ws, a.bs, a.gamma, a.nsplit);
   const int rows = a.bs * (a.gamma + 1);
   hipLaunchKernelGGL(vrow_kernel<TT>, dim3(rows, a.nsplit), dim3(256), 0, st, a, w);
-  hipLaunchKernelGGL(vdecide_kernel<TT>, dim3(a.bs), dim3(64), 0, st, a, w);
+  const int dw = a.gamma + 1 < 16 ? a.gamma + 1 : 16;  // one wave per target row, up to 16
+  hipLaunchKernelGGL(vdecide_kernel<TT>, dim3(a.bs), dim3(64 * dw), 0, st, a, w);
   if (a.mode == 1) {
     hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsamp), dim3(256), 0, st, a, w);
     hipLaunchKernelGGL(vfinish_kernel, dim3(a.bs), dim3(64), 0, st, a, w);
