@@ -23,6 +23,7 @@ __all__ = [
     "HEAD_GUMBEL", "HEAD_SHARED_GUMBEL", "VERIFY_GREEDY", "VERIFY_RS", "FLAG_NEAR_TIE_TARGET",
     "FLAG_NEAR_THRESHOLD", "FLAG_NEAR_TIE_SAMPLE", "FLAG_ZERO_RESIDUAL", "FLAG_BAD_INPUT",
     "FLAG_CTX_CLAMPED", "NEAR",
+    "dloop_branches", "dloop_merge", "verify_branches", "verify_branches_workspace_bytes",
 ]
 
 _DT = {"f32": F32, "bf16": BF16}
@@ -200,3 +201,51 @@ def verify(mode: int, draft_ids, target_logits, out_tokens, out_tau, out_flags, 
                                  _ptr(target_logits), tdt, _ptr(out_tokens), _ptr(out_tau),
                                  _ptr(out_flags), _ptr(ws), ws.numel(), _stream(stream)),
                "dstill_verify")
+
+
+# ---- D-Loop second pass ------------------------------------------------------
+def dloop_branches(anchor, ids, zmax, lse, K: int, mask_id: int, block_tokens, prefix_len,
+                   score=None, stream=None):
+    """anchor [bs], first-pass ids / zmax / lse [bs, gamma] -> block_tokens
+    [bs, K, gamma+1] int32, prefix_len [bs, K] int32, score [bs, K] fp64."""
+    lib = _lib.load()
+    _dev_check(anchor, ids, zmax, lse, block_tokens, prefix_len, score)
+    bs, g = ids.shape
+    _lib.check(lib.dstill_dloop_branches(bs, g, K, _ptr(anchor), _ptr(ids), _ptr(zmax), _ptr(lse),
+                                         int(mask_id), _ptr(block_tokens), _ptr(prefix_len),
+                                         _ptr(score), _stream(stream)), "dstill_dloop_branches")
+
+
+def dloop_merge(first_ids, second_ids, prefix_len, out_ids, stream=None):
+    """first_ids [bs, gamma], second_ids [bs, K, gamma], prefix_len [bs, K]
+    -> out_ids [bs, K, gamma] (int32)."""
+    lib = _lib.load()
+    _dev_check(first_ids, second_ids, prefix_len, out_ids)
+    bs, K, g = second_ids.shape
+    _lib.check(lib.dstill_dloop_merge(bs, g, K, _ptr(first_ids), _ptr(second_ids),
+                                      _ptr(prefix_len), _ptr(out_ids), _stream(stream)),
+               "dstill_dloop_merge")
+
+
+def verify_branches_workspace_bytes(bs: int, K: int, gamma: int, vocab: int) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t()
+    _lib.check(lib.dstill_verify_branches_workspace_bytes(bs, K, gamma, vocab, ctypes.byref(n)),
+               "dstill_verify_branches_workspace_bytes")
+    return n.value
+
+
+def verify_branches(draft_ids, target_logits, out_tokens, out_tau, out_branch, out_flags, ws,
+                    stream=None):
+    """draft_ids [bs, K, gamma] int32; target_logits [bs, K, gamma+1, V]
+    fp32/bf16 -> tokens [bs, gamma+1], tau [bs], branch [bs], flags [bs]."""
+    lib = _lib.load()
+    _dev_check(draft_ids, target_logits, out_tokens, out_tau, out_branch, out_flags, ws)
+    bs, K, g1, V = target_logits.shape
+    if target_logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("target logits must be fp32 or bf16")
+    tdt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    _lib.check(lib.dstill_verify_branches(bs, K, g1 - 1, V, _ptr(draft_ids), _ptr(target_logits),
+                                          tdt, _ptr(out_tokens), _ptr(out_tau), _ptr(out_branch),
+                                          _ptr(out_flags), _ptr(ws), ws.numel(), _stream(stream)),
+               "dstill_verify_branches")

@@ -508,4 +508,87 @@ int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float 
   return hip_check("verify launch");
 }
 
+int dstill_dloop_branches(int32_t bs, int32_t gamma, int32_t K, const int32_t *anchor,
+                          const int32_t *ids, const float *zmax, const float *lse,
+                          int32_t mask_id, int32_t *block_tokens, int32_t *prefix_len,
+                          double *score, void *stream) {
+  if (bs < 0 || gamma < 1 || gamma > 63 || K < 1 || K > gamma)
+    return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= gamma <= 63, 1 <= K <= gamma");
+  if (bs == 0) return DSTILL_OK;
+  if (!anchor || !ids || !zmax || !lse || !block_tokens || !prefix_len)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  DloopArgs a;
+  a.bs = bs; a.gamma = gamma; a.K = K; a.mask_id = mask_id;
+  a.anchor = anchor; a.ids = ids; a.zmax = zmax; a.lse = lse;
+  a.block_tokens = block_tokens; a.prefix_len = prefix_len; a.score = score;
+  launch_dloop_branches(a, (hipStream_t)stream);
+  return hip_check("dloop_branches launch");
+}
+
+int dstill_dloop_merge(int32_t bs, int32_t gamma, int32_t K, const int32_t *first_ids,
+                       const int32_t *second_ids, const int32_t *prefix_len, int32_t *out_ids,
+                       void *stream) {
+  if (bs < 0 || gamma < 1 || gamma > 63 || K < 1 || K > 65535)
+    return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= gamma <= 63, 1 <= K <= 65535");
+  if (bs == 0) return DSTILL_OK;
+  if (!first_ids || !second_ids || !prefix_len || !out_ids)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  launch_dloop_merge(bs, gamma, K, first_ids, second_ids, prefix_len, out_ids,
+                     (hipStream_t)stream);
+  return hip_check("dloop_merge launch");
+}
+
+static size_t branch_ws_bytes(int32_t bs, int32_t K, int32_t gamma, int32_t vocab) {
+  const long n = (long)bs * K;
+  const size_t inner = verify_ws_bytes((int)n, gamma, verify_plan_splits((int)n * (gamma + 1), vocab),
+                                       verify_plan_splits((int)n, vocab));
+  return a256(inner) + a256((size_t)n * (gamma + 1) * 4) + 2 * a256((size_t)n * 4);
+}
+
+int dstill_verify_branches_workspace_bytes(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
+                                           size_t *bytes) {
+  if (!bytes) return fail(DSTILL_EINVAL, "bytes is null");
+  if (bs < 0 || K < 1 || gamma < 1 || gamma > 63 || vocab < 2 || (long)bs * K > (1L << 24))
+    return fail(DSTILL_ESHAPE, "need bs >= 0, K >= 1, 1 <= gamma <= 63, vocab >= 2");
+  *bytes = branch_ws_bytes(bs, K, gamma, vocab);
+  return DSTILL_OK;
+}
+
+int dstill_verify_branches(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
+                           const int32_t *draft_ids, const void *target_logits,
+                           int32_t target_dtype, int32_t *out_tokens, int32_t *out_tau,
+                           int32_t *out_branch, uint32_t *out_flags, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (bs < 0 || K < 1 || gamma < 1 || gamma > 63 || vocab < 2 || (long)bs * K > (1L << 24))
+    return fail(DSTILL_ESHAPE, "need bs >= 0, K >= 1, 1 <= gamma <= 63, vocab >= 2");
+  if (target_dtype != DSTILL_F32 && target_dtype != DSTILL_BF16)
+    return fail(DSTILL_EUNSUPPORTED, "target_dtype %d", target_dtype);
+  if (bs == 0) return DSTILL_OK;
+  if (!draft_ids || !target_logits || !out_tokens || !out_tau || !out_flags || !ws)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  const size_t need = branch_ws_bytes(bs, K, gamma, vocab);
+  if (ws_bytes < need)
+    return fail(DSTILL_EWORKSPACE, "verify_branches needs %zu workspace bytes", need);
+  const int n = bs * K;
+  Carver cv(ws);
+  const int nsplit = verify_plan_splits(n * (gamma + 1), vocab);
+  const int nsamp = verify_plan_splits(n, vocab);
+  void *inner = cv.take<char>(verify_ws_bytes(n, gamma, nsplit, nsamp));
+  int32_t *tok = cv.take<int32_t>((size_t)n * (gamma + 1));
+  int32_t *tau = cv.take<int32_t>(n);
+  uint32_t *flg = cv.take<uint32_t>(n);
+  hipStream_t st = (hipStream_t)stream;
+  // every branch verified as its own sequence, then the longest one kept
+  VerifyArgs a;
+  a.mode = DSTILL_VERIFY_GREEDY; a.bs = n; a.gamma = gamma; a.vocab = vocab;
+  a.tdtype = target_dtype; a.temperature = 1.0f; a.seed = 0; a.cycle = 0;
+  a.draft_ids = draft_ids; a.draft_lse = nullptr; a.draft_logits = nullptr;
+  a.target = target_logits;
+  a.tokens = tok; a.tau = tau; a.flags = flg;
+  a.ws = inner; a.nsplit = nsplit; a.nsamp = nsamp;
+  launch_verify(a, st);
+  launch_branch_pick(bs, K, gamma, tok, tau, flg, out_tokens, out_tau, out_branch, out_flags, st);
+  return hip_check("verify_branches launch");
+}
+
 }  // extern "C"

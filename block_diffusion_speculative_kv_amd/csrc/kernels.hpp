@@ -138,4 +138,21 @@ int verify_plan_splits(int rows, int vocab);
 size_t verify_ws_bytes(int bs, int gamma, int nsplit, int nsamp);
 void launch_verify(const VerifyArgs &a, hipStream_t st);
 
+// ---- D-Loop second pass (dloop.hip) -----------------------------------------
+struct DloopArgs {
+  int bs, gamma, K, mask_id;
+  const int32_t *anchor;  // [bs]
+  const int32_t *ids;     // [bs, gamma] first-pass proposal
+  const float *zmax, *lse;  // [bs, gamma] first-pass head statistics
+  int32_t *block_tokens;  // [bs, K, gamma + 1]
+  int32_t *prefix_len;    // [bs, K]
+  double *score;          // [bs, K] or null
+};
+void launch_dloop_branches(const DloopArgs &a, hipStream_t st);
+void launch_dloop_merge(int bs, int gamma, int K, const int32_t *first, const int32_t *second,
+                        const int32_t *lens, int32_t *out, hipStream_t st);
+void launch_branch_pick(int bs, int K, int gamma, const int32_t *tok, const int32_t *tau,
+                        const uint32_t *flags, int32_t *out_tokens, int32_t *out_tau,
+                        int32_t *out_branch, uint32_t *out_flags, hipStream_t st);
+
 }  // namespace dstill

@@ -260,6 +260,54 @@ int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float 
                   int32_t *out_tau, uint32_t *out_flags, void *ws, size_t ws_bytes,
                   void *stream);
 
+/* ---- D-Loop: looped second draft pass and joint K-branch verification ----
+ * D-Loop page, section 3.1 (the prefix score after Eq. (4), Eq. (5)) and
+ * section 3.3 (inference: joint verification of K branches).
+ *
+ * dstill_dloop_branches: from the first pass's head statistics of slots
+ * 1..gamma (ids, zmax, lse: [bs][gamma], device), the confidence of each
+ * proposed token is c_k = exp(zmax_k - lse_k) (its softmax probability at
+ * T = 1, computed in fp64) and each prefix length l = 0..gamma-1 is scored
+ * r_l = (c_1 ... c_l)(1 - c_{l+1}) (taken left to right in fp64).  The K
+ * largest scores (ties to the smaller l) give the branches, in decreasing
+ * order of r: prefix_len [bs][K] int32, score [bs][K] fp64 (NULL to skip),
+ * and block_tokens [bs][K][gamma+1] int32 = (anchor[b], ids[b][0..l-1],
+ * mask_id, ..., mask_id), ready for dstill_block_draft with n_copies = K
+ * (each branch is a copy of the block behind the shared context).
+ * Non-finite statistics give unspecified (in-range) lengths.
+ * Errors: ESHAPE unless 1 <= K <= gamma <= 63; EINVAL on null pointers. */
+int dstill_dloop_branches(int32_t bs, int32_t gamma, int32_t K, const int32_t *anchor,
+                          const int32_t *ids, const float *zmax, const float *lse,
+                          int32_t mask_id, int32_t *block_tokens, int32_t *prefix_len,
+                          double *score, void *stream);
+
+/* dstill_dloop_merge: each branch's proposal (Eq. (5)): out_ids[b][j][k] =
+ * first_ids[b][k] for k < prefix_len[b][j], else second_ids[b][j][k]
+ * (first_ids [bs][gamma], second_ids and out_ids [bs][K][gamma], int32,
+ * device; second_ids are the second pass's head ids of slots 1..gamma).
+ * Errors: ESHAPE, EINVAL. */
+int dstill_dloop_merge(int32_t bs, int32_t gamma, int32_t K, const int32_t *first_ids,
+                       const int32_t *second_ids, const int32_t *prefix_len, int32_t *out_ids,
+                       void *stream);
+
+/* dstill_verify_branches: joint greedy verification of K branch proposals
+ * per sequence.  Branch j of sequence b has draft_ids [bs][K][gamma] and its
+ * own target rows target_logits [bs][K][gamma+1][vocab] (target_dtype
+ * DSTILL_F32 or DSTILL_BF16).  Each branch is verified by the GREEDY rule of
+ * dstill_verify; the branch with the largest tau (ties to the lowest j) is
+ * committed: out_tokens [bs][gamma+1] (-1 after tau), out_tau [bs],
+ * out_branch [bs] (NULL to skip); out_flags [bs] is the OR of every branch's
+ * flags (a near tie in any branch can change which is longest).
+ * Workspace: dstill_verify_branches_workspace_bytes.
+ * Errors: ESHAPE, EUNSUPPORTED, EINVAL, EWORKSPACE. */
+int dstill_verify_branches_workspace_bytes(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
+                                           size_t *bytes);
+int dstill_verify_branches(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
+                           const int32_t *draft_ids, const void *target_logits,
+                           int32_t target_dtype, int32_t *out_tokens, int32_t *out_tau,
+                           int32_t *out_branch, uint32_t *out_flags, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Message for the last non-zero status returned on this thread. */
 const char *dstill_last_error(void);
 /* Library ABI version (major * 100 + minor). */
