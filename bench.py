@@ -188,14 +188,16 @@ def main():
         taus = cyc.tau.cpu().numpy().tolist()
 
     # per-call timing (same stream, events around each library call)
-    names = ["inject", "draft", "head", "verify"]
+    names = ["inject", "draft", "head"] + (["loop"] if cyc.K else []) + ["verify"]
     evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] for n in names}
     tau_hist = []
     for i in range(args.steps):
         c = args.warmup + args.steps + i
-        for n, fn in (("inject", cyc.inject), ("draft", cyc.draft),
-                      ("head", lambda: cyc.head(c)), ("verify", lambda: cyc.verify(c))):
+        calls = {"inject": cyc.inject, "draft": cyc.draft, "head": lambda: cyc.head(c),
+                 "loop": lambda: cyc.loop(c), "verify": lambda: cyc.verify(c)}
+        for n in names:
+            fn = calls[n]
             evs[n][i][0].record(st)
             fn()
             evs[n][i][1].record(st)
@@ -209,6 +211,13 @@ def main():
 
     n_inj = cfg["bs"] * cyc.n_new
     alg = _algorithmic(cfg, cyc.rows, n_inj)
+    if cyc.K:
+        # second pass: the drafter over K copies and the head over K gamma
+        # rows; the joint verification reads every branch's target rows
+        alg2 = _algorithmic(dict(cfg, n_copies=cyc.K), cyc.rows2, n_inj)
+        alg["loop"] = dict(bytes=alg2["draft"]["bytes"] + alg2["head"]["bytes"],
+                           flops=alg2["draft"]["flops"] + alg2["head"]["flops"])
+        alg["verify"] = dict(bytes=alg["verify"]["bytes"] * cyc.K, flops=0)
     cycles_per_s = 1000.0 / ms_step
     bs = cfg["bs"]
     tokens_per_s = cycles_per_s * bs * tau_mean if tau_mean else None
@@ -293,7 +302,7 @@ def main():
         "config": {"workload": args.workload, "batch": bs, "block": cfg["block"],
                    "gamma": cfg["gamma"], "ctx": cfg["ctx"] if isinstance(cfg["ctx"], str)
                    else cfg["ctx_lens"], "verify": cfg["verify"], "head": cfg["lm_mode"],
-                   "n_new_per_cycle": cyc.n_new},
+                   "n_new_per_cycle": cyc.n_new, **({"dloop_k": cyc.K} if cyc.K else {})},
         "tokens_per_s": round(tokens_per_s, 1) if tokens_per_s else None,
         "tau_mean": tau_mean,
         "hbm_gbs": round(hbm_gbs, 1),

@@ -12,6 +12,12 @@ Inference and Preliminary; DStill, Inference):
                   multi-copy layout, whose verify is its own state-equality
                   rule)
 
+With dloop_k = K > 0 (D-Loop, section 3.1 and 3.3) the head is followed by
+the looped second pass: the K best prefix lengths of the first proposal are
+re-drafted as K copies of the block (branch set-up, block_draft, head,
+prefix/suffix merge), and the K branches are verified jointly, each against
+its own synthetic target rows.
+
 The context cache is filled once by injecting every context row (prefill),
 in chunks.  In steady state each cycle re-injects the n_new most recent
 context positions of every sequence (the same slots every cycle), so every
@@ -26,7 +32,8 @@ import torch
 
 from synth import gen
 
-from . import Drafter, verify, verify_workspace_bytes
+from . import (Drafter, dloop_branches, dloop_merge, verify, verify_branches,
+               verify_branches_workspace_bytes, verify_workspace_bytes)
 from ._lib import HEAD_ARGMAX, HEAD_GUMBEL, HEAD_SHARED_GUMBEL, VERIFY_GREEDY, VERIFY_RS
 
 _HEAD_MODE = {"argmax": HEAD_ARGMAX, "gumbel": HEAD_GUMBEL, "shared_gumbel": HEAD_SHARED_GUMBEL}
@@ -56,10 +63,12 @@ class Cycle:
             self.rows, self.rows_per_seq, self.seq_stride, self.row0 = bs * C * self.gamma, \
                 self.gamma, B, 1
         inj_rows = bs * self.n_new
-        self.ws = self.dr.workspace(max_batch=bs, max_copies=C, max_ctx=self.max_ctx,
+        self.K = int(cfg.get("dloop_k", 0))
+        self.rows2 = bs * self.K * self.gamma
+        self.ws = self.dr.workspace(max_batch=bs, max_copies=max(C, self.K), max_ctx=self.max_ctx,
                                     max_inject_rows=max(inj_rows, min(prefill_chunk,
                                                                       sum(self.ctx) or 1)),
-                                    max_head_rows=self.rows)
+                                    max_head_rows=max(self.rows, self.rows2))
         self._prefill(prefill_chunk)
         # per-cycle inputs
         self.tokens = gen.block_tokens(cfg, device=self.dev)
@@ -91,6 +100,19 @@ class Cycle:
             self.vflags = torch.empty(bs, dtype=torch.int32, device=self.dev)
             self.vws = torch.empty(verify_workspace_bytes(bs, self.gamma, cfg["vocab"]),
                                    dtype=torch.uint8, device=self.dev)
+        if self.K:
+            K, g, i32 = self.K, self.gamma, torch.int32
+            self.anchor = self.tokens[:, 0, 0].contiguous()
+            self.blocks = torch.empty((bs, K, B), dtype=i32, device=self.dev)
+            self.prefix_len = torch.empty((bs, K), dtype=i32, device=self.dev)
+            self.hidden2 = torch.empty((bs, K, B, d), dtype=self.dr.tdtype, device=self.dev)
+            self.ids2 = torch.empty(self.rows2, dtype=i32, device=self.dev)
+            self.proposal = torch.empty((bs, K, g), dtype=i32, device=self.dev)
+            self.branch = torch.empty(bs, dtype=i32, device=self.dev)
+            self.target_br = gen.normal((bs, K, g + 1, cfg["vocab"]), cfg["target_logit_std"],
+                                        seed=cfg["seed"], name="target_branches", device=self.dev)
+            self.vws_br = torch.empty(verify_branches_workspace_bytes(bs, K, g, cfg["vocab"]),
+                                      dtype=torch.uint8, device=self.dev)
         torch.cuda.synchronize(self.dev)
 
     def _prefill(self, chunk):
@@ -118,10 +140,29 @@ class Cycle:
                                cycle=cycle, zmax=self.zmax, lse=self.lse, zsel=self.zsel,
                                gap=self.gap, logits=self.logits)
 
+    def loop(self, cycle: int):
+        """D-Loop second pass: branches, K-copy draft, head, merge."""
+        if not self.K:
+            return
+        bs, g, B, d = self.cfg["bs"], self.gamma, self.cfg["block"], self.cfg["hidden"]
+        dloop_branches(self.anchor, self.ids.view(bs, g), self.zmax.view(bs, g),
+                       self.lse.view(bs, g), self.K, self.cfg["mask_token_id"], self.blocks,
+                       self.prefix_len)
+        self.dr.block_draft(self.blocks, self.ctx_len, self.max_ctx, self.kv, self.hidden2,
+                            self.ws)
+        self.dr.lm_head_argmax(self.hidden2.view(-1, d)[1:], self.rows2, g, B, self.ids2,
+                               self.ws, mode=HEAD_ARGMAX, cycle=cycle)
+        dloop_merge(self.ids.view(bs, g), self.ids2.view(bs, self.K, g), self.prefix_len,
+                    self.proposal)
+
     def verify(self, cycle: int):
         if self.verify_mode is None:
             return
         bs = self.cfg["bs"]
+        if self.K:
+            verify_branches(self.proposal, self.target_br, self.out_tokens, self.tau,
+                            self.branch, self.vflags, self.vws_br)
+            return
         verify(self.verify_mode, self.ids.view(bs, self.gamma), self.target, self.out_tokens,
                self.tau, self.vflags, self.vws, temperature=self.T, seed=self.seed, cycle=cycle,
                draft_lse=self.lse.view(bs, self.gamma) if self.logits is not None else None,
@@ -132,4 +173,5 @@ class Cycle:
         self.inject()
         self.draft()
         self.head(cycle)
+        self.loop(cycle)
         self.verify(cycle)

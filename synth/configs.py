@@ -57,6 +57,14 @@ WORKLOADS = {
         lm_mode="shared_gumbel", temperature=1.0, target_logit_std=2.0,
         target_dtype="f32", seed=0,
     ),
+    # D-Loop looped second pass (K = 4 branches) on the bs-1 greedy workload:
+    # first pass, top-4 prefix branches re-drafted as 4 copies of the block,
+    # joint greedy verification of the 4 branches.
+    "q8b_dloop_k4": dict(
+        _Q8B, bs=1, ctx=[4096], n_copies=1, verify="greedy",
+        lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
+        target_dtype="f32", seed=0, dloop_k=4,
+    ),
 }
 
 # Order used when a workload is referred to by index (0 = the tiny case).
