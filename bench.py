@@ -51,6 +51,8 @@ def _algorithmic(cfg, rows, n_inj):
     ver_bytes = bs * (g + 1) * V * tsz + (bs * V * 4 if cfg["verify"] == "rs" else 0)
     if cfg["verify"] == "none":
         ver_bytes = 0
+    if cfg["verify"] == "spot":  # per-slot head outputs and states of every copy
+        ver_bytes = bs * C * B * 5 * 4
     draft_bytes = eb * L * layer_params + attn_bytes
     draft_flops = 2 * R * L * layer_params + attn_flops
     return dict(
@@ -184,7 +186,7 @@ def main():
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
-    if cyc.verify_mode is not None:
+    if cyc.yields:
         taus = cyc.tau.cpu().numpy().tolist()
 
     # per-call timing (same stream, events around each library call)
@@ -201,7 +203,7 @@ def main():
             evs[n][i][0].record(st)
             fn()
             evs[n][i][1].record(st)
-        if cyc.verify_mode is not None and i < 8:
+        if cyc.yields and i < 8:
             tau_hist.append(cyc.tau.clone())
     torch.cuda.synchronize()
     per_call = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) for n in names}

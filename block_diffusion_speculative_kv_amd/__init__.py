@@ -24,6 +24,7 @@ __all__ = [
     "FLAG_NEAR_THRESHOLD", "FLAG_NEAR_TIE_SAMPLE", "FLAG_ZERO_RESIDUAL", "FLAG_BAD_INPUT",
     "FLAG_CTX_CLAMPED", "NEAR",
     "dloop_branches", "dloop_merge", "verify_branches", "verify_branches_workspace_bytes",
+    "spot_verify",
 ]
 
 _DT = {"f32": F32, "bf16": BF16}
@@ -249,3 +250,20 @@ def verify_branches(draft_ids, target_logits, out_tokens, out_tau, out_branch, o
                                           tdt, _ptr(out_tokens), _ptr(out_tau), _ptr(out_branch),
                                           _ptr(out_flags), _ptr(ws), ws.numel(), _stream(stream)),
                "dstill_verify_branches")
+
+
+# ---- SPOT state-equality verification -------------------------------------------
+def spot_verify(states, parent, ids, zmax, lse, mask_id: int, out_n, out_slots, out_tokens,
+                out_state, out_flags, *, temperature=1.0, gap=None, stream=None):
+    """states / ids / zmax / lse / gap [bs, n_states, L]; parent [bs, n_states]
+    -> out_n [bs], out_slots / out_tokens [bs, n_states], out_state [bs],
+    out_flags [bs]."""
+    lib = _lib.load()
+    _dev_check(states, parent, ids, zmax, lse, gap, out_n, out_slots, out_tokens, out_state,
+               out_flags)
+    bs, n, L = states.shape
+    _lib.check(lib.dstill_spot_verify(bs, n, L, int(mask_id), float(temperature), _ptr(states),
+                                      _ptr(parent), _ptr(ids), _ptr(zmax), _ptr(lse), _ptr(gap),
+                                      _ptr(out_n), _ptr(out_slots), _ptr(out_tokens),
+                                      _ptr(out_state), _ptr(out_flags), _stream(stream)),
+               "dstill_spot_verify")

@@ -591,4 +591,25 @@ int dstill_verify_branches(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
   return hip_check("verify_branches launch");
 }
 
+int dstill_spot_verify(int32_t bs, int32_t n_states, int32_t L, int32_t mask_id,
+                       float temperature, const int32_t *states, const int32_t *parent,
+                       const int32_t *ids, const float *zmax, const float *lse, const float *gap,
+                       int32_t *out_n, int32_t *out_slots, int32_t *out_tokens,
+                       int32_t *out_state, uint32_t *out_flags, void *stream) {
+  if (bs < 0 || n_states < 1 || n_states > 64 || L < 1 || L > 64)
+    return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= n_states <= 64, 1 <= L <= 64");
+  if (!(temperature > 0.f)) return fail(DSTILL_EINVAL, "temperature must be > 0");
+  if (bs == 0) return DSTILL_OK;
+  if (!states || !parent || !ids || !zmax || !lse || !out_n || !out_slots || !out_tokens ||
+      !out_state || !out_flags)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  SpotArgs a;
+  a.bs = bs; a.n_states = n_states; a.L = L; a.mask_id = mask_id; a.temperature = temperature;
+  a.states = states; a.parent = parent; a.ids = ids; a.zmax = zmax; a.lse = lse; a.gap = gap;
+  a.out_n = out_n; a.out_slots = out_slots; a.out_tokens = out_tokens; a.out_state = out_state;
+  a.out_flags = out_flags;
+  launch_spot_verify(a, (hipStream_t)stream);
+  return hip_check("spot_verify launch");
+}
+
 }  // extern "C"

@@ -155,4 +155,17 @@ void launch_branch_pick(int bs, int K, int gamma, const int32_t *tok, const int3
                         const uint32_t *flags, int32_t *out_tokens, int32_t *out_tau,
                         int32_t *out_branch, uint32_t *out_flags, hipStream_t st);
 
+// ---- SPOT state-equality verification (spot.hip) -------------------------------
+struct SpotArgs {
+  int bs, n_states, L, mask_id;
+  float temperature;
+  const int32_t *states;  // [bs, n_states, L]
+  const int32_t *parent;  // [bs, n_states]
+  const int32_t *ids;     // [bs, n_states, L] per-slot head outputs
+  const float *zmax, *lse, *gap;  // gap may be null
+  int32_t *out_n, *out_slots, *out_tokens, *out_state;
+  uint32_t *out_flags;
+};
+void launch_spot_verify(const SpotArgs &a, hipStream_t st);
+
 }  // namespace dstill

@@ -8,9 +8,9 @@ Inference and Preliminary; DStill, Inference):
   block_draft     one pass over anchor + gamma masks (per copy)
   lm_head_argmax  shared head: greedy argmax, Gumbel-max sampling, or the
                   shared-Gumbel argmax of the multi-copy layout
-  verify          greedy prefix match or rejection sampling (none for the
-                  multi-copy layout, whose verify is its own state-equality
-                  rule)
+  verify          greedy prefix match or rejection sampling; for the
+                  multi-copy layout, SPOT's state-equality verification of
+                  the drafted tree (root = copy 0)
 
 With dloop_k = K > 0 (D-Loop, section 3.1 and 3.3) the head is followed by
 the looped second pass: the K best prefix lengths of the first proposal are
@@ -32,7 +32,7 @@ import torch
 
 from synth import gen
 
-from . import (Drafter, dloop_branches, dloop_merge, verify, verify_branches,
+from . import (Drafter, dloop_branches, dloop_merge, spot_verify, verify, verify_branches,
                verify_branches_workspace_bytes, verify_workspace_bytes)
 from ._lib import HEAD_ARGMAX, HEAD_GUMBEL, HEAD_SHARED_GUMBEL, VERIFY_GREEDY, VERIFY_RS
 
@@ -54,6 +54,8 @@ class Cycle:
         self.kv = self.dr.kv_cache(bs, (self.max_ctx + B + 63) // 64 * 64)
         self.mode = _HEAD_MODE[cfg["lm_mode"]]
         self.verify_mode = {"greedy": VERIFY_GREEDY, "rs": VERIFY_RS}.get(cfg["verify"])
+        self.spot = cfg["verify"] == "spot"
+        self.yields = self.verify_mode is not None or self.spot  # tokens per cycle known
         self.T = float(cfg.get("temperature", 1.0))
         self.seed = seed
         # head rows: slots 1..gamma of every block, or all slots of every copy
@@ -71,7 +73,10 @@ class Cycle:
                                     max_head_rows=max(self.rows, self.rows2))
         self._prefill(prefill_chunk)
         # per-cycle inputs
-        self.tokens = gen.block_tokens(cfg, device=self.dev)
+        if self.spot:
+            self.tokens, self.parent = gen.draft_tree(cfg, device=self.dev)
+        else:
+            self.tokens = gen.block_tokens(cfg, device=self.dev)
         self.ctx_len = torch.tensor(self.ctx, dtype=torch.int32, device=self.dev)
         self.feats = gen.feats(cfg, inj_rows, name="feats_cycle", device=self.dev)
         seq, pos = [], []
@@ -92,6 +97,13 @@ class Cycle:
         self.gap = torch.empty(r, dtype=torch.float32, device=self.dev)
         self.logits = (torch.empty((r, cfg["vocab"]), dtype=torch.float32, device=self.dev)
                        if self.verify_mode == VERIFY_RS else None)
+        if self.spot:
+            i32 = torch.int32
+            self.tau = torch.empty(bs, dtype=i32, device=self.dev)  # commits this round
+            self.spot_slots = torch.empty((bs, C), dtype=i32, device=self.dev)
+            self.spot_tokens = torch.empty((bs, C), dtype=i32, device=self.dev)
+            self.spot_state = torch.empty(bs, dtype=i32, device=self.dev)
+            self.vflags = torch.empty(bs, dtype=i32, device=self.dev)
         if self.verify_mode is not None:
             self.target = gen.target_logits(cfg, device=self.dev)
             self.out_tokens = torch.empty((bs, self.gamma + 1), dtype=torch.int32,
@@ -156,9 +168,17 @@ class Cycle:
                     self.proposal)
 
     def verify(self, cycle: int):
+        bs = self.cfg["bs"]
+        if self.spot:
+            C, B = self.cfg["n_copies"], self.cfg["block"]
+            sh = (bs, C, B)
+            spot_verify(self.tokens, self.parent, self.ids.view(sh), self.zmax.view(sh),
+                        self.lse.view(sh), self.cfg["mask_token_id"], self.tau, self.spot_slots,
+                        self.spot_tokens, self.spot_state, self.vflags, temperature=self.T,
+                        gap=self.gap.view(sh))
+            return
         if self.verify_mode is None:
             return
-        bs = self.cfg["bs"]
         if self.K:
             verify_branches(self.proposal, self.target_br, self.out_tokens, self.tau,
                             self.branch, self.vflags, self.vws_br)

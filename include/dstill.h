@@ -308,6 +308,34 @@ int dstill_verify_branches(int32_t bs, int32_t K, int32_t gamma, int32_t vocab,
                            int32_t *out_branch, uint32_t *out_flags, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* ---- SPOT: state-equality verification over a draft tree ------------------
+ * SPOT page, section 4 (problem setting; state-equality verification; the
+ * coupled-noise match).  A block state is L slots, each a token or mask_id.
+ * State 0 of each sequence is the root, states 1..n_states-1 are drafts with
+ * parent[b][j] the index of an earlier state.  For every state the caller
+ * supplies the target's per-slot head outputs over all L slots (the
+ * multi-copy layout with the shared-Gumbel head: ids [bs][n_states][L] =
+ * argmax(z/T + G_slot), zmax and lse [bs][n_states][L] at temperature T,
+ * gap [bs][n_states][L] or NULL).  A state commits at its masked slot of
+ * largest confidence zmax/T - lse (fp64; ties to the lowest slot) the id of
+ * that slot; a state with no masked slot commits nothing.  Draft j is
+ * accepted iff its parent is accepted and state j equals the parent's state
+ * with the parent's commit filled in.  The path from the root follows the
+ * lowest accepted child; the round emits the commit of every state on it,
+ * the deepest included.
+ * Outputs (device): out_n [bs] commits emitted; out_slots, out_tokens
+ * [bs][n_states] (slot, token) in order, -1 after out_n; out_state [bs] the
+ * deepest accepted state; out_flags [bs]: DSTILL_FLAG_NEAR_TIE_TARGET when a
+ * state on the path has its two best confidences within 1e-5,
+ * DSTILL_FLAG_NEAR_TIE_SAMPLE when a commit on it has a head gap below 1e-5.
+ * Errors: ESHAPE unless 1 <= n_states, L <= 64; EINVAL on null pointers or
+ * temperature <= 0. */
+int dstill_spot_verify(int32_t bs, int32_t n_states, int32_t L, int32_t mask_id,
+                       float temperature, const int32_t *states, const int32_t *parent,
+                       const int32_t *ids, const float *zmax, const float *lse, const float *gap,
+                       int32_t *out_n, int32_t *out_slots, int32_t *out_tokens,
+                       int32_t *out_state, uint32_t *out_flags, void *stream);
+
 /* Message for the last non-zero status returned on this thread. */
 const char *dstill_last_error(void);
 /* Library ABI version (major * 100 + minor). */

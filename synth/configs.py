@@ -50,10 +50,11 @@ WORKLOADS = {
         lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
         target_dtype="f32", seed=0,
     ),
-    # Multi-copy verify shape: root block + 8 draft copies of 16 positions
-    # behind a 4096-token prefix, copy-local attention, shared-Gumbel argmax.
+    # Multi-copy verify shape: root block + 8 drafted states of 16 positions
+    # behind a 4096-token prefix, copy-local attention, shared-Gumbel argmax,
+    # state-equality verification of the draft tree.
     "q8b_multicopy": dict(
-        _Q8B, bs=1, ctx=[4096], n_copies=9, verify="none",
+        _Q8B, bs=1, ctx=[4096], n_copies=9, verify="spot",
         lm_mode="shared_gumbel", temperature=1.0, target_logit_std=2.0,
         target_dtype="f32", seed=0,
     ),

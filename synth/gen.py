@@ -138,6 +138,31 @@ def block_tokens(cfg: dict, device="cpu", seed=None):
     return tok
 
 
+def draft_tree(cfg: dict, device="cpu", seed=None):
+    """A root block state and n_copies - 1 drafted states for the multi-copy
+    layout: tokens [bs, n_copies, B] int32 (state 0 = anchor + masks) and
+    parent [bs, n_copies] int32 (-1 for the root).  Draft j extends a random
+    earlier state by one random token at one of its masked slots."""
+    s = cfg["seed"] if seed is None else seed
+    bs, C, B, V = cfg["bs"], cfg["n_copies"], cfg["block"], cfg["vocab"]
+    mask = cfg["mask_token_id"]
+    g = _gen("cpu", s, "draft_tree")
+    tok = torch.full((bs, C, B), mask, dtype=torch.int32)
+    par = torch.full((bs, C), -1, dtype=torch.int32)
+    for b in range(bs):
+        tok[b, 0, 0] = int(torch.randint(0, V - 1, (1,), generator=g))
+        for j in range(1, C):
+            p = int(torch.randint(0, j, (1,), generator=g))
+            st = tok[b, p].clone()
+            m = (st == mask).nonzero().flatten()
+            if m.numel():
+                k = int(m[int(torch.randint(0, m.numel(), (1,), generator=g))])
+                st[k] = int(torch.randint(0, V - 1, (1,), generator=g))
+            tok[b, j] = st
+            par[b, j] = p
+    return tok.to(device), par.to(device)
+
+
 def kv_cache(cfg: dict, cap: int, device="cpu", seed=None, name="kv"):
     """Synthetic per-layer K/V caches [bs, h_kv, cap, dh], N(0, 1), in the
     workload dtype (stands in for an injected context when a test exercises
