@@ -190,14 +190,18 @@ def main():
         taus = cyc.tau.cpu().numpy().tolist()
 
     # per-call timing (same stream, events around each library call)
-    names = ["inject", "draft", "head"] + (["loop"] if cyc.K else []) + ["verify"]
+    if cyc.RK:
+        names = ["inject", "refine", "verify"]
+    else:
+        names = ["inject", "draft", "head"] + (["loop"] if cyc.K else []) + ["verify"]
     evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] for n in names}
     tau_hist = []
     for i in range(args.steps):
         c = args.warmup + args.steps + i
         calls = {"inject": cyc.inject, "draft": cyc.draft, "head": lambda: cyc.head(c),
-                 "loop": lambda: cyc.loop(c), "verify": lambda: cyc.verify(c)}
+                 "loop": lambda: cyc.loop(c), "verify": lambda: cyc.verify(c),
+                 "refine": lambda: cyc.refine(c)}
         for n in names:
             fn = calls[n]
             evs[n][i][0].record(st)
@@ -220,13 +224,27 @@ def main():
         alg["loop"] = dict(bytes=alg2["draft"]["bytes"] + alg2["head"]["bytes"],
                            flops=alg2["draft"]["flops"] + alg2["head"]["flops"])
         alg["verify"] = dict(bytes=alg["verify"]["bytes"] * cyc.K, flops=0)
+    if cyc.RK:
+        # K passes of the drafter and the head
+        alg["refine"] = dict(bytes=cyc.RK * (alg["draft"]["bytes"] + alg["head"]["bytes"]),
+                             flops=cyc.RK * (alg["draft"]["flops"] + alg["head"]["flops"]))
     cycles_per_s = 1000.0 / ms_step
     bs = cfg["bs"]
     tokens_per_s = cycles_per_s * bs * tau_mean if tau_mean else None
-    total_bytes = sum(v["bytes"] for v in alg.values())
+    total_bytes = sum(alg[n]["bytes"] for n in names)
     hbm_gbs = total_bytes / (ms_step * 1e-3) / 1e9
 
-    # roofline of the LM-head call (one main kernel plus a small merge)
+    # roofline of the LM-head call (one main kernel plus a small merge); in
+    # the refinement rollout the head runs inside each pass and is timed once
+    # on its own here
+    if "head" not in per_call:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(args.steps):
+            cyc.head(0)
+        e1.record(st)
+        torch.cuda.synchronize()
+        per_call["head"] = e0.elapsed_time(e1) / args.steps
     head_s = per_call["head"] * 1e-3
     head_bound = "mfma" if alg["head"]["flops"] / alg["head"]["bytes"] > \
         MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
@@ -304,7 +322,8 @@ def main():
         "config": {"workload": args.workload, "batch": bs, "block": cfg["block"],
                    "gamma": cfg["gamma"], "ctx": cfg["ctx"] if isinstance(cfg["ctx"], str)
                    else cfg["ctx_lens"], "verify": cfg["verify"], "head": cfg["lm_mode"],
-                   "n_new_per_cycle": cyc.n_new, **({"dloop_k": cyc.K} if cyc.K else {})},
+                   "n_new_per_cycle": cyc.n_new, **({"dloop_k": cyc.K} if cyc.K else {}),
+                   **({"refine_k": cyc.RK} if cyc.RK else {})},
         "tokens_per_s": round(tokens_per_s, 1) if tokens_per_s else None,
         "tau_mean": tau_mean,
         "hbm_gbs": round(hbm_gbs, 1),

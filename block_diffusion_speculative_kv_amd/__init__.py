@@ -24,7 +24,7 @@ __all__ = [
     "FLAG_NEAR_THRESHOLD", "FLAG_NEAR_TIE_SAMPLE", "FLAG_ZERO_RESIDUAL", "FLAG_BAD_INPUT",
     "FLAG_CTX_CLAMPED", "NEAR",
     "dloop_branches", "dloop_merge", "verify_branches", "verify_branches_workspace_bytes",
-    "spot_verify",
+    "spot_verify", "refine_commit",
 ]
 
 _DT = {"f32": F32, "bf16": BF16}
@@ -267,3 +267,15 @@ def spot_verify(states, parent, ids, zmax, lse, mask_id: int, out_n, out_slots, 
                                       _ptr(out_n), _ptr(out_slots), _ptr(out_tokens),
                                       _ptr(out_state), _ptr(out_flags), _stream(stream)),
                "dstill_spot_verify")
+
+
+# ---- multi-step refinement ----------------------------------------------------------
+def refine_commit(ids, zmax, lse, t: int, K: int, tokens, kappa, stream=None):
+    """ids / zmax / lse [bs, block-1] of pass t of K; tokens, kappa [bs, block]
+    int32, updated in place."""
+    lib = _lib.load()
+    _dev_check(ids, zmax, lse, tokens, kappa)
+    bs, B = tokens.shape
+    _lib.check(lib.dstill_refine_commit(bs, B, int(t), int(K), _ptr(ids), _ptr(zmax), _ptr(lse),
+                                        _ptr(tokens), _ptr(kappa), _stream(stream)),
+               "dstill_refine_commit")

@@ -33,7 +33,7 @@ EXPORTS = [
     "dstill_inject_kv", "dstill_block_draft", "dstill_lm_head_argmax",
     "dstill_verify_workspace_bytes", "dstill_verify", "dstill_dloop_branches",
     "dstill_dloop_merge", "dstill_verify_branches_workspace_bytes", "dstill_verify_branches",
-    "dstill_spot_verify", "dstill_last_error", "dstill_version",
+    "dstill_spot_verify", "dstill_refine_commit", "dstill_last_error", "dstill_version",
 ]
 
 
@@ -102,6 +102,7 @@ def _declare(lib):
                                    c_int32),
         "dstill_spot_verify": ([i32, i32, i32, i32, c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, vp, vp], c_int32),
+        "dstill_refine_commit": ([i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], c_int32),
         "dstill_last_error": ([], ctypes.c_char_p),
         "dstill_version": ([], c_int32),
     }

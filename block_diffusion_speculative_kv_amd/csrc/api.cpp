@@ -612,4 +612,19 @@ int dstill_spot_verify(int32_t bs, int32_t n_states, int32_t L, int32_t mask_id,
   return hip_check("spot_verify launch");
 }
 
+int dstill_refine_commit(int32_t bs, int32_t block, int32_t t, int32_t K, const int32_t *ids,
+                         const float *zmax, const float *lse, int32_t *tokens, int32_t *kappa,
+                         void *stream) {
+  if (bs < 0 || block < 2 || block > 64 || K < 1 || t < 1 || t > K)
+    return fail(DSTILL_ESHAPE, "need bs >= 0, 2 <= block <= 64, 1 <= t <= K");
+  if (bs == 0) return DSTILL_OK;
+  if (!ids || !zmax || !lse || !tokens || !kappa)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  RefineArgs a;
+  a.bs = bs; a.block = block; a.t = t; a.K = K;
+  a.ids = ids; a.zmax = zmax; a.lse = lse; a.tokens = tokens; a.kappa = kappa;
+  launch_refine_commit(a, (hipStream_t)stream);
+  return hip_check("refine_commit launch");
+}
+
 }  // extern "C"

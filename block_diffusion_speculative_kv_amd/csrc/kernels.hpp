@@ -168,4 +168,13 @@ struct SpotArgs {
 };
 void launch_spot_verify(const SpotArgs &a, hipStream_t st);
 
+// ---- multi-step refinement (refine.hip) ------------------------------------------
+struct RefineArgs {
+  int bs, block, t, K;
+  const int32_t *ids;       // [bs, block - 1] greedy ids of slots 1..block-1
+  const float *zmax, *lse;  // [bs, block - 1]
+  int32_t *tokens, *kappa;  // [bs, block], updated in place
+};
+void launch_refine_commit(const RefineArgs &a, hipStream_t st);
+
 }  // namespace dstill

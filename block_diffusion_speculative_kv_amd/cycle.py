@@ -18,6 +18,10 @@ re-drafted as K copies of the block (branch set-up, block_draft, head,
 prefix/suffix merge), and the K branches are verified jointly, each against
 its own synthetic target rows.
 
+With refine_k = K > 0 (DStill, multi-step drafting) the draft and head run
+K times per cycle on the evolving block state, each pass committing its most
+confident masked positions (refine_commit); the endpoint is then verified.
+
 The context cache is filled once by injecting every context row (prefill),
 in chunks.  In steady state each cycle re-injects the n_new most recent
 context positions of every sequence (the same slots every cycle), so every
@@ -32,8 +36,8 @@ import torch
 
 from synth import gen
 
-from . import (Drafter, dloop_branches, dloop_merge, spot_verify, verify, verify_branches,
-               verify_branches_workspace_bytes, verify_workspace_bytes)
+from . import (Drafter, dloop_branches, dloop_merge, refine_commit, spot_verify, verify,
+               verify_branches, verify_branches_workspace_bytes, verify_workspace_bytes)
 from ._lib import HEAD_ARGMAX, HEAD_GUMBEL, HEAD_SHARED_GUMBEL, VERIFY_GREEDY, VERIFY_RS
 
 _HEAD_MODE = {"argmax": HEAD_ARGMAX, "gumbel": HEAD_GUMBEL, "shared_gumbel": HEAD_SHARED_GUMBEL}
@@ -112,6 +116,14 @@ class Cycle:
             self.vflags = torch.empty(bs, dtype=torch.int32, device=self.dev)
             self.vws = torch.empty(verify_workspace_bytes(bs, self.gamma, cfg["vocab"]),
                                    dtype=torch.uint8, device=self.dev)
+        self.RK = int(cfg.get("refine_k", 0))
+        if self.RK:
+            self.rtok0 = self.tokens.view(bs, B).clone()
+            self.rtok = self.rtok0.clone()
+            self.rkap0 = torch.full((bs, B), -1, dtype=torch.int32, device=self.dev)
+            self.rkap0[:, 0] = 0
+            self.rkap = self.rkap0.clone()
+            self.rids = torch.empty((bs, self.gamma), dtype=torch.int32, device=self.dev)
         if self.K:
             K, g, i32 = self.K, self.gamma, torch.int32
             self.anchor = self.tokens[:, 0, 0].contiguous()
@@ -152,6 +164,20 @@ class Cycle:
                                cycle=cycle, zmax=self.zmax, lse=self.lse, zsel=self.zsel,
                                gap=self.gap, logits=self.logits)
 
+    def refine(self, cycle: int):
+        """K drafter passes over the evolving block state, each followed by
+        the head and the commit of its most confident positions."""
+        bs, g, B = self.cfg["bs"], self.gamma, self.cfg["block"]
+        self.rtok.copy_(self.rtok0)
+        self.rkap.copy_(self.rkap0)
+        for t in range(1, self.RK + 1):
+            self.dr.block_draft(self.rtok.view(bs, 1, B), self.ctx_len, self.max_ctx, self.kv,
+                                self.hidden, self.ws, flags=self.draft_flags)
+            self.head(cycle)
+            refine_commit(self.ids.view(bs, g), self.zmax.view(bs, g), self.lse.view(bs, g), t,
+                          self.RK, self.rtok, self.rkap)
+        self.rids.copy_(self.rtok[:, 1:])
+
     def loop(self, cycle: int):
         """D-Loop second pass: branches, K-copy draft, head, merge."""
         if not self.K:
@@ -183,7 +209,8 @@ class Cycle:
             verify_branches(self.proposal, self.target_br, self.out_tokens, self.tau,
                             self.branch, self.vflags, self.vws_br)
             return
-        verify(self.verify_mode, self.ids.view(bs, self.gamma), self.target, self.out_tokens,
+        ids = self.rids if self.RK else self.ids.view(bs, self.gamma)
+        verify(self.verify_mode, ids, self.target, self.out_tokens,
                self.tau, self.vflags, self.vws, temperature=self.T, seed=self.seed, cycle=cycle,
                draft_lse=self.lse.view(bs, self.gamma) if self.logits is not None else None,
                draft_logits=(self.logits.view(bs, self.gamma, -1)
@@ -191,7 +218,10 @@ class Cycle:
 
     def step(self, cycle: int = 0):
         self.inject()
-        self.draft()
-        self.head(cycle)
-        self.loop(cycle)
+        if self.RK:
+            self.refine(cycle)
+        else:
+            self.draft()
+            self.head(cycle)
+            self.loop(cycle)
         self.verify(cycle)

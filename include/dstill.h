@@ -336,6 +336,21 @@ int dstill_spot_verify(int32_t bs, int32_t n_states, int32_t L, int32_t mask_id,
                        int32_t *out_n, int32_t *out_slots, int32_t *out_tokens,
                        int32_t *out_state, uint32_t *out_flags, void *stream);
 
+/* ---- DStill multi-step refinement: one commit pass --------------------------
+ * DStill page, "Multi-step drafting" and the teacher rollout of its appendix.
+ * Between drafter passes over a block state tokens [bs][block] (slot 0 the
+ * anchor), with kappa [bs][block] the commit pass of each slot (0 for the
+ * anchor, -1 while masked): given the head's greedy ids, zmax and lse of
+ * slots 1..block-1 on pass t of K ([bs][block-1], device), the
+ * n_t = ceil(masked / (K - t + 1)) masked slots of largest confidence
+ * max_v softmax(z) (ranked as zmax - lse in fp64, ties to the lower slot)
+ * take their ids and kappa = t.  Pass t = K commits every remaining slot.
+ * tokens and kappa are updated in place (device).
+ * Errors: ESHAPE unless 2 <= block <= 64 and 1 <= t <= K; EINVAL on nulls. */
+int dstill_refine_commit(int32_t bs, int32_t block, int32_t t, int32_t K, const int32_t *ids,
+                         const float *zmax, const float *lse, int32_t *tokens, int32_t *kappa,
+                         void *stream);
+
 /* Message for the last non-zero status returned on this thread. */
 const char *dstill_last_error(void);
 /* Library ABI version (major * 100 + minor). */

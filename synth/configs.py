@@ -66,6 +66,14 @@ WORKLOADS = {
         lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
         target_dtype="f32", seed=0, dloop_k=4,
     ),
+    # DStill multi-step refinement (the teacher rollout): 8 drafter passes per
+    # block on the bs-1 greedy workload, each committing its most confident
+    # positions, then greedy verification of the endpoint.
+    "q8b_refine_k8": dict(
+        _Q8B, bs=1, ctx=[4096], n_copies=1, verify="greedy",
+        lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
+        target_dtype="f32", seed=0, refine_k=8,
+    ),
 }
 
 # Order used when a workload is referred to by index (0 = the tiny case).
