@@ -158,8 +158,13 @@ class Drafter:
             k = k.reshape(C, B, self.hkv, self.dh)
             v = v.reshape(C, B, self.hkv, self.dh)
             out = np.empty((C, B, self.hq, self.dh))
-            ck = _f64(ctx_k[li])[:, :S]
-            cv = _f64(ctx_v[li])[:, :S]
+            # sliding window (DStill appendix drafter table, SWA layers): the
+            # block sees the last W context positions; full layers see all
+            W = int(self.cfg.get("swa_window", 0))
+            full = (int(self.cfg.get("full_attn_mask", 0)) >> li) & 1
+            lo = max(0, S - W) if W > 0 and not full else 0
+            ck = _f64(ctx_k[li])[:, lo:S]
+            cv = _f64(ctx_v[li])[:, lo:S]
             for c in range(C):
                 for j in range(self.hq):
                     g = j // group

@@ -291,3 +291,42 @@ def test_lm_head_pins():
     W2[2] = W2[4] = [1, 0]
     o2 = od.lm_head(W2, np.array([[1.0, 0.0]]))
     assert o2["ids"][0] == 2 and o2["gap"][0] == 0.0
+
+
+@pytest.mark.parametrize("S,W", [(20, 6), (20, 19), (5, 8)])
+def test_sliding_window_matches_explicit_mask(S, W):
+    """The windowed layer's attention equals SDPA over [context; block] with
+    the mask that lets the block see context positions [S - W, S) and itself;
+    a layer whose full-attention bit is set, and a window of at least S, give
+    the unwindowed result."""
+    cfg = _tiny(n_layers=2, swa_window=W, full_attn_mask=0b10)
+    m, w = _model(cfg)
+    rng = np.random.default_rng(11)
+    feats = rng.normal(0, 1, (S, cfg["feat_dim"]))
+    ks, vs = m.inject_rows(feats, np.arange(S))
+    ck = [k.transpose(1, 0, 2) for k in ks]
+    cv = [v.transpose(1, 0, 2) for v in vs]
+    B = cfg["block"]
+    tok = np.array([[4] + [cfg["mask_token_id"]] * (B - 1)])
+    tr = []
+    m.draft(ck, cv, tok, S, trace=tr)
+    hq, dh = cfg["n_q_heads"], cfg["head_dim"]
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    for li in (0, 1):
+        q = tr[li]["q"][0]
+        kk = np.concatenate([ks[li], tr[li]["k"][0]], 0)
+        vv = np.concatenate([vs[li], tr[li]["v"][0]], 0)
+        mask = np.zeros((B, S + B), dtype=bool)
+        lo = max(0, S - W) if li == 0 else 0
+        mask[:, lo:S] = True
+        mask[:, S:] = True
+        o = F.scaled_dot_product_attention(T(q.transpose(1, 0, 2))[None],
+                                           T(kk.transpose(1, 0, 2))[None],
+                                           T(vv.transpose(1, 0, 2))[None],
+                                           attn_mask=T(mask)[None, None], enable_gqa=True)
+        o = o[0].transpose(0, 1).reshape(B, hq * dh).numpy()
+        assert np.allclose(o, tr[li]["attn"], atol=1e-12)
+    if W >= S:
+        full = _tiny(n_layers=2)
+        mf, _ = _model(full)
+        assert np.allclose(mf.draft(ck, cv, tok, S), m.draft(ck, cv, tok, S), atol=1e-13)
