@@ -67,7 +67,9 @@ class Drafter:
             vocab=cfg["vocab"], n_feat_layers=cfg["n_feat_layers"],
             target_hidden=cfg["target_hidden"], max_block=cfg["block"],
             mask_token_id=cfg["mask_token_id"], qk_norm=int(cfg["qk_norm"]), dtype=self.dtype,
-            rms_eps=float(cfg["rms_eps"]), rope_theta=float(cfg["rope_theta"]))
+            rms_eps=float(cfg["rms_eps"]), rope_theta=float(cfg["rope_theta"]),
+            swa_window=int(cfg.get("swa_window", 0)),
+            full_attn_mask=int(cfg.get("full_attn_mask", 0)))
         self._cfg_c = c
         L = len(weights["layers"])
         self._layers = (_lib.LayerWeights * L)()

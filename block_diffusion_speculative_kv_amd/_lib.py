@@ -41,7 +41,8 @@ class Config(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "mlp", "vocab",
         "n_feat_layers", "target_hidden", "max_block", "mask_token_id", "qk_norm", "dtype")] + [
-        ("rms_eps", c_float), ("rope_theta", c_float)]
+        ("rms_eps", c_float), ("rope_theta", c_float), ("swa_window", c_int32),
+        ("full_attn_mask", c_uint32)]
 
 
 class LayerWeights(ctypes.Structure):

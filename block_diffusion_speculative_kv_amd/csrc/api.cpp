@@ -180,6 +180,7 @@ int check_config(const dstill_config *c) {
   if (c->n_q_heads % c->n_kv_heads)
     return fail(DSTILL_ESHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", c->n_q_heads,
                 c->n_kv_heads);
+  if (c->swa_window < 0) return fail(DSTILL_ESHAPE, "swa_window %d < 0", c->swa_window);
   if (c->n_q_heads / c->n_kv_heads > 16)
     return fail(DSTILL_EUNSUPPORTED, "GQA group %d exceeds 16", c->n_q_heads / c->n_kv_heads);
   if (c->max_block < 1 || c->max_block > 16)
@@ -399,6 +400,7 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
                     w.eff_ctx, n_copies * block, block, L.q_norm, L.k_norm, c.qk_norm, c.rms_eps,
                     w.rope, w.q, w.kb, w.vb, st);
     a.kc = kv->k[l]; a.vc = kv->v[l];
+    a.window = c.swa_window > 0 && !((c.full_attn_mask >> l) & 1u) ? c.swa_window : 0;
     launch_attention(a, st);
     // O projection, then h += o and the pre-MLP norm
     g.X = w.attn; g.ldx = qd; g.W = L.wo; g.ldw = qd; g.N = d; g.K = qd;

@@ -177,6 +177,16 @@ __device__ __forceinline__ void split_coords(const AttnArgs &a, int *sp, int *h,
   *bc = (L % pairs) / a.hkv;
 }
 
+// Context range of a sequence under the sliding window: the first visible
+// key, and the chunk-aligned start the splits count from (the V cache is
+// tiled in 64-key tiles); keys between the two are masked in the first chunk.
+__device__ __forceinline__ int ctx_first(int S, int window) {
+  return window > 0 && S > window ? S - window : 0;
+}
+__device__ __forceinline__ int ctx_lo(int S, int window) {
+  return ctx_first(S, window) & ~(ATT_KC - 1);
+}
+
 // Counting sort of the items by decreasing number of 64-key context chunks
 // (split 0 counts one more for the block keys; empty splits go last).  One
 // workgroup; the order within a count is whatever the atomics give, which
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(1024) void attn_worklist_kernel(AttnArgs a, int *__
   auto count = [&](int L) {
     const int sp = L / pairs, bc = (L % pairs) / a.hkv;
     const int S = a.eff_ctx[bc / a.C];
-    const int k0 = sp * a.split, k1 = min(k0 + a.split, S);
+    const int k0 = ctx_lo(S, a.window) + sp * a.split, k1 = min(k0 + a.split, S);
     const int c = k1 > k0 ? (k1 - k0 + ATT_KC - 1) / ATT_KC : 0;
     return min(c + (sp == 0 ? 1 : 0), NB - 1);
   };
@@ -207,16 +217,17 @@ __global__ __launch_bounds__(1024) void attn_worklist_kernel(AttnArgs a, int *__
   for (int L = threadIdx.x; L < n; L += blockDim.x) list[atomicAdd(&base[count(L)], 1)] = L;
 }
 
-// One wave's pass over a staged chunk holding `nk` valid keys (1..64), with
-// one online-softmax update for the whole chunk.  Scores stay in raw units
+// One wave's pass over a staged chunk holding valid keys kf..nk-1 (nk in
+// 1..64; kf > 0 only in the first chunk under a sliding window, with at least
+// one valid key), with one online-softmax update for the whole chunk.  Scores stay in raw units
 // (m is the reference max of raw scores); probabilities are
 // exp2(s * c - m * c) with c = log2(e) / sqrt(dh), one FMA and one v_exp_f32
 // each.
 template <typename T, int DH, class Lay>
 __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
                                              const T *__restrict__ vt_lds,
-                                             const typename Mma<T>::frag *qf, int nk, float c,
-                                             WaveState<T, DH> &ws) {
+                                             const typename Mma<T>::frag *qf, int nk, int kf,
+                                             float c, WaveState<T, DH> &ws) {
   constexpr int VEC = Mma<T>::VEC, KW = Mma<T>::KW;
   typedef typename Mma<T>::frag F;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -236,12 +247,14 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
                            qf[ks], s[t]);
     }
   }
-  if (nk < ATT_KC) {
+  if (nk < ATT_KC || kf > 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (32 * (t >> 1) + 8 * g + 4 * (t & 1) + i >= nk) s[t][i] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int key = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i;
+        if (key >= nk || key < kf) s[t][i] = -INFINITY;
+      }
   }
   float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -292,12 +305,13 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
 }
 
 // One wave's pass over the 32-key sub-chunk `sub` of a staged chunk, of which
-// the first nk (1..32) keys are valid: two S^T tiles, one online-softmax
+// keys kf..nk-1 (nk in 1..32; kf > 0 only under a sliding window) are valid: two S^T tiles, one online-softmax
 // update, one P.V pass (same lane layout as attend_chunk).
 template <int DH, class Lay>
 __device__ __forceinline__ void attend_sub(const bf16 *__restrict__ ks_lds,
                                            const bf16 *__restrict__ vt_lds, const bf16x8 *qf,
-                                           int sub, int nk, float c, WaveState<bf16, DH> &ws) {
+                                           int sub, int nk, int kf, float c,
+                                           WaveState<bf16, DH> &ws) {
   typedef bf16x8 F;
   constexpr int KW = 32;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -311,12 +325,14 @@ __device__ __forceinline__ void attend_sub(const bf16 *__restrict__ ks_lds,
       s[t] = Mma<bf16>::run(*reinterpret_cast<const F *>(Lay::k(ks_lds, krow, ks * KW + 8 * g)),
                             qf[ks], s[t]);
   }
-  if (nk < 32) {
+  if (nk < 32 || kf > 0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (8 * g + 4 * t + i >= nk) s[t][i] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int key = 8 * g + 4 * t + i;
+        if (key >= nk || key < kf) s[t][i] = -INFINITY;
+      }
   }
   float cmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -350,7 +366,8 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   split_coords(a, &sp, &h, &bc);
   const int b = bc / a.C;
   const int S = a.eff_ctx[b];
-  const int k_beg = sp * a.split;
+  const int s_lo = ctx_lo(S, a.window), kf0 = ctx_first(S, a.window) - s_lo;
+  const int k_beg = s_lo + sp * a.split;
   if (sp > 0 && k_beg >= S) return;
   const int k_end = min(k_beg + a.split, S);
   const int group = a.hq / a.hkv;
@@ -397,7 +414,9 @@ __global__ __launch_bounds__(NTHR) void attn_split_kernel(AttnArgs a) {
   for (int c = 0; c < nchunk; ++c) {
     const int cur = c & 1;
     if (c + 1 < nchunk) issue(c + 1);
-    if (active) attend_chunk<T, DH, PadLayout<T, DH>>(sm.k[cur], sm.vt[cur], qf, nk, c_log2, st);
+    // the window's first visible key lies in context chunk 0 of split 0
+    const int kf = (sp == 0 && c == 0 && c < nctx) ? kf0 : 0;
+    if (active) attend_chunk<T, DH, PadLayout<T, DH>>(sm.k[cur], sm.vt[cur], qf, nk, kf, c_log2, st);
     if (c + 1 < nchunk) {
       nk = ld.nk;
       ld.store(sm, cur ^ 1);
@@ -459,7 +478,8 @@ __global__ __launch_bounds__(NTHR) void attn_split_dma_kernel(AttnArgs a) {
   split_coords(a, &sp, &h, &bc);
   const int b = bc / a.C;
   const int S = a.eff_ctx[b];
-  const int k_beg = sp * a.split;
+  const int s_lo = ctx_lo(S, a.window), kf0 = ctx_first(S, a.window) - s_lo;
+  const int k_beg = s_lo + sp * a.split;
   if (sp > 0 && k_beg >= S) return;
   const int k_end = min(k_beg + a.split, S);
   const int group = a.hq / a.hkv;
@@ -542,9 +562,9 @@ __global__ __launch_bounds__(NTHR) void attn_split_dma_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (KSPLIT == 1) {
-      if (active) attend_chunk<T, DH, Lay>(sm.k[BS], sm.vt[BS], qf, a.B, c_log2, st);
+      if (active) attend_chunk<T, DH, Lay>(sm.k[BS], sm.vt[BS], qf, a.B, 0, c_log2, st);
     } else if (kset == 0) {  // B <= 16 keys: all in the first sub-chunk
-      attend_sub<DH, Lay>(sm.k[BS], sm.vt[BS], qf, 0, a.B, c_log2, st);
+      attend_sub<DH, Lay>(sm.k[BS], sm.vt[BS], qf, 0, a.B, 0, c_log2, st);
     }
   }
 
@@ -573,11 +593,16 @@ __global__ __launch_bounds__(NTHR) void attn_split_dma_kernel(AttnArgs a) {
       __syncthreads();
     }
     if (c + ATT_NS - 1 < nctx) issue(c + ATT_NS - 1);
+    // the window's first visible key lies in chunk 0 of split 0; split 0 has
+    // taken its block keys already, so a wave set whose sub-chunk is wholly
+    // below the window keeps a finite reference
+    const int kf = (sp == 0 && c == 0) ? kf0 : 0;
     if (KSPLIT == 1) {
-      if (active) attend_chunk<T, DH, Lay>(sm.k[slot], sm.vt[slot], qf, nk, c_log2, st);
+      if (active) attend_chunk<T, DH, Lay>(sm.k[slot], sm.vt[slot], qf, nk, kf, c_log2, st);
     } else if (active) {
       const int nks = min(32, nk - 32 * kset);
-      if (nks > 0) attend_sub<DH, Lay>(sm.k[slot], sm.vt[slot], qf, kset, nks, c_log2, st);
+      if (nks > 0)
+        attend_sub<DH, Lay>(sm.k[slot], sm.vt[slot], qf, kset, nks, kf - 32 * kset, c_log2, st);
     }
   }
   if constexpr (KSPLIT == 2) {
@@ -655,7 +680,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int d = (threadIdx.x % per_row) * 4;
   if (s >= a.B) return;
   const int b = bc / a.C;
-  const int S = a.eff_ctx[b];
+  const int S = a.eff_ctx[b] - ctx_lo(a.eff_ctx[b], a.window);  // keys from the first split
   const int nvalid = max(1, (S + a.split - 1) / a.split);
   const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B + s;  // record of split sp: rec0 + sp*B
   // splits in groups of 8 with predicated loads, so a group's loads are in

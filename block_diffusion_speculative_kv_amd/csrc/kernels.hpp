@@ -90,6 +90,9 @@ struct AttnArgs {
   float *mlpart;       // [bs*C][hq][nsplit][B][2]  (running max in log2 units, sum)
   void *out;           // [bs*C*B, hq*dh]
   const int *worklist = nullptr;  // optional [nsplit * hkv * bs*C] item order
+  // Sliding window over the context: the block sees context positions
+  // [S - window, S) (all of [0, S) when window is 0 or S <= window).
+  int window = 0;
 };
 // Item order for launch_attention, longest first (one small kernel; depends
 // only on eff_ctx and the split plan, so one list serves every layer).

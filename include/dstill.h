@@ -113,6 +113,14 @@ typedef struct {
   int32_t qk_norm;                       /* 1 = per-head q/k RMSNorm        */
   int32_t dtype;                         /* DSTILL_F32 or DSTILL_BF16       */
   float rms_eps, rope_theta;
+  /* Sliding-window drafter attention (DStill appendix drafter table: SWA of
+   * 2048 on the Gemma and Nemotron drafters, "SWA + 1 Full" on one).  With
+   * swa_window = W > 0 the block of a sequence with context length S sees
+   * the context positions [max(0, S - W), S) and the whole block; layers
+   * whose bit is set in full_attn_mask (bit l = layer l) see all of [0, S).
+   * 0 = every layer sees the whole context. */
+  int32_t swa_window;
+  uint32_t full_attn_mask;
 } dstill_config;
 
 /* One draft layer; every tensor has the config dtype.

@@ -141,6 +141,41 @@ def test_small_bf16_head_geometries(hq, hkv, dh):
     assert flags.cpu().tolist() == [0, 0, 0]
 
 
+@pytest.mark.parametrize("W,mask,hq,hkv,dh", [
+    (200, 0b10, 8, 2, 128),   # first visible key inside a chunk (kf 36, 61); layer 1 full
+    (236, 0b00, 8, 2, 128),   # 300 - 236 = 64: a chunk-aligned window start; every layer windowed
+    (1000, 0b01, 8, 2, 128),  # wider than two of the contexts
+    (200, 0b10, 8, 1, 128),   # two wave sets of 8 heads: a set whose first sub-chunk is masked
+    (200, 0b00, 8, 1, 64),    # head_dim 64 through registers
+])
+def test_small_bf16_sliding_window(W, mask, hq, hkv, dh):
+    ctx = [37, 300, 1029]
+    cfg = configs.small_bf16(ctx=ctx, swa_window=W, full_attn_mask=mask, n_q_heads=hq,
+                             n_kv_heads=hkv, head_dim=dh)
+    dev, w, dr, kv = _setup(cfg, 1152)
+    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
+    want = _oracle(cfg, to_np(w), kv, tok, ctx)
+    _compare(cfg, to_np(w), out, want, f"window {W} mask {mask} heads {hq}/{hkv} dh {dh}")
+    assert flags.cpu().tolist() == [0, 0, 0]
+
+
+def test_tiny_fp32_sliding_window():
+    # the fp32 register-staged kernel, first visible key 78 (chunk 64, kf 14)
+    cfg = configs.get("tiny_fp32", swa_window=50)
+    dev, w, dr, kv = _setup(cfg, 128)
+    tok, out, flags = _draft(cfg, dr, kv, dev, cfg["ctx_lens"], 128)
+    want = _oracle(cfg, to_np(w), kv, tok, cfg["ctx_lens"])
+    _compare(cfg, to_np(w), out, want, "tiny window")
+
+
+def test_small_bf16_multicopy_sliding_window():
+    cfg = configs.small_bf16(ctx=[200, 513, 7], n_copies=3, swa_window=150)
+    dev, w, dr, kv = _setup(cfg, 640)
+    tok, out, _ = _draft(cfg, dr, kv, dev, cfg["ctx_lens"], 513)
+    want = _oracle(cfg, to_np(w), kv, tok, cfg["ctx_lens"])
+    _compare(cfg, to_np(w), out, want, "multicopy window")
+
+
 def test_small_bf16_batch32_fused_swiglu():
     # 512 rows and mlp 5632 (352 tiles): the gate|up product runs unsplit,
     # with SwiGLU in its epilogue
