@@ -39,8 +39,11 @@ def _algorithmic(cfg, rows, n_inj):
     R = bs * C * B
     layer_params = (hq + 2 * hkv) * dh * d + d * hq * dh + 2 * m * d + d * m
     ctx = cfg["ctx_lens"]
-    attn_bytes = L * sum((S + B * C) * hkv * dh * 2 * eb for S in ctx)
-    attn_flops = L * sum(C * 4 * B * hq * dh * (S + B) for S in ctx)
+    W, full = int(cfg.get("swa_window", 0)), int(cfg.get("full_attn_mask", 0))
+    # context keys each layer reads: the last W under a sliding window
+    seen = [[min(S, W) if W > 0 and not (full >> l) & 1 else S for S in ctx] for l in range(L)]
+    attn_bytes = sum((S + B * C) * hkv * dh * 2 * eb for sl in seen for S in sl)
+    attn_flops = sum(C * 4 * B * hq * dh * (S + B) for sl in seen for S in sl)
     head_logits = 4 * rows * V if cfg["verify"] == "rs" else 0
     head_bytes = eb * V * d + rows * (eb * d + 16) + head_logits
     head_flops = 2 * rows * V * d
@@ -323,7 +326,8 @@ def main():
                    "gamma": cfg["gamma"], "ctx": cfg["ctx"] if isinstance(cfg["ctx"], str)
                    else cfg["ctx_lens"], "verify": cfg["verify"], "head": cfg["lm_mode"],
                    "n_new_per_cycle": cyc.n_new, **({"dloop_k": cyc.K} if cyc.K else {}),
-                   **({"refine_k": cyc.RK} if cyc.RK else {})},
+                   **({"refine_k": cyc.RK} if cyc.RK else {}),
+                   **({"swa_window": cfg["swa_window"]} if cfg.get("swa_window") else {})},
         "tokens_per_s": round(tokens_per_s, 1) if tokens_per_s else None,
         "tau_mean": tau_mean,
         "hbm_gbs": round(hbm_gbs, 1),

@@ -115,7 +115,7 @@ AttnPlan attn_plan(int max_ctx, int pairs, int ncu) {
 
 // Workspace of one block_draft call.
 struct DraftWs {
-  int32_t *eff_ctx, *tok, *wlist;
+  int32_t *eff_ctx, *tok, *wlist, *wlist_win;
   float *h, *parts, *opart, *mlpart, *ssp, *rope;
   void *u, *q, *kb, *vb, *attn, *act;
 };
@@ -128,6 +128,7 @@ size_t draft_ws(const dstill_config &c, int bs, int C, int B, AttnPlan ap, int n
   w.eff_ctx = cv.take<int32_t>(bs);
   w.tok = cv.take<int32_t>(R);
   w.wlist = cv.take<int32_t>((size_t)ap.nsplit * bs * C * c.n_kv_heads);
+  w.wlist_win = cv.take<int32_t>((size_t)ap.nsplit * bs * C * c.n_kv_heads);  // windowed layers
   w.h = cv.take<float>((size_t)R * d);
   w.ssp = cv.take<float>((size_t)R * ((d + 1023) / 1024));
   w.rope = cv.take<float>((size_t)R * c.head_dim);  // [R][dh/2] (cos, sin)
@@ -388,6 +389,25 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
   a.opart = w.opart; a.mlpart = w.mlpart; a.out = w.attn;
   launch_attention_worklist(a, w.wlist, st);
   a.worklist = w.wlist;
+  // Windowed layers see at most swa_window + 63 keys from the chunk holding
+  // the window's first key: they get a split plan of their own for that
+  // range (no more splits than the full plan, whose records the workspace
+  // holds) and their own work list.
+  AttnArgs aw = a;
+  aw.window = c.swa_window;
+  bool any_window = false;
+  for (int l = 0; l < c.n_layers; ++l)
+    any_window = any_window || (c.swa_window > 0 && !((c.full_attn_mask >> l) & 1u));
+  if (any_window) {
+    const int range = std::min(ctx_limit, c.swa_window + 63);
+    const AttnPlan apw = attn_plan(std::max(1, range), bs * n_copies * c.n_kv_heads, ncu);
+    if (apw.nsplit <= ap.nsplit) {
+      aw.split = apw.split;
+      aw.nsplit = apw.nsplit;
+    }
+    launch_attention_worklist(aw, w.wlist_win, st);
+    aw.worklist = w.wlist_win;
+  }
   for (int l = 0; l < c.n_layers; ++l) {
     const dstill_layer_weights &L = h->layers[l];
     GemmArgs g;
@@ -399,9 +419,10 @@ int dstill_block_draft(const dstill_handle *h, const int32_t *block_tokens,
     launch_qkv_post(c.dtype, w.parts, g.splits, R, c.n_q_heads, c.n_kv_heads, c.head_dim,
                     w.eff_ctx, n_copies * block, block, L.q_norm, L.k_norm, c.qk_norm, c.rms_eps,
                     w.rope, w.q, w.kb, w.vb, st);
-    a.kc = kv->k[l]; a.vc = kv->v[l];
-    a.window = c.swa_window > 0 && !((c.full_attn_mask >> l) & 1u) ? c.swa_window : 0;
-    launch_attention(a, st);
+    const bool windowed = c.swa_window > 0 && !((c.full_attn_mask >> l) & 1u);
+    AttnArgs &al = windowed ? aw : a;
+    al.kc = kv->k[l]; al.vc = kv->v[l];
+    launch_attention(al, st);
     // O projection, then h += o and the pre-MLP norm
     g.X = w.attn; g.ldx = qd; g.W = L.wo; g.ldw = qd; g.N = d; g.K = qd;
     g.splits = gemm_plan_splits(R, d, qd, c.dtype, ncu);

@@ -74,6 +74,13 @@ WORKLOADS = {
         lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
         target_dtype="f32", seed=0, refine_k=8,
     ),
+    # Sliding-window drafter (SWA 2048 in every layer, as on the Gemma and
+    # Nemotron drafters) on the long-context shape: batch 4, context 32768.
+    "q8b_swa_long": dict(
+        _Q8B, bs=4, ctx=[32768] * 4, n_copies=1, verify="greedy",
+        lm_mode="argmax", temperature=1.0, target_logit_std=2.0,
+        target_dtype="f32", seed=0, swa_window=2048,
+    ),
 }
 
 # Order used when a workload is referred to by index (0 = the tiny case).
