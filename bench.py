@@ -304,7 +304,11 @@ def main():
         del src, dst
 
     cpu = None
-    if args.cpu_budget > 0:
+    # the oracle baseline times the one-pass cycle (inject, draft, head, greedy
+    # or RS verify); workloads with a second pass, refinement passes or the
+    # multi-copy layout are not that cycle, so they carry no baseline
+    plain = not (cyc.K or cyc.RK or cyc.spot or cyc.mode == 2)
+    if args.cpu_budget > 0 and plain:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = _cpu_baseline(cfg, cyc, args.cpu_budget)
 
