@@ -41,9 +41,10 @@ def _stats(bs, g, seed, dev):
     zmax = gen.normal((bs, g), 3.0, seed=seed, name="zmax", device=dev).float()
     gapl = gen.normal((bs, g), 1.0, seed=seed, name="gapl", device=dev).abs().float()
     lse = zmax + gapl
-    lse[0, 3] = zmax[0, 3]
-    lse[1, 0] = zmax[1, 0]
-    lse[1, 5:9] = zmax[1, 5:9]
+    if g > 8:
+        lse[0, 3] = zmax[0, 3]
+        lse[1, 0] = zmax[1, 0]
+        lse[1, 5:9] = zmax[1, 5:9]
     ids = gen.integers((bs, g), 0, 1000, seed=seed, name="ids", device=dev)
     anchor = gen.integers((bs,), 0, 1000, seed=seed, name="anchor", device=dev)
     return anchor, ids, zmax.contiguous(), lse.contiguous()
@@ -177,3 +178,47 @@ def test_second_pass_end_to_end():
         assert np.array_equal(to_np(merged)[b], want)
     print(f"second pass: {near} near-tie rows excluded; {flips} of {rows2} ids differ from the "
           f"all-oracle chain (bf16 rounding flips)")
+
+
+def test_edges_empty_batch_gamma_one_single_branch():
+    dev = device()
+    # bs = 0: nothing is launched, nothing written
+    z = torch.zeros((0, 3), dtype=torch.float32, device=dev)
+    i0 = torch.zeros((0, 3), dtype=torch.int32, device=dev)
+    blocks = torch.full((0, 2, 4), 7, dtype=torch.int32, device=dev)
+    lens = torch.full((0, 2), 7, dtype=torch.int32, device=dev)
+    bd.dloop_branches(torch.zeros(0, dtype=torch.int32, device=dev), i0, z, z, 2, 9, blocks, lens)
+    # gamma = 1, K = 1: the only length is 0, the block is (anchor, MASK)
+    anchor, ids, zmax, lse = _stats(3, 1, 5, dev)
+    blocks = torch.empty((3, 1, 2), dtype=torch.int32, device=dev)
+    lens = torch.empty((3, 1), dtype=torch.int32, device=dev)
+    bd.dloop_branches(anchor, ids, zmax, lse, 1, 4999, blocks, lens)
+    torch.cuda.synchronize()
+    assert to_np(lens).tolist() == [[0]] * 3
+    assert to_np(blocks)[:, 0, 1].tolist() == [4999] * 3
+    assert to_np(blocks)[:, 0, 0].tolist() == to_np(anchor).tolist()
+    # K larger than gamma is refused before any launch
+    with pytest.raises(bd.DstillError):
+        bd.dloop_branches(anchor, ids, zmax, lse, 2, 4999, torch.empty((3, 2, 2), dtype=torch.int32,
+                          device=dev), torch.empty((3, 2), dtype=torch.int32, device=dev))
+
+
+@pytest.mark.parametrize("K,dtype", [(1, torch.float32), (4, torch.bfloat16)])
+def test_verify_branches_full_vocabulary(K, dtype):
+    # the 8B-shaped drafter's vocabulary and block (gamma 15)
+    dev = device()
+    bs, g, V = 2, 15, 151936
+    y, zt = _branch_targets(bs, K, g, V, dtype, dev, 31)
+    toks = torch.empty((bs, g + 1), dtype=torch.int32, device=dev)
+    tau = torch.empty(bs, dtype=torch.int32, device=dev)
+    br = torch.empty(bs, dtype=torch.int32, device=dev)
+    fl = torch.empty(bs, dtype=torch.int32, device=dev)
+    ws = torch.empty(bd.verify_branches_workspace_bytes(bs, K, g, V), dtype=torch.uint8,
+                     device=dev)
+    bd.verify_branches(y, zt, toks, tau, br, fl, ws)
+    torch.cuda.synchronize()
+    ztn, yn = to_np(zt), to_np(y)
+    for b in range(bs):
+        wt, wtau, wbr, wf = odl.verify_branches_greedy(ztn[b], yn[b])
+        assert (int(tau[b]), int(br[b]), int(fl[b])) == (wtau, wbr, wf)
+        assert to_np(toks)[b][:wtau].tolist() == wt

@@ -159,6 +159,18 @@ def test_small_bf16_sliding_window(W, mask, hq, hkv, dh):
     assert flags.cpu().tolist() == [0, 0, 0]
 
 
+@pytest.mark.parametrize("W", [1, 300])
+def test_small_bf16_window_extremes(W):
+    # a one-key window (only the context's last position is seen); a window
+    # equal to one context (that sequence sees all of it)
+    ctx = [37, 300, 1029]
+    cfg = configs.small_bf16(ctx=ctx, swa_window=W)
+    dev, w, dr, kv = _setup(cfg, 1152)
+    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
+    want = _oracle(cfg, to_np(w), kv, tok, ctx)
+    _compare(cfg, to_np(w), out, want, f"window {W}")
+
+
 def test_tiny_fp32_sliding_window():
     # the fp32 register-staged kernel, first visible key 78 (chunk 64, kf 14)
     cfg = configs.get("tiny_fp32", swa_window=50)

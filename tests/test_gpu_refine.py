@@ -100,3 +100,31 @@ def test_rollout_on_the_drafter():
     torch.cuda.synchronize()
     assert np.array_equal(to_np(tok), t_ref) and np.array_equal(to_np(kap), k_ref)
     assert (to_np(kap) >= 0).all()
+
+
+@pytest.mark.parametrize("B,K", [(2, 1), (64, 5), (64, 63)])
+def test_block_size_edges(B, K):
+    # gamma = 1; the largest block the kernel takes, with few and with B - 1 passes
+    dev = device()
+    rng = np.random.default_rng(B + K)
+    bs, mask = 3, 4999
+    tokens = np.full((bs, B), mask, dtype=np.int64)
+    tokens[:, 0] = 1
+    kappa = np.full((bs, B), -1, dtype=np.int64)
+    kappa[:, 0] = 0
+    tg = torch.tensor(tokens, dtype=torch.int32, device=dev)
+    kg = torch.tensor(kappa, dtype=torch.int32, device=dev)
+    for t in range(1, K + 1):
+        ids = rng.integers(0, 5000, (bs, B - 1))
+        zmax = rng.normal(0, 3, (bs, B - 1)).astype(np.float32)
+        lse = (zmax + np.abs(rng.normal(0, 1, (bs, B - 1)))).astype(np.float32)
+        tt = lambda a, dt: torch.tensor(a, dtype=dt, device=dev)
+        bd.refine_commit(tt(ids, torch.int32), tt(zmax, torch.float32), tt(lse, torch.float32),
+                         t, K, tg, kg)
+        for b in range(bs):
+            tokens[b], kappa[b] = orf.refine_step(tokens[b], kappa[b], ids[b],
+                                                  zmax[b].astype(np.float64),
+                                                  lse[b].astype(np.float64), t, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(tg), tokens) and np.array_equal(to_np(kg), kappa)
+    assert (kappa >= 0).all()

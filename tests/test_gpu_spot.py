@@ -156,3 +156,23 @@ def test_multicopy_layout_end_to_end():
                       to_np(gap).reshape(sh))
     got = _run(states, parent, i_, z_, l_, g_, 1.0, dev)
     _check(states, parent, i_, z_, l_, g_, 1.0, got)
+
+
+@pytest.mark.parametrize("n,L", [(1, 16), (64, 64), (5, 1)])
+def test_tree_size_edges(n, L):
+    # root only; the largest tree and block the kernel takes; a one-slot block
+    dev = device()
+    rng = np.random.default_rng(n * 100 + L)
+    bs = 3
+    ids = rng.integers(0, 5000, (bs, n, L))
+    zmax = rng.normal(0, 3, (bs, n, L)).astype(np.float32)
+    lse = (zmax + np.abs(rng.normal(0, 1, (bs, n, L)))).astype(np.float32)
+    states, parent = [], []
+    for b in range(bs):
+        root = np.full(L, MASK)
+        s_, p_ = _tree(rng, L, n, ids[b], zmax[b], lse[b], 1.0, root)
+        states.append(s_)
+        parent.append(p_)
+    states, parent = np.stack(states), np.stack(parent)
+    got = _run(states, parent, ids, zmax, lse, None, 1.0, dev)
+    _check(states, parent, ids, zmax, lse, None, 1.0, got)
