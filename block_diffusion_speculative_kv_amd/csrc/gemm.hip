@@ -65,10 +65,11 @@ __global__ __launch_bounds__(256) void gemm_nt_partial(const T *__restrict__ X, 
   }
 }
 
-// LDS-tiled path, k in stages of 64.  Below 2048 rows: 128 features x 32 MW
-// rows (MW = 4 from 65 rows, else 1 or 2), 2 x 2 waves, two workgroups per
-// compute unit.  From 2048 rows: 256 x 256, 2 x 4 waves, one workgroup per
-// compute unit: half the bytes copied into LDS per product term.
+// LDS-tiled path, k in stages of 64.  Small: 128 features x 32 MW rows (MW =
+// 4 from 65 rows, else 1 or 2), 2 x 2 waves, two workgroups per compute unit.
+// Big (use_big: from 2048 rows, or from 512 rows on the large products): 256
+// x 256, 2 x 4 waves, one workgroup per compute unit: half the bytes copied
+// into LDS per product term.
 constexpr int LDS_KT = 64;
 template <int MW>
 using SmallTile = TileEngine<2, 2, 4, MW, LDS_KT, 3, 2>;
@@ -78,6 +79,14 @@ static_assert(sizeof(BigTile::Smem) <= 160 * 1024, "one workgroup per CU");
 constexpr int BIG_MIN_ROWS = 2048;
 
 static int lds_mw(int M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
+
+// 256 x 256 tiles from 2048 rows, and from 512 rows for the large products
+// (N K >= 24 Mi elements): measured on the 8B-shaped drafter at 512 and 1024
+// rows, the big tile wins on the QKV (6144 x 4096), gate|up (24576 x 4096)
+// and down (4096 x 12288) products and loses on the 4096 x 4096 one.
+static bool use_big(int M, int N, int K) {
+  return M >= BIG_MIN_ROWS || (M >= 512 && (long)N * K >= (24L << 20));
+}
 
 // Wave rows (groups of 16 MW rows) staged per pass of the partial store: the
 // most that fit the idle rings as a [rows][BN + 4] fp32 tile.
@@ -209,7 +218,7 @@ struct LdsPlan {
 
 static LdsPlan lds_geometry(int M, int N, int K, int ncu) {
   LdsPlan p;
-  p.big = M >= BIG_MIN_ROWS;
+  p.big = use_big(M, N, K);
   p.BN = p.big ? BigTile::BN : SmallTile<4>::BN;
   p.BM = p.big ? BigTile::BM : 32 * lds_mw(M);
   p.nnb = (N + p.BN - 1) / p.BN;
@@ -256,6 +265,9 @@ static void launch_tile(const GemmArgs &a, hipStream_t st) {
 
 bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu) {
   if (!use_lds(K, dtype) || mlp % 64 != 0 || M <= 0 || M >= BIG_MIN_ROWS) return false;
+  // on the big tile (128 features per n-block) one split is what the
+  // unfused product runs with at these sizes too
+  if (use_big(M, 2 * mlp, K)) return mlp % 128 == 0;
   const long tiles = (long)(mlp / 64) * ((M + 32 * lds_mw(M) - 1) / (32 * lds_mw(M)));
   return tiles >= num_cu;
 }
@@ -313,19 +325,24 @@ static void launch_lds(const GemmArgs &a, int nnb, int nmb, int per, int splits,
 
 void launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.swiglu_act) {
-    // fused gate|up + SwiGLU (small tiles only): 64 features (128 weight rows)
-    // per n-block
-    const int mw = lds_mw(a.M), BM = 32 * mw;
-    const int nnb = a.mlp / 64, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
+    // fused gate|up + SwiGLU: BN / 2 features (BN weight rows) per n-block
     bf16 *act = (bf16 *)a.swiglu_act;
+    const int nst = a.K / LDS_KT;
+    if (use_big(a.M, 2 * a.mlp, a.K)) {
+      launch_lds<BigTile>(a, a.mlp / (BigTile::BN / 2), (a.M + BigTile::BM - 1) / BigTile::BM, nst,
+                          1, act, st);
+      return;
+    }
+    const int mw = lds_mw(a.M), BM = 32 * mw;
+    const int nnb = a.mlp / 64, nmb = (a.M + BM - 1) / BM;
     if (mw == 1) launch_lds<SmallTile<1>>(a, nnb, nmb, nst, 1, act, st);
     else if (mw == 2) launch_lds<SmallTile<2>>(a, nnb, nmb, nst, 1, act, st);
     else launch_lds<SmallTile<4>>(a, nnb, nmb, nst, 1, act, st);
     return;
   }
   if (use_lds(a.K, a.dtype)) {
-    // the tile depends on M alone (the plan that chose a.splits used it too)
-    const bool big = a.M >= BIG_MIN_ROWS;
+    // the tile depends on the shape alone (the plan that chose a.splits used it too)
+    const bool big = use_big(a.M, a.N, a.K);
     const int mw = lds_mw(a.M);
     const int BN = big ? BigTile::BN : SmallTile<4>::BN, BM = big ? BigTile::BM : 32 * mw;
     const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;

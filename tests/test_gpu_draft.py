@@ -244,6 +244,22 @@ def test_q8b_one_layer_ctx4096():
     assert flags.cpu().tolist() == [0]
 
 
+def test_q8b_one_layer_bs32():
+    # 512 rows: the QKV, gate|up (fused SwiGLU) and down products run on the
+    # 256 x 256 tile, the O product on the 128 x 128 one
+    ctx = [int(x) for x in np.random.default_rng(2).integers(64, 1025, 32)]
+    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs32_rs"], n_layers=1, ctx=ctx), "q8b_1layer_bs32")
+    dev, w, dr, kv = _setup(cfg, 1088)
+    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
+    w_np = to_np(w)
+    want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, ctx)
+    err = _logit_err(cfg, w_np, out, want)
+    print(f"q8b one layer bs 32: GPU-oracle logit error {err.max():.3e}, "
+          f"oracle self-divergence {self_div:.3e}")
+    assert err.max() <= max(2e-2, 3 * self_div)
+    assert flags.cpu().tolist() == [0] * 32
+
+
 def test_q8b_bs1_ctx4096_chain():
     cfg = configs.get("q8b_bs1_greedy")
     dev, w, dr, kv = _setup(cfg, 4096)
