@@ -364,11 +364,13 @@ template <typename T>
 __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
-    int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap) {
+    int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap,
+    int with_v) {
+  // K heads, and the V heads too when with_v (else inject_v_kernel does them)
   const int r = blockIdx.x, head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
   const int layer = blockIdx.z, lane = threadIdx.x & 63;
   const int sq = seq[r], ps = pos[r];
-  if (head >= 2 * hkv || sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
+  if (head >= (with_v ? 2 : 1) * hkv || sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
   const int half = dh / 2, ncol = 2 * hkv * dh, width = il.layers * ncol;
   const bool is_k = head < hkv;
   const int h = is_k ? head : head - hkv;
@@ -405,18 +407,84 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
   }
 }
 
+// V rows of the injected layers, 64 rows x dh per workgroup: the split sums
+// are staged in LDS as [row][d] (loads along d) and written out along rows,
+// so the rows of consecutive positions of one sequence, which share a 64-key
+// tile of the d-major V cache, fill consecutive 2-byte slots of each tile
+// row.  Sums in split order, one rounding to the cache dtype, as for K.
+constexpr int INJ_VROWS = 64;
+constexpr int INJ_V_MIN_ROWS = 2048;
+template <typename T>
+__global__ __launch_bounds__(256) void inject_v_kernel(
+    const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
+    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
+    int max_batch, int cap) {
+  extern __shared__ float tile[];  // [INJ_VROWS][dh + 1]
+  const int r0 = blockIdx.x * INJ_VROWS, h = blockIdx.y, layer = blockIdx.z;
+  const int ncol = 2 * hkv * dh, width = il.layers * ncol, ts = dh + 1;
+  const long col0 = (long)layer * ncol + (long)hkv * dh + (long)h * dh;
+  // 16-byte loads, eight per thread issued together (dh is 64 or 128)
+  const int q4 = dh / 4;
+  constexpr int U = 8;
+  for (int i0 = threadIdx.x; i0 < INJ_VROWS * q4; i0 += U * blockDim.x) {
+    f32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * blockDim.x, row = i / q4, r = r0 + row;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < INJ_VROWS * q4 && r < n) {
+        const float *src = parts + (long)r * width + col0 + 4 * (i % q4);
+        for (int s = 0; s < nsplit; ++s)
+          x[u] += *reinterpret_cast<const f32x4 *>(src + (long)s * n * width);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * blockDim.x;
+      if (i >= INJ_VROWS * q4) break;
+      const int row = i / q4, d = 4 * (i % q4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[row * ts + d + e] = x[u][e];
+    }
+  }
+  __syncthreads();
+  T *vc = (T *)il.vc[layer];
+  for (int i = threadIdx.x; i < INJ_VROWS * dh; i += blockDim.x) {
+    const int d = i / INJ_VROWS, row = i % INJ_VROWS, r = r0 + row;
+    if (r >= n) continue;
+    const int sq = seq[r], ps = pos[r];
+    if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
+    vc[((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (long)d * 64 + (ps & 63)] =
+        from_f32<T>(tile[row * ts + d]);
+  }
+}
+
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
                         const int32_t *seq, const int32_t *pos, const InjectLayers &il,
                         int qk_norm, float eps, const float *rope, int max_batch, int cap,
                         hipStream_t st) {
   if (n == 0 || il.layers == 0) return;
-  dim3 grid(n, (2 * hkv + POST_HEADS - 1) / POST_HEADS, il.layers);
+  // K heads: per-head norm + rotary embedding, one wave per (row, head).  V
+  // heads: with few rows the same per-row pass (enough workgroups), from
+  // INJ_V_MIN_ROWS rows the row-tiled transposing pass (contiguous stores)
+  const int with_v = n < INJ_V_MIN_ROWS;
+  dim3 grid(n, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS, il.layers);
   if (dtype == 1)
     hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v);
   else
     hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v);
+  if (with_v) return;
+  // V heads: staged and written along rows
+  const dim3 vgrid((n + INJ_VROWS - 1) / INJ_VROWS, hkv, il.layers);
+  const size_t lds = (size_t)INJ_VROWS * (dh + 1) * sizeof(float);
+  if (dtype == 1)
+    hipLaunchKernelGGL(inject_v_kernel<bf16>, vgrid, dim3(256), lds, st, parts, nsplit, n, hkv, dh,
+                       seq, pos, il, max_batch, cap);
+  else
+    hipLaunchKernelGGL(inject_v_kernel<float>, vgrid, dim3(256), lds, st, parts, nsplit, n, hkv,
+                       dh, seq, pos, il, max_batch, cap);
 }
 
 }  // namespace dstill
