@@ -284,6 +284,29 @@ def main():
         stages[n] = dict(ms=round(per_call[n], 4), gbs=round(b / t / 1e9, 1) if t else None,
                          tflops=round(f / t / 1e12, 2) if t else None)
 
+    # prefill-size injection (outside the cycle timing): one inject_kv call on
+    # the first prefill chunk (8192 rows), algorithmic flops 2 rows (W_c + the
+    # K/V rows of every layer) against the bf16 MFMA peak
+    prefill = None
+    if cfg["dtype"] == "bf16" and sum(cfg["ctx_lens"]) >= 8192:
+        f, sq, ps = cyc.prefill_chunk(8192)
+        n = f.shape[0]
+        cyc.dr.inject_kv(f, sq, ps, cyc.kv, cyc.ws)
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        p0.record(st)
+        for _ in range(reps):
+            cyc.dr.inject_kv(f, sq, ps, cyc.kv, cyc.ws)
+        p1.record(st)
+        torch.cuda.synchronize()
+        t = p0.elapsed_time(p1) / reps * 1e-3
+        d, L, kvd = cfg["hidden"], cfg["n_layers"], cfg["n_kv_heads"] * cfg["head_dim"]
+        fl = 2.0 * n * (d * cfg["feat_dim"] + L * 2 * kvd * d)
+        prefill = dict(rows=n, ms=round(t * 1e3, 4), tflops=round(fl / t / 1e12, 1),
+                       mfma_frac=round(fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+        del f, sq, ps
+
     # calibration copy of known size for HBM byte counters (outside timing):
     # one elementwise kernel that reads and writes `copy_mib` MiB
     copy_info = None
@@ -338,6 +361,7 @@ def main():
         "stages": stages,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "prefill_inject": prefill,
         "calibration_copy": copy_info,
     }
     print(json.dumps(out), flush=True)

@@ -139,6 +139,16 @@ class Cycle:
                                       dtype=torch.uint8, device=self.dev)
         torch.cuda.synchronize(self.dev)
 
+    def prefill_chunk(self, chunk: int = 8192):
+        """The first prefill chunk (features, sequence ids, positions), for
+        timing an injection at prefill size; injecting it again rewrites the
+        same cache rows with the same values."""
+        rows = [(b, p) for b, S in enumerate(self.ctx) for p in range(S)][:chunk]
+        f = gen.feats(self.cfg, len(rows), name="feats_prefill0", device=self.dev)
+        seq = torch.tensor([b for b, _ in rows], dtype=torch.int32, device=self.dev)
+        pos = torch.tensor([p for _, p in rows], dtype=torch.int32, device=self.dev)
+        return f, seq, pos
+
     def _prefill(self, chunk):
         rows = [(b, p) for b, S in enumerate(self.ctx) for p in range(S)]
         for i in range(0, len(rows), chunk):
