@@ -88,6 +88,18 @@ static bool use_big(int M, int N, int K) {
   return M >= BIG_MIN_ROWS || (M >= 512 && (long)N * K >= (24L << 20));
 }
 
+// Below 2048 rows a big product whose width divides by 192 takes 192-wide
+// weight tiles (still 256 rows, 2 x 4 waves of 6 x 4 MFMA tiles, one
+// workgroup per CU): at 512 rows the 256-wide tiles of the 8B-shaped
+// drafter's fused gate|up make 96 x 2 workgroups, too few for 256 compute
+// units, the 192-wide ones 128 x 2.  The choice depends on the shape alone,
+// so the split plan and the launch agree without the CU count.
+using MidTile = TileEngine<2, 4, 6, 4, LDS_KT, 3, 2>;
+static_assert(sizeof(MidTile::Smem) <= 160 * 1024, "one workgroup per CU");
+static bool use_mid(int M, int N, int K) {
+  return M < BIG_MIN_ROWS && use_big(M, N, K) && N % MidTile::BN == 0;
+}
+
 // Wave rows (groups of 16 MW rows) staged per pass of the partial store: the
 // most that fit the idle rings as a [rows][BN + 4] fp32 tile.
 template <class E>
@@ -219,20 +231,23 @@ struct LdsPlan {
 static LdsPlan lds_geometry(int M, int N, int K, int ncu) {
   LdsPlan p;
   p.big = use_big(M, N, K);
-  p.BN = p.big ? BigTile::BN : SmallTile<4>::BN;
+  const bool mid = use_mid(M, N, K);
+  p.BN = mid ? MidTile::BN : p.big ? BigTile::BN : SmallTile<4>::BN;
   p.BM = p.big ? BigTile::BM : 32 * lds_mw(M);
   p.nnb = (N + p.BN - 1) / p.BN;
   p.nmb = (M + p.BM - 1) / p.BM;
   p.nst = K / LDS_KT;
   const long tiles = (long)p.nnb * p.nmb;
   // Workgroups run in rounds of ncu x (2 small or 1 large) slots.  Estimated
-  // time of a split count s: rounds x (stages per workgroup x ~0.6 us per
-  // 64-deep stage of a round of small tiles, ~1.5 times that for large ones,
-  // + ~1 us of pipeline fill), plus the fp32 partial plane each split writes
-  // and the consumer reads back (~6 TB/s).  The smallest s within 3% of the
-  // best wins.
+  // time of a split count s: rounds x (stages per workgroup x the time of a
+  // 64-deep stage of a round, ~0.6 us for small tiles, ~0.95 us for 192-wide
+  // and ~1.2 us for 256-wide big ones, + ~1 us of pipeline fill), plus the
+  // fp32 partial plane each split writes and the consumer reads back (~6
+  // TB/s).  The smallest s within 3% of the best wins.  (Stage times fitted
+  // to split sweeps of the 8B-shaped drafter's QKV and down products at 512
+  // rows, where filling every compute unit beats one partial plane fewer.)
   const long slots = (long)ncu * (p.big ? 1 : 2);
-  const double stage_us = p.big ? 0.9 : 0.6;
+  const double stage_us = mid ? 0.95 : p.big ? 1.2 : 0.6;
   auto est = [&](int s) {
     const int per = (p.nst + s - 1) / s;
     const long rounds = (tiles * s + slots - 1) / slots;
@@ -267,6 +282,7 @@ bool gemm_can_fuse_swiglu(int M, int mlp, int K, int dtype, int num_cu) {
   if (!use_lds(K, dtype) || mlp % 64 != 0 || M <= 0 || M >= BIG_MIN_ROWS) return false;
   // on the big tile (128 features per n-block) one split is what the
   // unfused product runs with at these sizes too
+  if (use_mid(M, 2 * mlp, K)) return true;
   if (use_big(M, 2 * mlp, K)) return mlp % 128 == 0;
   const long tiles = (long)(mlp / 64) * ((M + 32 * lds_mw(M) - 1) / (32 * lds_mw(M)));
   return tiles >= num_cu;
@@ -328,6 +344,11 @@ void launch_gemm(const GemmArgs &a, hipStream_t st) {
     // fused gate|up + SwiGLU: BN / 2 features (BN weight rows) per n-block
     bf16 *act = (bf16 *)a.swiglu_act;
     const int nst = a.K / LDS_KT;
+    if (use_mid(a.M, 2 * a.mlp, a.K)) {
+      launch_lds<MidTile>(a, a.mlp / (MidTile::BN / 2), (a.M + MidTile::BM - 1) / MidTile::BM, nst,
+                          1, act, st);
+      return;
+    }
     if (use_big(a.M, 2 * a.mlp, a.K)) {
       launch_lds<BigTile>(a, a.mlp / (BigTile::BN / 2), (a.M + BigTile::BM - 1) / BigTile::BM, nst,
                           1, act, st);
@@ -342,12 +363,17 @@ void launch_gemm(const GemmArgs &a, hipStream_t st) {
   }
   if (use_lds(a.K, a.dtype)) {
     // the tile depends on the shape alone (the plan that chose a.splits used it too)
+    // (weight groups must hold whole tiles: with other group sizes the
+    // 256-wide tile runs under the plan's split count)
     const bool big = use_big(a.M, a.N, a.K);
+    const bool mid = use_mid(a.M, a.N, a.K) && a.wg_rows % MidTile::BN == 0;
     const int mw = lds_mw(a.M);
-    const int BN = big ? BigTile::BN : SmallTile<4>::BN, BM = big ? BigTile::BM : 32 * mw;
+    const int BN = mid ? MidTile::BN : big ? BigTile::BN : SmallTile<4>::BN;
+    const int BM = big ? BigTile::BM : 32 * mw;
     const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
     const int per = (nst + a.splits - 1) / a.splits;
-    if (big) launch_lds<BigTile>(a, nnb, nmb, per, a.splits, nullptr, st);
+    if (mid) launch_lds<MidTile>(a, nnb, nmb, per, a.splits, nullptr, st);
+    else if (big) launch_lds<BigTile>(a, nnb, nmb, per, a.splits, nullptr, st);
     else if (mw == 1) launch_lds<SmallTile<1>>(a, nnb, nmb, per, a.splits, nullptr, st);
     else if (mw == 2) launch_lds<SmallTile<2>>(a, nnb, nmb, per, a.splits, nullptr, st);
     else launch_lds<SmallTile<4>>(a, nnb, nmb, per, a.splits, nullptr, st);

@@ -244,20 +244,24 @@ def test_q8b_one_layer_ctx4096():
     assert flags.cpu().tolist() == [0]
 
 
-def test_q8b_one_layer_bs32():
-    # 512 rows: the QKV, gate|up (fused SwiGLU) and down products run on the
-    # 256 x 256 tile, the O product on the 128 x 128 one
-    ctx = [int(x) for x in np.random.default_rng(2).integers(64, 1025, 32)]
-    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs32_rs"], n_layers=1, ctx=ctx), "q8b_1layer_bs32")
-    dev, w, dr, kv = _setup(cfg, 1088)
+@pytest.mark.parametrize("bs,hi", [(32, 1025), (44, 300)])
+def test_q8b_one_layer_batched(bs, hi):
+    # 512 rows: the QKV (4 k-splits) and the gate|up product (fused SwiGLU)
+    # run on the 192 x 256 tile, the down product (8 k-splits) on the
+    # 256 x 256 one, the O product on the 128 x 128 one; 704 rows: three row
+    # blocks of 256, the last one ragged
+    ctx = [int(x) for x in np.random.default_rng(2).integers(64, hi, bs)]
+    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs32_rs"], bs=bs, n_layers=1, ctx=ctx),
+                         f"q8b_1layer_bs{bs}")
+    dev, w, dr, kv = _setup(cfg, (max(ctx) + 16 + 63) // 64 * 64)
     tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
     w_np = to_np(w)
     want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, ctx)
     err = _logit_err(cfg, w_np, out, want)
-    print(f"q8b one layer bs 32: GPU-oracle logit error {err.max():.3e}, "
+    print(f"q8b one layer bs {bs}: GPU-oracle logit error {err.max():.3e}, "
           f"oracle self-divergence {self_div:.3e}")
     assert err.max() <= max(2e-2, 3 * self_div)
-    assert flags.cpu().tolist() == [0] * 32
+    assert flags.cpu().tolist() == [0] * bs
 
 
 def test_q8b_bs1_ctx4096_chain():
