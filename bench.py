@@ -25,6 +25,12 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# Per-position acceptance of the planted variant: with gamma = 15 it gives
+# E[tau] = 1 + sum_{j=1..15} 0.86^j = 6.50, the mean acceptance length the
+# DFlash review's main results table (temperature 0) reports for the
+# Qwen3-8B drafter with block size 16 (6.49).  Random weights alone give
+# tau ~ 1.1.
+PLANT_ALPHA = 0.86
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
@@ -218,6 +224,36 @@ def main():
         taus = torch.cat(tau_hist).cpu().numpy().tolist()
     tau_mean = float(np.mean(taus)) if taus else None
 
+    # per-cycle spread: events between consecutive cycles, no host sync inside
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    cev[0].record(st)
+    for i in range(args.steps):
+        cyc.step(cycle=args.warmup + 2 * args.steps + i)
+        cev[i + 1].record(st)
+    torch.cuda.synchronize()
+    cyc_ms = np.array([cev[i].elapsed_time(cev[i + 1]) for i in range(args.steps)])
+    cycle_ms = {q: round(float(np.percentile(cyc_ms, v)), 4)
+                for q, v in (("p10", 10), ("median", 50), ("p90", 90))}
+
+    # planted acceptance (plain one-pass cycles with verification): the same
+    # cycles with accepted-prefix lengths planted into the target rows between
+    # head and verification (harness work, untimed); the verification must
+    # return tau = k + 1 for every sequence
+    planted = None
+    if cyc.can_plant():
+        p_tau, p_bad = [], 0
+        for i in range(args.steps):
+            c = args.warmup + 3 * args.steps + i
+            k = cyc.plant_draw(c, PLANT_ALPHA)
+            cyc.step(cycle=c, plant_k=k)
+            t = cyc.tau.cpu().numpy()
+            p_bad += int(np.sum(t != k + 1))
+            p_tau.append(t)
+        planted = dict(alpha=PLANT_ALPHA, tau_mean=round(float(np.mean(p_tau)), 4),
+                       tau_expected=round(1 + sum(PLANT_ALPHA ** j
+                                                  for j in range(1, cyc.gamma + 1)), 4),
+                       tau_mismatches=p_bad)
+
     n_inj = cfg["bs"] * cyc.n_new
     alg = _algorithmic(cfg, cyc.rows, n_inj)
     if cyc.K:
@@ -234,6 +270,10 @@ def main():
     cycles_per_s = 1000.0 / ms_step
     bs = cfg["bs"]
     tokens_per_s = cycles_per_s * bs * tau_mean if tau_mean else None
+    if planted:
+        # the cycle's work does not depend on tau (n_new is fixed), so the
+        # planted tokens/s uses the timed cycle rate
+        planted["tokens_per_s"] = round(cycles_per_s * bs * planted["tau_mean"], 1)
     total_bytes = sum(alg[n]["bytes"] for n in names)
     hbm_gbs = total_bytes / (ms_step * 1e-3) / 1e9
 
@@ -357,6 +397,8 @@ def main():
                    **({"swa_window": cfg["swa_window"]} if cfg.get("swa_window") else {})},
         "tokens_per_s": round(tokens_per_s, 1) if tokens_per_s else None,
         "tau_mean": tau_mean,
+        "planted": planted,
+        "cycle_ms": cycle_ms,
         "hbm_gbs": round(hbm_gbs, 1),
         "stages": stages,
         "roofline": roof,

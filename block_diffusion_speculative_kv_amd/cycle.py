@@ -32,6 +32,7 @@ inside a cycle.
 
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from synth import gen
@@ -226,7 +227,43 @@ class Cycle:
                draft_logits=(self.logits.view(bs, self.gamma, -1)
                              if self.logits is not None else None))
 
-    def step(self, cycle: int = 0):
+    # -- planted acceptance (harness only) ------------------------------------
+    def can_plant(self) -> bool:
+        return (self.verify_mode is not None and not (self.K or self.RK or self.spot)
+                and self.cfg["n_copies"] == 1)
+
+    def plant_draw(self, cycle: int, alpha: float) -> np.ndarray:
+        """Accepted-prefix lengths k in [0, gamma] per sequence: each draft
+        position is accepted with probability alpha independently until the
+        first rejection (P(k) = alpha^k (1 - alpha) for k < gamma, alpha^gamma
+        at k = gamma), so E[tau] = 1 + sum_{j=1..gamma} alpha^j; drawn on the
+        host from the cycle's own stream of numbers."""
+        rng = np.random.default_rng([int(self.seed), 4, int(cycle)])
+        acc = rng.random((self.cfg["bs"], self.gamma)) < alpha
+        return np.where(acc.all(axis=1), self.gamma, np.argmin(acc, axis=1))
+
+    def _plant(self, k: np.ndarray):
+        """Makes target row j of sequence b favour the drafted token y_{j+1}
+        for j < k_b (greedy: it is the row's argmax; rejection sampling: p(y)
+        = 1, so the ratio p/q >= 1 accepts) and give it no mass at j = k_b
+        (greedy mismatch; p(y) = 0 rejects), so tau_b = k_b + 1.  Returns
+        what is needed to undo it."""
+        bs, g = self.cfg["bs"], self.gamma
+        y = self.ids.view(bs, g).long()
+        kk = torch.as_tensor(k, device=self.dev).view(bs, 1)
+        j = torch.arange(g, device=self.dev).view(1, g)
+        bi = torch.arange(bs, device=self.dev).view(bs, 1).expand(bs, g)
+        ji = j.expand(bs, g)
+        old = self.target[bi, ji, y].clone()
+        new = torch.where(j < kk, torch.full_like(old, 1e4),
+                          torch.where(j == kk, torch.full_like(old, -1e4), old))
+        self.target[bi, ji, y] = new
+        return bi, ji, y, old
+
+    def step(self, cycle: int = 0, plant_k: np.ndarray = None):
+        """One cycle.  plant_k (plain one-pass cycles with verification only)
+        plants those accepted-prefix lengths into the target rows between the
+        head and the verification and restores the rows afterwards."""
         self.inject()
         if self.RK:
             self.refine(cycle)
@@ -234,4 +271,8 @@ class Cycle:
             self.draft()
             self.head(cycle)
             self.loop(cycle)
+        undo = self._plant(plant_k) if plant_k is not None else None
         self.verify(cycle)
+        if undo is not None:
+            bi, ji, y, old = undo
+            self.target[bi, ji, y] = old
