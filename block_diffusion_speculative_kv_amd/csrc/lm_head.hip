@@ -17,10 +17,11 @@
 // are permuted so that lane group g of a wave holds the 8 consecutive ids
 // 8g .. 8g+7 of a 32-id span: exactly one Philox4x64-10 block.
 //
-// Two main loops: up to 64 rows the weight is streamed once with fragments
-// loaded straight into registers (HBM-bound); with more rows (bf16) the
-// 128 x 128 LDS-tiled loop of mma_tile.hpp re-uses each staged weight tile
-// across 128 rows.  Both end in the same per-lane reduction epilogue.
+// Main loops (bf16): up to 64 rows the weight streams once through an LDS
+// ring of direct copies (HBM-bound); with more rows the tile engine of
+// mma_tile.hpp re-uses each staged weight tile across 160 or 256 rows.  fp32
+// (and shapes neither takes) load fragments straight into registers.  All
+// end in the same per-lane reduction epilogue.
 //
 // Launch: the row blocks of one vocabulary block are placed on the same XCD
 // (workgroup i runs on XCD i mod 8) and next to each other in dispatch order,
@@ -37,7 +38,8 @@ namespace dstill {
 
 constexpr int HEAD_VB = 256;  // vocabulary ids per workgroup, register path (64 per wave)
 constexpr int HEAD_KT = 64;   // LDS path: k per stage
-// LDS-path tiles (vocabulary ids x rows): 64 x 32 and 64 x 64 up to 64 rows,
+// LDS-path tiles (vocabulary ids x rows): 64 x 32 and 64 x 64 up to 64 rows
+// when the streaming kernel does not take them (depth not a multiple of 128),
 // 128 x 160 up to 160 rows (2 x 2 waves, two workgroups per CU; the 160-row
 // tile with a two-deep weight ring to fit); 256 x 256 beyond (2 x 4 waves, one
 // workgroup per CU, the weight three stages ahead in all of LDS), which
@@ -306,7 +308,10 @@ __global__ __launch_bounds__(E::NT) void lm_head_lds_kernel(HeadArgs a, int nmb)
         const f32x4 x = *reinterpret_cast<const f32x4 *>(lg + rl * LGS + (v - v0));
         float *dst = a.logits + (long)r * V + v;
         if (v + 4 <= V && (V & 3) == 0) {
-          *reinterpret_cast<f32x4 *>(dst) = x;
+          // streaming store: the logits are read back at most one row per
+          // sequence, long after, so they should not displace weight tiles
+          // that the other row blocks still read through L2
+          __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(dst));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -339,119 +344,156 @@ constexpr int head_stage_wave_rows() {
   return w;
 }
 
-// Weight-streaming variant for up to 16 rows (bf16, one row tile): the
-// weight tile of 128 vocabulary rows streams through a ring of HS_NS LDS
-// stages of k = 128 (256 contiguous bytes of every row, 32 KB), filled by
-// direct global->LDS copies HS_NS - 1 stages ahead, so about 96 KB per
-// compute unit stay in flight however short each stage's multiply.  The 16
-// hidden rows' slice of the stage (4 KB) rides in the same ring.  LDS rows
-// are unpadded and XOR-swizzled per 16-byte chunk, so the 16 rows one
-// fragment read touches (in the permuted vocabulary order) fall on distinct
-// banks.
+// Weight-streaming variant for up to 64 rows (bf16): the weight tile of 128
+// vocabulary rows streams through a ring of LDS stages of k = 128 (256
+// contiguous bytes of every row, 32 KB), filled by direct global->LDS copies
+// NS - 1 stages ahead (four stages, so ~96 KB per compute unit in flight, for
+// up to 32 rows; three for 33..64 rows, whose larger hidden slices leave room
+// for three).  The slice of the 16 RT hidden rows (4 RT KB) rides in the same
+// ring.  The kernel also takes several row blocks, those of one vocabulary
+// block placed on one XCD next to each other (workgroup i runs on XCD i mod
+// 8); measured on the 8B-shaped head that was slower than the 128 x 160 tile
+// from 100 rows on (144 rows: 473 against 377 us), so the launch uses one row
+// block.  LDS rows are unpadded and XOR-swizzled per 16-byte chunk, so the 16
+// rows one fragment read touches (in the permuted vocabulary order) fall on
+// distinct banks.
 constexpr int HS_K = 128;       // k per stage
-constexpr int HS_NS = 4;        // ring stages
 constexpr int HS_ROWS = 128;    // vocabulary rows per workgroup (32 per wave)
 constexpr int HS_WC = HS_ROWS * HS_K * 2 / 1024 / 4;  // weight copies per wave per stage
-constexpr int HS_OPS = HS_WC + 1;                      // + one hidden-slice copy
+constexpr int HS_MAX_RT = 4;    // row tiles of 16 per workgroup
 
+template <int RT>
 struct HsStage {
   bf16 w[HS_ROWS * HS_K];
-  bf16 x[16 * HS_K];
+  bf16 x[16 * RT * HS_K];
 };
+template <int RT>
+constexpr int hs_stages() { return RT <= 2 ? 4 : 3; }
+static_assert(sizeof(HsStage<2>) * hs_stages<2>() <= 160 * 1024, "ring fits LDS");
+static_assert(sizeof(HsStage<4>) * hs_stages<4>() <= 160 * 1024, "ring fits LDS");
 
 __device__ __forceinline__ int hs_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
 
-__global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a) {
-  __shared__ HsStage ring[HS_NS];
-  const int vb = blockIdx.x;
+template <int RT>
+__global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb) {
+  constexpr int NS = hs_stages<RT>(), OPS = HS_WC + RT;  // copies per wave per stage
+  __shared__ HsStage<RT> ring[NS];
+  // XCD-aware mapping of the linear workgroup id to (vocab block, row block)
+  const int L = blockIdx.x;
+  const int xcd = L % NXCD, slot = L / NXCD;
+  const int vb = (slot / nrb) * NXCD + xcd, rb = slot % nrb;
+  if (vb >= a.nvb) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int V = a.vocab, d = a.d;
-  const int v0 = vb * HS_ROWS;
+  const int v0 = vb * HS_ROWS, r0 = rb * 16 * RT;
+  auto hrow = [&](int r) { return (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq; };
+  const long h0 = hrow(r0);
   const char *wblk = reinterpret_cast<const char *>((const bf16 *)a.w + (long)v0 * d);
-  const char *xblk = reinterpret_cast<const char *>(a.hidden);
+  const char *xblk = reinterpret_cast<const char *>((const bf16 *)a.hidden + h0 * d);
   // weight copy j of wave w fills LDS vectors 64 (4 j + w) + lane: tile row
-  // 4 (4 j + w) + lane / 16, physical chunk lane % 16; the hidden copy of
-  // wave w fills rows 4 w + lane / 16 of the stage's 16 x 128 slice
+  // 4 (4 j + w) + lane / 16, physical chunk lane % 16; hidden copy j of wave
+  // w fills rows 4 (4 j + w) + lane / 16 of the stage's 16 RT x 128 slice
   uint32_t goff[HS_WC];
 #pragma unroll
   for (int j = 0; j < HS_WC; ++j) {
     const int row = 4 * (4 * j + wave) + (lane >> 4), pc = lane & 15;
     goff[j] = (uint32_t)((min(v0 + row, V - 1) - v0) * d * 2 + 16 * (pc ^ hs_swz(row)));
   }
-  uint32_t xoff;
-  {
-    const int row = 4 * wave + (lane >> 4), pc = lane & 15;
-    const int r = min(row, a.rows - 1);
-    const long hr = (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq;
-    xoff = (uint32_t)(hr * d * 2 + 16 * (pc ^ row));
+  uint32_t xoff[RT];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    const int row = 4 * (4 * j + wave) + (lane >> 4), pc = lane & 15;
+    const int r = min(r0 + row, a.rows - 1);
+    xoff[j] = (uint32_t)((hrow(r) - h0) * d * 2 + 16 * (pc ^ (row & 15)));
   }
   // A-operand rows of this wave's tile pair (permuted vocabulary order)
   int arow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) arow[t] = 32 * wave + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[2][RT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = d / HS_K;
   // each block starts its k walk at a different stage, so concurrent blocks
-  // do not sweep the same column offset of their rows at the same time
+  // do not sweep the same column offset of their rows at the same time (the
+  // row blocks of one vocabulary block share the start, so they read the
+  // same weight bytes at about the same time)
   const int rot = (vb * 5) % nst;
   auto kst = [&](int s) { return s + rot < nst ? s + rot : s + rot - nst; };
   auto issue = [&](int s) {
     const long k0 = (long)kst(s) * HS_K * 2;
-    HsStage &st = ring[s % HS_NS];
+    HsStage<RT> &st = ring[s % NS];
     const uint32_t wl = lds_u32(&st.w[0]) + wave * 1024;
 #pragma unroll
     for (int j = 0; j < HS_WC; ++j) dma16(wblk + k0, goff[j], wl + j * 4096);
-    dma16(xblk + k0, xoff, lds_u32(&st.x[0]) + wave * 1024);
+    const uint32_t xl = lds_u32(&st.x[0]) + wave * 1024;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) dma16(xblk + k0, xoff[j], xl + j * 4096);
   };
-  auto compute = [&](const HsStage &st) {
+  auto compute = [&](const HsStage<RT> &st) {
     const char *ws = reinterpret_cast<const char *>(&st.w[0]);
     const char *xs = reinterpret_cast<const char *>(&st.x[0]);
 #pragma unroll
     for (int kk = 0; kk < HS_K / 32; ++kk) {
-      const bf16x8 xf =
-          *reinterpret_cast<const bf16x8 *>(xs + r16 * HS_K * 2 + 16 * ((kk * 4 + g) ^ r16));
+      bf16x8 xf[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        xf[rt] = *reinterpret_cast<const bf16x8 *>(xs + (16 * rt + r16) * HS_K * 2 +
+                                                   16 * ((kk * 4 + g) ^ r16));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
             ws + arow[t] * HS_K * 2 + 16 * ((kk * 4 + g) ^ hs_swz(arow[t])));
-        acc[t] = Mma<bf16>::run(fa, xf, acc[t]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[t][rt] = Mma<bf16>::run(fa, xf[rt], acc[t][rt]);
       }
     }
   };
 #pragma unroll
-  for (int p = 0; p < HS_NS - 1; ++p)
+  for (int p = 0; p < NS - 1; ++p)
     if (p < nst) issue(p);
   for (int s = 0; s < nst; ++s) {
     // stage s has landed once at most the copies of the stages after it (up
-    // to HS_NS - 2 of them) are outstanding
-    const int ahead = min(nst - 1 - s, HS_NS - 2);
-    if (ahead >= 2) wait_vmcnt<2 * HS_OPS>();
-    else if (ahead == 1) wait_vmcnt<HS_OPS>();
+    // to NS - 2 of them) are outstanding
+    const int ahead = min(nst - 1 - s, NS - 2);
+    if (ahead >= 2) wait_vmcnt<2 * OPS>();
+    else if (ahead == 1) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     // every wave's copies of stage s are visible, and the buffer refilled
     // next (read at stage s - 1) is free
     __syncthreads();
-    if (s + HS_NS - 1 < nst) issue(s + HS_NS - 1);
-    compute(ring[s % HS_NS]);
+    if (s + NS - 1 < nst) issue(s + NS - 1);
+    compute(ring[s % NS]);
   }
   __syncthreads();
   // epilogue: per row, the wave's 32 ids, then the four waves in LDS
-  RowStat(*red)[16] = reinterpret_cast<RowStat(*)[16]>(&ring[0]);
+  RowStat(*red)[16 * RT] = reinterpret_cast<RowStat(*)[16 * RT]>(&ring[0]);
   const int vw = v0 + 32 * wave;
-  float zz[1][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zz[0][e] = acc[e >> 2][e & 3];
-  RowStat st2 = lane_rowstat<1>(a, r16, vw, g, zz);
-  if (g == 0) red[wave][r16] = st2;
+  for (int rt = 0; rt < RT; ++rt) {
+    float zz[1][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zz[0][e] = acc[e >> 2][rt][e & 3];
+    RowStat st2 = lane_rowstat<1>(a, r0 + 16 * rt + r16, vw, g, zz);
+    if (g == 0) red[wave][16 * rt + r16] = st2;
+  }
   __syncthreads();
-  if (threadIdx.x < 16 && threadIdx.x < a.rows) {
+  if (threadIdx.x < 16 * RT && r0 + (int)threadIdx.x < a.rows) {
     const int i = threadIdx.x;
     RowStat t = red[0][i];
 #pragma unroll
     for (int w = 1; w < 4; ++w) t = rowstat_merge(t, red[w][i]);
-    a.part[(long)i * a.nvb + vb] = to_partial(t);
+    a.part[(long)(r0 + i) * a.nvb + vb] = to_partial(t);
   }
+}
+
+template <int RT>
+static void launch_stream(const HeadArgs &a, int nrb, hipStream_t st) {
+  const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nrb);
+  hipLaunchKernelGGL((lm_head_stream_kernel<RT>), grid, dim3(256), 0, st, a, nrb);
 }
 
 // One workgroup per row merges the row's vocabulary-block records in two
@@ -558,17 +600,25 @@ static void launch_head_tile(const HeadArgs &a, dim3 grid, int nmb, hipStream_t 
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
-  // up to 16 rows stream the weight in 512-byte row slices; more rows go
-  // through the tile engine, with a tile fitted to the row count (the LDS
-  // kernel addresses a block's hidden rows with 32-bit byte offsets)
+  // up to 64 rows stream the weight through an LDS ring; more rows go
+  // through the tile engine, with a tile fitted to the row count (both
+  // address a block's hidden rows with 32-bit byte offsets)
   int BN = HeadMidTile::BN, BM = HeadMidTile::BM;
   if (a.rows <= 32) BN = 64, BM = 32;
   else if (a.rows <= 64) BN = 64, BM = 64;
   else if (a.rows > 160) BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
-  if (a.dtype == 1 && a.rows <= 16 && a.d % HS_K == 0) {
+  // streaming path: up to 64 rows, one row block of 16 RT rows (measured on
+  // the 8B-shaped head: 30 rows 306 -> 248 us, 60 rows 298 -> 273 us against
+  // the 64 x 32 / 64 x 64 tiles)
+  const int snrb = 1, srt = (a.rows + 15) / 16;
+  const long sspan = ((long)(16 * srt - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
+  if (a.dtype == 1 && a.rows <= 16 * HS_MAX_RT && a.d % HS_K == 0 && sspan < (1L << 31)) {
     a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
-    hipLaunchKernelGGL(lm_head_stream_kernel, dim3(a.nvb), dim3(256), 0, st, a);
+    if (srt == 1) launch_stream<1>(a, snrb, st);
+    else if (srt == 2) launch_stream<2>(a, snrb, st);
+    else if (srt == 3) launch_stream<3>(a, snrb, st);
+    else launch_stream<4>(a, snrb, st);
   } else if (a.dtype == 1 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
     a.nvb = (a.vocab + BN - 1) / BN;
     const int nmb = (a.rows + BM - 1) / BM;

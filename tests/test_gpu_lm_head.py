@@ -11,8 +11,10 @@ these inputs is ~1e-4 absolute; the near-tie count is reported.
 
 Shapes: the tiny fp32 workload (V 1024, d 256, gamma 7 rows), ragged bf16
 cases (V 5003, d 512, rows in blocks of 15 with a stride of 16) at 11, 30,
-37, 45, 100 and 300 rows (one case per kernel row band: <= 16, <= 32, <= 64,
-<= 160, two row blocks of the largest tile), and the full 8B-shaped head (V
+37, 45, 100 and 300 rows (the streaming kernel with 1, 2 and 3 row tiles,
+the 128 x 160 tile, two row blocks of the largest tile), the 64 x 32 and
+64 x 64 tiles at depth 576 (not a multiple of the streaming stage), and the
+full 8B-shaped head (V
 151936, d 4096) at the row counts of the greedy bs-1 (15 rows, argmax), bs-4
 (60 rows), bs-32 rejection-sampling (480 rows, Gumbel, logits stored; sampled
 rows checked) and multi-copy (144 rows, shared Gumbel) workloads.
@@ -119,13 +121,20 @@ def test_ragged_bf16_argmax():
 
 
 def test_ragged_bf16_gumbel_up_to_32_rows():
-    # 17..32 rows: the 32-row tile of the tile engine
+    # 17..32 rows: the streaming kernel with two row tiles
     _run_case(5003, 512, "bf16", 30, 15, 16, bd.HEAD_GUMBEL, keep_logits=True)
 
 
 def test_ragged_bf16_stream_up_to_16_rows():
-    # <= 16 rows: the weight-streaming kernel, with a partial last vocabulary block
+    # <= 16 rows: the streaming kernel with one row tile, partial last vocabulary block
     _run_case(5003, 512, "bf16", 11, 11, 16, bd.HEAD_GUMBEL, T=1.3, keep_logits=True)
+
+
+@pytest.mark.parametrize("rows,mode", [(30, bd.HEAD_GUMBEL), (60, bd.HEAD_ARGMAX)])
+def test_ragged_bf16_tiles_off_the_streaming_depth(rows, mode):
+    # depth 576 is a whole number of 64-deep tile stages but not of 128-deep
+    # streaming stages: the 64 x 32 and 64 x 64 tiles of the tile engine
+    _run_case(5003, 576, "bf16", rows, 15, 16, mode, keep_logits=True)
 
 
 def test_ragged_bf16_gumbel_up_to_160_rows():
@@ -139,7 +148,8 @@ def test_ragged_bf16_argmax_two_row_blocks():
 
 
 def test_q8b_bs4_rows():
-    # 60 rows (4 sequences x 15 slots): the 64-row tile at full vocabulary
+    # 60 rows (4 sequences x 15 slots): the streaming kernel with four row
+    # tiles (three-stage ring) at full vocabulary
     n, _, _ = _run_case(151936, 4096, "bf16", 60, 15, 16, bd.HEAD_ARGMAX, sample=12)
     assert n <= 1
 
