@@ -9,8 +9,9 @@
 // use Gumbel-max over log-weights with counter-based Philox noise.
 //
 // Four kernels, all streaming:
-//   vrow     per (target row, vocab split): max, argmax (lowest id), runner-
-//            up, and the softmax mass at temperature T (fp64 accumulation)
+//   vrow     per (target row, vocab split): greedy: max, argmax (lowest
+//            id) and runner-up; rejection sampling: the softmax mass at
+//            temperature T (fp64 accumulation)
 //   vdecide  per sequence: merge the splits, then the greedy prefix match or
 //            the accept scan (one lane per block slot, first failure by
 //            ballot); writes the accepted prefix, tau and the flags
@@ -167,11 +168,15 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ag[e] = ArgTop2{-INFINITY, -INFINITY, 0x7fffffff};
     // (each position chain sees its ids in increasing order: top2_push_inc)
-    const bool want_lse = a.mode != 0;  // greedy decisions use the top-2 only
+    // greedy decisions use the top-2 only, the rejection-sampling test the
+    // softmax mass only (the flags for non-finite values come from either)
+    const bool want_lse = a.mode != 0;
     auto group = [&](const float (&x)[8], int v) {
+      if (!want_lse) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) top2_push_inc(ag[e], x[e], v + e);
-      if (!want_lse) return;
+        for (int e = 0; e < 8; ++e) top2_push_inc(ag[e], x[e], v + e);
+        return;
+      }
       float y[8], gm = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
