@@ -400,7 +400,23 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
   const int v0 = sp * chunk, v1 = min(v0 + chunk, V);
   D2 rr{-INFINITY, -INFINITY, 0x7fffffff}, pp{-INFINITY, -INFINITY, 0x7fffffff};
   int any_r = 0, bad = 0;
+  // vector loads need rows of whole 8-id groups on 16-byte boundaries
+  const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
+                   (bonus || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
   for (int vb = v0 + 8 * threadIdx.x; vb < v1; vb += 8 * blockDim.x) {
+    // the 8 target and draft logits are loaded before the noise is drawn, as
+    // vectors where the row allows (one round trip instead of one per id)
+    float xt[8], xd[8];
+    if (vec && vb + 8 <= v1) {
+      ld8(zt + vb, xt);
+      if (!bonus) ld8(zd + vb, xd);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xt[e] = vb + e < v1 ? ld(zt, vb + e) : 0.f;
+        xd[e] = !bonus && vb + e < v1 ? zd[vb + e] : 0.f;
+      }
+    }
     uint32_t raw[8];
     philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
 #pragma unroll
@@ -408,10 +424,10 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
       const int v = vb + e;
       if (v >= v1) break;
       const double g = (double)gumbel_of(raw[e]);
-      const double lp = (double)ld(zt, v) / T - lse_t;
+      const double lp = (double)xt[e] / T - lse_t;
       d2_push(pp, lp + g, v);
       if (!bonus) {
-        const double zdv = (double)zd[v];
+        const double zdv = (double)xd[e];
         if (!isfinite(zdv)) bad = 1;
         const double r = exp(lp) - exp(zdv / T - lse_d);
         if (r > 0.0) {
