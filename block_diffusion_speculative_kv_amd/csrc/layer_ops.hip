@@ -265,6 +265,7 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
 }
 
 constexpr int POST_HEADS = 4;  // heads per workgroup, one wave each
+constexpr int POST_ROWS = 4;   // injected rows per workgroup
 template <typename T>
 __global__ __launch_bounds__(64 * POST_HEADS) void qkv_post_kernel(
     const float *__restrict__ parts, int nsplit, int R, int hq, int hkv, int dh,
@@ -366,43 +367,51 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
     int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap,
     int with_v) {
-  // K heads, and the V heads too when with_v (else inject_v_kernel does them)
-  const int r = blockIdx.x, head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
+  // K heads, and the V heads too when with_v (else inject_v_kernel does them);
+  // each wave takes its head in POST_ROWS consecutive rows (per-row work is
+  // small, so fewer, longer waves)
+  const int head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
   const int layer = blockIdx.z, lane = threadIdx.x & 63;
-  const int sq = seq[r], ps = pos[r];
-  if (head >= (with_v ? 2 : 1) * hkv || sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) return;
+  if (head >= (with_v ? 2 : 1) * hkv) return;
   const int half = dh / 2, ncol = 2 * hkv * dh, width = il.layers * ncol;
   const bool is_k = head < hkv;
   const int h = is_k ? head : head - hkv;
-  // all loads of the split planes first (they are independent), then the sums
-  // in split order
-  float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
+  T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
+#pragma unroll 1
+  for (int i = 0; i < POST_ROWS; ++i) {
+    const int r = blockIdx.x * POST_ROWS + i;
+    if (r >= n) break;
+    const int sq = seq[r], ps = pos[r];
+    if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
+    // all loads of the split planes first (they are independent), then the
+    // sums in split order
+    float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = lane + 64 * i;
-    if (p < half) {
-      const float *src = parts + (long)r * width + layer * ncol + head * dh + p;
-      for (int s = 0; s < nsplit; ++s) {
-        x1[i] += src[(long)s * n * width];
-        x2[i] += src[(long)s * n * width + half];
+    for (int j = 0; j < 2; ++j) {
+      const int p = lane + 64 * j;
+      if (p < half) {
+        const float *src = parts + (long)r * width + layer * ncol + head * dh + p;
+        for (int s = 0; s < nsplit; ++s) {
+          x1[j] += src[(long)s * n * width];
+          x2[j] += src[(long)s * n * width + half];
+        }
       }
     }
-  }
-  // K cache rows are dh-vectors [cap][dh]; the V cache is stored in tiles of
-  // 64 keys, d-major inside a tile: [cap/64][dh][64]
-  T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
-  const long stride = is_k ? 1 : 64;
-  T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
-                : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
-  if (is_k)
-    head_norm_rope<T>(x1, x2, dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
-                      rope + (long)r * half);
+    // K cache rows are dh-vectors [cap][dh]; the V cache is stored in tiles
+    // of 64 keys, d-major inside a tile: [cap/64][dh][64]
+    const long stride = is_k ? 1 : 64;
+    T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
+                  : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
+    if (is_k)
+      head_norm_rope<T>(x1, x2, dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
+                        rope + (long)r * half);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = lane + 64 * i;
-    if (p < half) {
-      dst[p * stride] = from_f32<T>(x1[i]);
-      dst[(p + half) * stride] = from_f32<T>(x2[i]);
+    for (int j = 0; j < 2; ++j) {
+      const int p = lane + 64 * j;
+      if (p < half) {
+        dst[p * stride] = from_f32<T>(x1[j]);
+        dst[(p + half) * stride] = from_f32<T>(x2[j]);
+      }
     }
   }
 }
@@ -468,7 +477,8 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
   // heads: with few rows the same per-row pass (enough workgroups), from
   // INJ_V_MIN_ROWS rows the row-tiled transposing pass (contiguous stores)
   const int with_v = n < INJ_V_MIN_ROWS;
-  dim3 grid(n, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS, il.layers);
+  dim3 grid((n + POST_ROWS - 1) / POST_ROWS, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
+            il.layers);
   if (dtype == 1)
     hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
                        seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v);
