@@ -265,7 +265,11 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
 }
 
 constexpr int POST_HEADS = 4;  // heads per workgroup, one wave each
-constexpr int POST_ROWS = 4;   // injected rows per workgroup
+// Rows per workgroup of the injection's head pass: per-row work is small, so
+// with many rows each wave takes its head in a few consecutive rows (fewer,
+// longer waves); with few rows one, so the launch still fills the chip.  (The
+// same change left the drafter's per-layer head pass at bs 32 unchanged.)
+static int post_rows(int n) { return n >= 256 ? 4 : 1; }
 template <typename T>
 __global__ __launch_bounds__(64 * POST_HEADS) void qkv_post_kernel(
     const float *__restrict__ parts, int nsplit, int R, int hq, int hkv, int dh,
@@ -366,10 +370,9 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
     int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap,
-    int with_v) {
+    int with_v, int rpw) {
   // K heads, and the V heads too when with_v (else inject_v_kernel does them);
-  // each wave takes its head in POST_ROWS consecutive rows (per-row work is
-  // small, so fewer, longer waves)
+  // each wave takes its head in rpw consecutive rows
   const int head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
   const int layer = blockIdx.z, lane = threadIdx.x & 63;
   if (head >= (with_v ? 2 : 1) * hkv) return;
@@ -378,8 +381,8 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
   const int h = is_k ? head : head - hkv;
   T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
 #pragma unroll 1
-  for (int i = 0; i < POST_ROWS; ++i) {
-    const int r = blockIdx.x * POST_ROWS + i;
+  for (int i = 0; i < rpw; ++i) {
+    const int r = blockIdx.x * rpw + i;
     if (r >= n) break;
     const int sq = seq[r], ps = pos[r];
     if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
@@ -477,14 +480,15 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
   // heads: with few rows the same per-row pass (enough workgroups), from
   // INJ_V_MIN_ROWS rows the row-tiled transposing pass (contiguous stores)
   const int with_v = n < INJ_V_MIN_ROWS;
-  dim3 grid((n + POST_ROWS - 1) / POST_ROWS, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
+  const int rpw = post_rows(n);
+  dim3 grid((n + rpw - 1) / rpw, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
             il.layers);
   if (dtype == 1)
     hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v, rpw);
   else
     hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v);
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v, rpw);
   if (with_v) return;
   // V heads: staged and written along rows
   const dim3 vgrid((n + INJ_VROWS - 1) / INJ_VROWS, hkv, il.layers);
