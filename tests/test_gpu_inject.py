@@ -124,3 +124,13 @@ def test_many_rows_transposed_v_path():
                 bd.KVCache.untile_v(c2).float().cpu().numpy()
             assert_bf16_rows_close(a[seq[rows], :, pos[rows]], b[seq[rows], :, pos[rows]],
                                    f"{what} layer {l}: one call vs chunks")
+
+
+def test_q8b_three_layers_grouped_kv_off_the_192_tile():
+    # 1000 rows, three 8B-shaped layers: the grouped K/V product (N = 3 x
+    # 2048 = 6144, K = 4096) has the shape that takes 192-wide weight tiles,
+    # but its 2048-row weight groups are not whole tiles of 192, so it runs on
+    # the 256-wide tile under the split count planned for the 192-wide one
+    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs1_greedy"], n_layers=3), "q8b_3layer")
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 1000, 4096, 1)
+    _check(cfg, w, kv, feats, seq, pos, np.arange(0, 1000, 37))
