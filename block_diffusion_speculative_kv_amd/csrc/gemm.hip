@@ -100,6 +100,20 @@ static bool use_mid(int M, int N, int K) {
   return M < BIG_MIN_ROWS && use_big(M, N, K) && N % MidTile::BN == 0;
 }
 
+// Products that take neither big tile run from 256 rows on 128 x 256 tiles
+// (2 x 4 waves of 4 x 4 MFMA tiles, one workgroup per CU, a quarter fewer
+// bytes copied into LDS per product term than two 128 x 128 workgroups)
+// where that still makes enough workgroups: from 512 rows, and from 256 rows
+// for the products with N K >= 24 Mi.  Measured on the 8B-shaped drafter
+// under the same split counts: 512 rows O 27.7 -> 25.7 us; 256 rows QKV
+// 27.3 -> 25.3, down 42.1 -> 37.7, W_c 63.9 -> 56.8, grouped K/V 36.9 ->
+// 32.3 us; slower at 256 rows for the 4096 x 4096 product (half the CUs).
+using WideTile = TileEngine<2, 4, 4, 4, LDS_KT, 3, 2>;
+static_assert(sizeof(WideTile::Smem) <= 160 * 1024, "one workgroup per CU");
+static bool use_wide(int M, int N, int K) {
+  return !use_big(M, N, K) && (M >= 512 || (M >= 256 && (long)N * K >= (24L << 20)));
+}
+
 // Wave rows (groups of 16 MW rows) staged per pass of the partial store: the
 // most that fit the idle rings as a [rows][BN + 4] fp32 tile.
 template <class E>
@@ -372,7 +386,10 @@ void launch_gemm(const GemmArgs &a, hipStream_t st) {
     const int BM = big ? BigTile::BM : 32 * mw;
     const int nnb = (a.N + BN - 1) / BN, nmb = (a.M + BM - 1) / BM, nst = a.K / LDS_KT;
     const int per = (nst + a.splits - 1) / a.splits;
-    if (mid) launch_lds<MidTile>(a, nnb, nmb, per, a.splits, nullptr, st);
+    if (use_wide(a.M, a.N, a.K) && a.wg_rows % WideTile::BN == 0)
+      launch_lds<WideTile>(a, (a.N + WideTile::BN - 1) / WideTile::BN,
+                           (a.M + WideTile::BM - 1) / WideTile::BM, per, a.splits, nullptr, st);
+    else if (mid) launch_lds<MidTile>(a, nnb, nmb, per, a.splits, nullptr, st);
     else if (big) launch_lds<BigTile>(a, nnb, nmb, per, a.splits, nullptr, st);
     else if (mw == 1) launch_lds<SmallTile<1>>(a, nnb, nmb, per, a.splits, nullptr, st);
     else if (mw == 2) launch_lds<SmallTile<2>>(a, nnb, nmb, per, a.splits, nullptr, st);

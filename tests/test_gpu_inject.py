@@ -98,6 +98,14 @@ def test_q8b_rows_sampled():
     _check(cfg, w, kv, feats, seq, pos, np.arange(0, 40, 5))
 
 
+def test_q8b_256_rows_sampled():
+    # 256 rows (the per-cycle injection at batch 32): the W_c and grouped K/V
+    # products on the 128 x 256 tile
+    cfg = configs.get("q8b_bs1_greedy")
+    dev, w, dr, kv, feats, seq, pos, _ = _inject(cfg, 256, 4096, 1)
+    _check(cfg, w, kv, feats, seq, pos, np.arange(0, 256, 23))
+
+
 def test_many_rows_transposed_v_path():
     # 2500 rows (from 2048 rows the V rows are written by the row-tiled pass):
     # against the oracle, with skipped rows, and against the same rows
