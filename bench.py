@@ -160,9 +160,9 @@ def main():
                     help="size of the calibration copy for HBM byte counters (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path shards "
-              "over sequences with no per-cycle exchange, and multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the path shards "
+              "over sequences with no per-cycle exchange, so the measure is one GPU's share "
+              "at its real shape; no multi-GPU run is implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
