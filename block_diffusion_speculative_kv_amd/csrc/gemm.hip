@@ -376,7 +376,9 @@ void launch_gemm(const GemmArgs &a, hipStream_t st) {
     return;
   }
   if (use_lds(a.K, a.dtype)) {
-    // the tile depends on the shape alone (the plan that chose a.splits used it too)
+    // the tile depends on the shape alone: the plan that chose a.splits
+    // used the same big and 192-wide tests; the 128 x 256 tile runs under
+    // the split count planned for the small one (the best of the sweeps)
     // (weight groups must hold whole tiles: with other group sizes the
     // 256-wide tile runs under the plan's split count)
     const bool big = use_big(a.M, a.N, a.K);
