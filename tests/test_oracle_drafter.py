@@ -2,6 +2,9 @@
 
 What fixes each part, other than the oracle itself:
 * bfloat16 rounding: torch's float32 -> bfloat16 conversion (library routine).
+* bfloat16 rounding points: an independent fp64 torch composition that rounds
+  (frexp / round-half-even) at the stated points; leaving out any one point
+  from the oracle breaks the agreement (mutation checks).
 * RMSNorm: torch.nn.functional.rms_norm; closed forms (constant vector, scale
   invariance).
 * Rotary embedding: the complex-number form (x1 + i x2) e^{i pos w}; norm
@@ -330,3 +333,178 @@ def test_sliding_window_matches_explicit_mask(S, W):
         full = _tiny(n_layers=2)
         mf, _ = _model(full)
         assert np.allclose(mf.draft(ck, cv, tok, S), m.draft(ck, cv, tok, S), atol=1e-13)
+
+
+# -- bfloat16 rounding points -------------------------------------------------
+#
+# The oracle's bf16 mode rounds (round to nearest even) exactly where the
+# library stores bfloat16: the fused state H_t, the cached K/V, the RMSNorm
+# outputs fed to a projection, q and k after the rotary embedding, v, the
+# attention output, the SiLU-times-up product and the final hidden state.
+# An independent composition of torch routines in fp64 rounds at those points
+# with a rounding of its own (frexp / round-half-even / ldexp, since torch's
+# float64 -> bfloat16 conversion goes through float32 and so rounds twice);
+# the two must agree to fp64 noise, and dropping any single rounding point
+# from the oracle must break that agreement.
+
+def _bf16_frexp(x):
+    """Round to 8 significant bits, ties to even, through frexp / ldexp."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def test_frexp_rounding_is_bf16():
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 3, 200000).astype(np.float32)
+    ties = (rng.integers(0x0080, 0x7F00, 1000).astype(np.uint32) << 16) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(_bf16_frexp(x.astype(np.float64)), want)
+    # a float64 value just above a bfloat16 midpoint rounds up (one rounding)
+    mid = 1.0 + 2.0 ** -8
+    assert _bf16_frexp(np.array([mid + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+    assert od.round_bf16(np.array([mid + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+
+
+def _bf16_model(**kw):
+    cfg = _tiny(dtype="bf16", **kw)
+    w = _np(gen.weights(cfg))          # bf16 values, held as float64
+    for lw in w["layers"]:
+        lw["wqkv"] *= 8                # a power of two keeps them bf16 values
+    return cfg, w
+
+
+def _torch_inject_bf16(cfg, w, feats, pos, rb):
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    R = lambda t: T(rb(t.numpy()))
+    qd, kvd, dh = cfg["q_dim"], cfg["kv_dim"], cfg["head_dim"]
+    ht = R(F.rms_norm(F.linear(T(feats), T(w["w_fuse"])), (cfg["hidden"],),
+                      T(w["g_fuse"]), cfg["rms_eps"]))
+    ks, vs = [], []
+    for lw in w["layers"]:
+        k = F.linear(ht, T(lw["wqkv"])[qd:qd + kvd]).view(len(pos), -1, dh)
+        k = _torch_rope(F.rms_norm(k, (dh,), T(lw["k_norm"]), cfg["rms_eps"]), list(pos),
+                        cfg["rope_theta"])
+        ks.append(rb(k.numpy()))
+        vs.append(rb(F.linear(ht, T(lw["wqkv"])[qd + kvd:]).view(len(pos), -1, dh).numpy()))
+    return ks, vs
+
+
+def _torch_draft_bf16(cfg, w, ctx_k, ctx_v, tokens, S, rb):
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    R = lambda t: T(rb(t.numpy()))
+    C, B = tokens.shape
+    hq, hkv, dh, d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["hidden"]
+    eps = cfg["rms_eps"]
+    h = F.embedding(torch.from_numpy(tokens.reshape(-1)).long(), T(w["embed"]))
+    pos = [S + s for _ in range(C) for s in range(B)]
+    for li, lw in enumerate(w["layers"]):
+        u = R(F.rms_norm(h, (d,), T(lw["attn_norm"]), eps))
+        q, k, v = F.linear(u, T(lw["wqkv"])).split([hq * dh, hkv * dh, hkv * dh], -1)
+        q = R(_torch_rope(F.rms_norm(q.reshape(-1, hq, dh), (dh,), T(lw["q_norm"]), eps), pos,
+                          cfg["rope_theta"]))
+        k = R(_torch_rope(F.rms_norm(k.reshape(-1, hkv, dh), (dh,), T(lw["k_norm"]), eps), pos,
+                          cfg["rope_theta"]))
+        v = R(v.reshape(-1, hkv, dh))
+        outs = []
+        for c in range(C):
+            sl = slice(c * B, (c + 1) * B)
+            K = torch.cat([T(ctx_k[li])[:, :S], k[sl].transpose(0, 1)], 1)
+            Vv = torch.cat([T(ctx_v[li])[:, :S], v[sl].transpose(0, 1)], 1)
+            o = F.scaled_dot_product_attention(q[sl].transpose(0, 1)[None], K[None],
+                                               Vv[None], enable_gqa=True)
+            outs.append(o[0].transpose(0, 1).reshape(B, hq * dh))
+        h = h + F.linear(R(torch.cat(outs, 0)), T(lw["wo"]))
+        u = R(F.rms_norm(h, (d,), T(lw["mlp_norm"]), eps))
+        g, up = F.linear(u, T(lw["w_gate_up"])).chunk(2, -1)
+        h = h + F.linear(R(F.silu(g) * up), T(lw["w_down"]))
+    return rb(F.rms_norm(h, (d,), T(w["g_final"]), eps).view(C, B, d).numpy())
+
+
+class _SkipRound:
+    """Oracle rounding that leaves out one rounding point: calls are counted
+    per draft pass (seven per layer: attention-norm output, q, k, v, attention
+    output, MLP-norm output, SiLU-times-up product; then the final state)."""
+
+    def __init__(self, skip, per_layer=7):
+        self.skip, self.per_layer, self.n = skip, per_layer, 0
+
+    def __call__(self, x):
+        i, self.n = self.n, self.n + 1
+        if i % self.per_layer == self.skip or (self.skip == "final" and i == self.last):
+            return np.asarray(x, dtype=np.float64)
+        return od.round_bf16(x)
+
+
+def _bf16_case(C=1, S=9):
+    cfg, w = _bf16_model(n_copies=C)
+    m = od.Drafter(cfg, w)
+    rng = np.random.default_rng(13)
+    n = max(S, 1)
+    feats = _bf16_frexp(rng.normal(0, 1, (n, cfg["feat_dim"])))
+    ks, vs = m.inject_rows(feats, np.arange(n))
+    tokens = np.full((C, cfg["block"]), cfg["mask_token_id"])
+    tokens[:, 0] = 7
+    if C > 1:
+        tokens[1:, 2] = rng.integers(0, 49, C - 1)
+    return cfg, w, m, feats, ks, vs, tokens
+
+
+@pytest.mark.parametrize("S,C", [(9, 1), (0, 1), (13, 3)])
+def test_bf16_draft_rounding_points(S, C):
+    cfg, w, m, feats, ks, vs, tokens = _bf16_case(C, S)
+    ck = [k.transpose(1, 0, 2) for k in ks]
+    cv = [v.transpose(1, 0, 2) for v in vs]
+    got = m.draft(ck, cv, tokens, S)
+    want = _torch_draft_bf16(cfg, w, ck, cv, tokens, S, _bf16_frexp)
+    assert np.array_equal(_bf16_frexp(got), got)      # the final state is bf16
+    assert np.allclose(got, want, rtol=0, atol=1e-9)
+    # the f32-mode oracle on the same inputs differs: rounding happens at all
+    m32 = od.Drafter(dict(cfg, dtype="f32"), w)
+    assert np.abs(m32.draft(ck, cv, tokens, S) - want).max() > 1e-4
+
+
+def test_bf16_injection_rounding_points():
+    cfg, w, m, feats, ks, vs, _ = _bf16_case()
+    pos = np.array([0, 5, 2, 9, 100, 3, 7, 1, 4])
+    tk, tv = _torch_inject_bf16(cfg, w, feats, pos, _bf16_frexp)
+    gk, gv = m.inject_rows(feats, pos)
+    for li in range(cfg["n_layers"]):
+        assert np.allclose(gk[li], tk[li], rtol=0, atol=1e-12)
+        assert np.allclose(gv[li], tv[li], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("skip", [0, 1, 2])
+def test_bf16_each_injection_rounding_point_is_needed(skip):
+    """Mutation check: leaving out the round of H_t (call 0), of the cached K
+    (call 1) or of the cached V (call 2) breaks the agreement."""
+    cfg, w, m, feats, ks, vs, _ = _bf16_case()
+    pos = np.array([0, 5, 2, 9, 100, 3, 7, 1, 4])
+    tk, tv = _torch_inject_bf16(cfg, w, feats, pos, _bf16_frexp)
+    calls = []
+
+    def rb(x):
+        calls.append(1)
+        return np.asarray(x, np.float64) if len(calls) - 1 == skip else od.round_bf16(x)
+    m.rb = rb
+    gk, gv = m.inject_rows(feats, pos)
+    assert len(calls) == 1 + 2 * cfg["n_layers"]
+    assert max(np.abs(gk[0] - tk[0]).max(), np.abs(gv[0] - tv[0]).max()) > 1e-6
+
+
+@pytest.mark.parametrize("skip", [0, 1, 2, 3, 4, 5, 6, "final"])
+def test_bf16_each_rounding_point_is_needed(skip):
+    """Mutation check: an oracle that leaves out any single rounding point no
+    longer matches the independent composition."""
+    S, C = 9, 1
+    cfg, w, m, feats, ks, vs, tokens = _bf16_case(C, S)
+    ck = [k.transpose(1, 0, 2) for k in ks]
+    cv = [v.transpose(1, 0, 2) for v in vs]
+    want = _torch_draft_bf16(cfg, w, ck, cv, tokens, S, _bf16_frexp)
+    mut = _SkipRound(skip)
+    mut.last = 7 * cfg["n_layers"]
+    m.rb = mut
+    got = m.draft(ck, cv, tokens, S)
+    assert mut.n == 7 * cfg["n_layers"] + 1          # every point was visited
+    assert np.abs(got - want).max() > 1e-6
