@@ -273,14 +273,15 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
       ws.l += p[t][i];
     }
   // P^T fragments per sub-chunk: keys 8g .. 8g+7 are p[2sc][0..3], p[2sc+1][0..3].
-  // bf16 carries them as a hi + lo pair (lo = the rounding residual of hi) so
-  // P.V keeps ~16 significant bits of P; fp32 uses two exact fragments.
+  // bf16 carries each probability as three terms hi + mid + lo (each the
+  // bf16 rounding of what the previous ones leave), so P.V sees the full fp32
+  // probability (8 + 8 + 8 significant bits); fp32 uses two exact fragments.
   constexpr int NPF = 8 / VEC;
   constexpr bool SPLIT = VEC == 8;
 #pragma unroll
   for (int sc = 0; sc < 2; ++sc) {
     if (sc >= nsub) break;
-    F pf[NPF], pl[NPF];
+    F pf[NPF], pm[NPF], pl[NPF];
 #pragma unroll
     for (int f = 0; f < NPF; ++f)
 #pragma unroll
@@ -289,7 +290,12 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
         const float pv = p[2 * sc + (k8 >> 2)][k8 & 3];
         const T hi = from_f32<T>(pv);
         pf[f][e] = hi;
-        if (SPLIT) pl[f][e] = from_f32<T>(pv - to_f32(hi));
+        if (SPLIT) {
+          const float r1 = pv - to_f32(hi);
+          const T mid = from_f32<T>(r1);
+          pm[f][e] = mid;
+          pl[f][e] = from_f32<T>(r1 - to_f32(mid));
+        }
       }
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
@@ -297,8 +303,11 @@ __device__ __forceinline__ void attend_chunk(const T *__restrict__ ks_lds,
       for (int f = 0; f < NPF; ++f) {
         const F vf =
             *reinterpret_cast<const F *>(Lay::v(vt_lds, dt * 16 + r16, sc * 32 + 8 * g + f * VEC));
+        if (SPLIT) {
+          ws.o[dt] = Mma<T>::run(vf, pl[f], ws.o[dt]);
+          ws.o[dt] = Mma<T>::run(vf, pm[f], ws.o[dt]);
+        }
         ws.o[dt] = Mma<T>::run(vf, pf[f], ws.o[dt]);
-        if (SPLIT) ws.o[dt] = Mma<T>::run(vf, pl[f], ws.o[dt]);
       }
     }
   }
@@ -340,20 +349,24 @@ __device__ __forceinline__ void attend_sub(const bf16 *__restrict__ ks_lds,
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, WAVE));
   rescale<DH>(ws, cmax, c);
   const float mc = ws.m * c;
-  F pf, pl;
+  F pf, pm, pl;
 #pragma unroll
   for (int k8 = 0; k8 < 8; ++k8) {
     const float pv = __builtin_amdgcn_exp2f(fmaf(s[k8 >> 2][k8 & 3], c, -mc));
     ws.l += pv;
     const bf16 hi = from_f32<bf16>(pv);
+    const float r1 = pv - to_f32(hi);
+    const bf16 mid = from_f32<bf16>(r1);
     pf[k8] = hi;
-    pl[k8] = from_f32<bf16>(pv - to_f32(hi));
+    pm[k8] = mid;
+    pl[k8] = from_f32<bf16>(r1 - to_f32(mid));
   }
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) {
     const F vf = *reinterpret_cast<const F *>(Lay::v(vt_lds, dt * 16 + r16, sub * 32 + 8 * g));
-    ws.o[dt] = Mma<bf16>::run(vf, pf, ws.o[dt]);
     ws.o[dt] = Mma<bf16>::run(vf, pl, ws.o[dt]);
+    ws.o[dt] = Mma<bf16>::run(vf, pm, ws.o[dt]);
+    ws.o[dt] = Mma<bf16>::run(vf, pf, ws.o[dt]);
   }
 }
 

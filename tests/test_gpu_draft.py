@@ -5,15 +5,20 @@ N(0, 1) K/V standing in for injected rows) and the same block tokens.
 
 Tolerances.  The tiny fp32 workload must match to 1e-5 relative.  bf16
 drafters are compared on the LM-head logits of the final hidden state: 2e-2
-absolute for the 2-layer reduced drafter.  A chain of bf16 rounding points
-amplifies any fp32-sized difference into rounding flips that the oracle
-cannot mirror; nudging the fp64 oracle's own norm inputs by 2^-24 relative
-moves its 8B-shaped logits by ~0.01 (one layer) and ~0.03 (five layers), and
-the kernel's fp32 sums carry more than that (the attention output is a sum of
-~1-sized terms that cancels to ~0.016, so its fp32 relative error is ~2e-4
-before rounding).  So the 8B-shaped drafters are held to a bound derived in
-the test from that experiment: the GPU may differ from the oracle by at most
-max(2e-2, 3x what the oracle differs from itself under the perturbation).
+absolute for the 2-layer reduced drafter.  At 8B sizes a chain of bf16
+rounding points turns any fp32-sized difference into rounding flips that
+cascade (a flip in one norm output moves every downstream pre-rounding value
+by a fraction of an ulp, which flips a share of the next rounding point, and
+so on); the fp64 oracle shows the same when its own norm inputs are nudged by
+a relative 2^-24 (one fp32 rounding): its logits move by up to 0.017-0.026
+with one layer and 0.045-0.052 with five, on these workloads' inputs (the
+'oracle_self_div' each case records).  An implementation that accumulates in
+fp32, as this one does, cannot sit closer to the fp64 oracle than that, so
+the 8B-shaped cases are held to fixed bounds above those figures: 3e-2 for
+one layer, 8e-2 for the five-layer chains.  Each case records its achieved
+maximum and mean logit error, the oracle's own divergence and the greedy ids
+that differ; an id may differ only on a row whose oracle top-2 gap is below
+twice the bound.
 
 Cases: the tiny workload; a reduced bf16 drafter with ragged contexts (37,
 300, 1029: several 64-key chunks, several context splits and ragged tails),
@@ -231,53 +236,86 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
-def test_q8b_one_layer_ctx4096():
-    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs1_greedy"], n_layers=1), "q8b_1layer")
-    dev, w, dr, kv = _setup(cfg, 4096)
-    tok, out, flags = _draft(cfg, dr, kv, dev, [4096], 4096)
+
+
+# -- the 8B-shaped drafter at the workloads' own shapes ----------------------
+#
+# Bounds on |logit(GPU) - logit(oracle)| for the 8B-shaped drafter (see the
+# module docstring): above what one fp32 rounding of the oracle's norm inputs
+# already moves its own logits by.  Each case records the achieved maximum
+# logit error, the oracle's own divergence under that nudge, and the greedy
+# ids that differ.
+
+ONE_LAYER_BOUND = 3e-2
+CHAIN_BOUND = 8e-2
+
+
+def _q8b_cfg(name, **kw):
+    return configs.finish(dict(configs.WORKLOADS[name], **kw), f"{name}_test")
+
+
+def _q8b_case(cfg, cap, bound, record, what, tokens=None, self_div=True):
+    dev, w, dr, kv = _setup(cfg, cap)
+    S = cfg["ctx_lens"]
+    tok, out, flags = _draft(cfg, dr, kv, dev, S, max(S), tokens=tokens)
     w_np = to_np(w)
-    want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, [4096])
+    del w
+    if self_div:
+        want, sd = _oracle_self_divergence(cfg, w_np, kv, tok, S)
+    else:
+        want, sd = _oracle(cfg, w_np, kv, tok, S), float("nan")
     err = _logit_err(cfg, w_np, out, want)
-    print(f"q8b one layer: GPU-oracle logit error {err.max():.3e}, "
-          f"oracle self-divergence {self_div:.3e}")
-    assert err.max() <= max(2e-2, 3 * self_div)
-    assert flags.cpu().tolist() == [0]
+    # greedy ids of the slots the head would score (1..gamma; every slot of
+    # the multi-copy layout); a flip is possible only where the oracle's
+    # top-2 gap is below twice the logit bound
+    first = 0 if cfg["n_copies"] > 1 else 1
+    g = to_np(out)[:, :, first:].reshape(-1, cfg["hidden"])
+    r = np.asarray(want)[:, :, first:].reshape(-1, cfg["hidden"])
+    hg = oracle_head(w_np["lm_head"], g)
+    hr = oracle_head(w_np["lm_head"], r)
+    flip = hg["ids"] != hr["ids"]
+    ambiguous = hr["gap"] < 2 * bound
+    record(max_logit_err=float(err.max()), mean_logit_err=float(err.mean()),
+           oracle_self_div=sd, bound=bound, rows=int(flip.size), id_flips=int(flip.sum()),
+           rows_gap_below_2bound=int(ambiguous.sum()))
+    assert err.max() <= bound, (
+        f"{what}: logits differ by {err.max():.3e} > {bound:g} "
+        f"(oracle self-divergence {sd:.3e}, {int(flip.sum())} of {flip.size} greedy ids differ)")
+    assert not (flip & ~ambiguous).any(), f"{what}: an id differs where the top-2 gap is wide"
+    assert flags.cpu().tolist() == [0] * cfg["bs"]
 
 
-@pytest.mark.parametrize("bs,hi", [(32, 1025), (44, 300)])
-def test_q8b_one_layer_batched(bs, hi):
-    # 512 rows: the QKV (4 k-splits) and the gate|up product (fused SwiGLU)
-    # run on the 192 x 256 tile, the down product (8 k-splits) on the
-    # 256 x 256 one, the O product on the 128 x 128 one; 704 rows: three row
-    # blocks of 256, the last one ragged
-    ctx = [int(x) for x in np.random.default_rng(2).integers(64, hi, bs)]
-    cfg = configs.finish(dict(configs.WORKLOADS["q8b_bs32_rs"], bs=bs, n_layers=1, ctx=ctx),
-                         f"q8b_1layer_bs{bs}")
-    dev, w, dr, kv = _setup(cfg, (max(ctx) + 16 + 63) // 64 * 64)
-    tok, out, flags = _draft(cfg, dr, kv, dev, ctx, max(ctx))
-    w_np = to_np(w)
-    want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, ctx)
-    err = _logit_err(cfg, w_np, out, want)
-    print(f"q8b one layer bs {bs}: GPU-oracle logit error {err.max():.3e}, "
-          f"oracle self-divergence {self_div:.3e}")
-    assert err.max() <= max(2e-2, 3 * self_div)
-    assert flags.cpu().tolist() == [0] * bs
+def test_q8b_one_layer_ctx4096(parity_record):
+    cfg = _q8b_cfg("q8b_bs1_greedy", n_layers=1)
+    _q8b_case(cfg, 4096, ONE_LAYER_BOUND, parity_record, "q8b one layer S 4096")
 
 
-def test_q8b_bs1_ctx4096_chain():
-    cfg = configs.get("q8b_bs1_greedy")
-    dev, w, dr, kv = _setup(cfg, 4096)
-    tok, out, flags = _draft(cfg, dr, kv, dev, [4096], 4096)
-    w_np = to_np(w)
-    want, self_div = _oracle_self_divergence(cfg, w_np, kv, tok, [4096])
-    err = _logit_err(cfg, w_np, out, want)
-    print(f"q8b 5-layer chain: GPU-oracle logit error {err.max():.3e}, "
-          f"oracle self-divergence {self_div:.3e}")
-    assert err.max() <= max(2e-2, 3 * self_div)
-    # the greedy ids the head would pick from the two hidden states
-    g = to_np(out)[0, 0, 1:]
-    zg = oracle_head(w_np["lm_head"], g)
-    zr = oracle_head(w_np["lm_head"], want[0, 0, 1:])
-    flips = int(np.sum(zg["ids"] != zr["ids"]))
-    print(f"q8b 5-layer chain: {flips} of 15 greedy ids differ")
-    assert flags.cpu().tolist() == [0]
+def test_q8b_one_layer_bs32_ragged_to_8192(parity_record):
+    # the bs-32 workload's own contexts (integers uniform in [1024, 8192],
+    # default_rng(0)): splits of ~2752 keys, 43 chunks each
+    cfg = _q8b_cfg("q8b_bs32_rs", n_layers=1)
+    cap = (max(cfg["ctx_lens"]) + 63) // 64 * 64
+    _q8b_case(cfg, cap, ONE_LAYER_BOUND, parity_record, "q8b one layer bs 32 ragged")
+
+
+def test_q8b_one_layer_bs4_ctx32768(parity_record):
+    # the long-context workload: 16 splits of 2048 keys per (sequence, KV head)
+    cfg = _q8b_cfg("q8b_bs4_long", n_layers=1)
+    _q8b_case(cfg, 32768, ONE_LAYER_BOUND, parity_record, "q8b one layer bs 4 S 32768",
+              self_div=False)
+
+
+def test_q8b_one_layer_multicopy(parity_record):
+    # nine copies of a 16-slot block (the root and eight drafted states)
+    # behind a 4096-token prefix, copy-local block attention
+    cfg = _q8b_cfg("q8b_multicopy", n_layers=1)
+    tok, _ = gen.draft_tree(cfg, device=device())
+    _q8b_case(cfg, 4096, ONE_LAYER_BOUND, parity_record, "q8b one layer 9 copies", tokens=tok)
+
+
+@pytest.mark.parametrize("name", ["q8b_bs1_greedy", "q8b_multicopy", "q8b_bs32_rs"])
+def test_q8b_five_layer_chain(name, parity_record):
+    cfg = _q8b_cfg(name)
+    cap = (max(cfg["ctx_lens"]) + 63) // 64 * 64
+    tok = gen.draft_tree(cfg, device=device())[0] if cfg["n_copies"] > 1 else None
+    _q8b_case(cfg, cap, CHAIN_BOUND, parity_record, f"{name} five layers", tokens=tok)
