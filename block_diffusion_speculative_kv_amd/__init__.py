@@ -16,11 +16,12 @@ import torch
 from . import _lib
 from ._lib import (BF16, F32, FLAG_BAD_INPUT, FLAG_CTX_CLAMPED, FLAG_NEAR_THRESHOLD,
                    FLAG_NEAR_TIE_SAMPLE, FLAG_NEAR_TIE_TARGET, FLAG_ZERO_RESIDUAL, HEAD_ARGMAX,
-                   HEAD_GUMBEL, HEAD_SHARED_GUMBEL, NEAR, VERIFY_GREEDY, VERIFY_RS, DstillError)
+                   HEAD_GUMBEL, HEAD_SHARED_GUMBEL, NEAR, NOALLOC_SCRATCH_BYTES, VERIFY_GREEDY,
+                   VERIFY_RS, DstillError)
 
 __all__ = [
-    "Drafter", "verify", "verify_workspace_bytes", "DstillError", "F32", "BF16", "HEAD_ARGMAX",
-    "HEAD_GUMBEL", "HEAD_SHARED_GUMBEL", "VERIFY_GREEDY", "VERIFY_RS", "FLAG_NEAR_TIE_TARGET",
+    "Drafter", "verify", "verify_noalloc", "verify_workspace_bytes", "DstillError", "F32",
+    "BF16", "HEAD_ARGMAX", "HEAD_GUMBEL", "HEAD_SHARED_GUMBEL", "VERIFY_GREEDY", "VERIFY_RS", "FLAG_NEAR_TIE_TARGET",
     "FLAG_NEAR_THRESHOLD", "FLAG_NEAR_TIE_SAMPLE", "FLAG_ZERO_RESIDUAL", "FLAG_BAD_INPUT",
     "FLAG_CTX_CLAMPED", "NEAR",
     "dloop_branches", "dloop_merge", "verify_branches", "verify_branches_workspace_bytes",
@@ -204,6 +205,25 @@ def verify(mode: int, draft_ids, target_logits, out_tokens, out_tau, out_flags, 
                                  _ptr(target_logits), tdt, _ptr(out_tokens), _ptr(out_tau),
                                  _ptr(out_flags), _ptr(ws), ws.numel(), _stream(stream)),
                "dstill_verify")
+
+
+def verify_noalloc(mode: int, draft_ids, target_logits, out_tokens, out_tau, out_flags, *,
+                   temperature=1.0, seed=0, cycle=0, draft_lse=None, draft_logits=None,
+                   stream=None):
+    """verify() without a workspace argument: the library's fixed per-device
+    scratch (NOALLOC_SCRATCH_BYTES) serves as workspace; nothing is allocated.
+    Calls that overlap on one device race on that scratch."""
+    lib = _lib.load()
+    _dev_check(draft_ids, target_logits, out_tokens, out_tau, out_flags, draft_lse, draft_logits)
+    bs, g1, V = target_logits.shape
+    tdt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    if target_logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("target logits must be fp32 or bf16")
+    _lib.check(lib.dstill_verify_noalloc(mode, bs, g1 - 1, V, float(temperature), int(seed),
+                                         int(cycle), _ptr(draft_ids), _ptr(draft_lse),
+                                         _ptr(draft_logits), _ptr(target_logits), tdt,
+                                         _ptr(out_tokens), _ptr(out_tau), _ptr(out_flags),
+                                         _stream(stream)), "dstill_verify_noalloc")
 
 
 # ---- D-Loop second pass ------------------------------------------------------

@@ -26,12 +26,14 @@ FLAG_ZERO_RESIDUAL = 8
 FLAG_BAD_INPUT = 16
 FLAG_CTX_CLAMPED = 32
 NEAR = 1e-5
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # every symbol the header declares
 EXPORTS = [
     "dstill_create", "dstill_destroy", "dstill_kv_bytes", "dstill_workspace_bytes",
     "dstill_inject_kv", "dstill_block_draft", "dstill_lm_head_argmax",
-    "dstill_verify_workspace_bytes", "dstill_verify", "dstill_dloop_branches",
+    "dstill_verify_workspace_bytes", "dstill_verify", "dstill_verify_noalloc",
+    "dstill_dloop_branches",
     "dstill_dloop_merge", "dstill_verify_branches_workspace_bytes", "dstill_verify_branches",
     "dstill_spot_verify", "dstill_refine_commit", "dstill_last_error", "dstill_version",
 ]
@@ -95,6 +97,8 @@ def _declare(lib):
         "dstill_verify_workspace_bytes": ([i32, i32, i32, POINTER(c_size_t)], c_int32),
         "dstill_verify": ([i32, i32, i32, i32, c_float, c_uint64, c_uint64, vp, vp, vp, vp, i32,
                            vp, vp, vp, vp, sz, vp], c_int32),
+        "dstill_verify_noalloc": ([i32, i32, i32, i32, c_float, c_uint64, c_uint64, vp, vp, vp, vp,
+                                   i32, vp, vp, vp, vp], c_int32),
         "dstill_dloop_branches": ([i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp], c_int32),
         "dstill_dloop_merge": ([i32, i32, i32, vp, vp, vp, vp, vp], c_int32),
         "dstill_verify_branches_workspace_bytes": ([i32, i32, i32, i32, POINTER(c_size_t)],

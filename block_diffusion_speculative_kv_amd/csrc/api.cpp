@@ -211,6 +211,48 @@ int check_kv(const dstill_handle *h, const dstill_kv *kv) {
 
 }  // namespace
 
+namespace dstill {
+
+int verify_call(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float temperature,
+                uint64_t seed, uint64_t cycle, const int32_t *draft_ids, const float *draft_lse,
+                const float *draft_logits, const void *target_logits, int32_t target_dtype,
+                int32_t *out_tokens, int32_t *out_tau, uint32_t *out_flags, void *ws,
+                size_t ws_bytes, void *stream) {
+  if (mode != DSTILL_VERIFY_GREEDY && mode != DSTILL_VERIFY_RS)
+    return fail(DSTILL_EINVAL, "unknown verify mode %d", mode);
+  if (bs < 0 || gamma < 1 || gamma > 63 || vocab < 2)
+    return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= gamma <= 63, vocab >= 2");
+  if (target_dtype != DSTILL_F32 && target_dtype != DSTILL_BF16)
+    return fail(DSTILL_EUNSUPPORTED, "target_dtype %d", target_dtype);
+  if (bs == 0) return DSTILL_OK;
+  if (!draft_ids || !target_logits || !out_tokens || !out_tau || !out_flags || !ws)
+    return fail(DSTILL_EINVAL, "null tensor argument");
+  if (mode == DSTILL_VERIFY_RS) {
+    if (!draft_lse || !draft_logits)
+      return fail(DSTILL_EINVAL, "rejection sampling needs draft_lse and draft_logits");
+    if (!(temperature > 0.f)) return fail(DSTILL_EINVAL, "temperature must be > 0");
+  }
+  if (cycle >> 56) return fail(DSTILL_EINVAL, "cycle must be < 2^56");
+  const int nsplit = verify_plan_splits(bs * (gamma + 1), vocab);
+  const int nsamp = verify_plan_splits(bs, vocab);
+  const size_t need = verify_ws_bytes(bs, gamma, nsplit, nsamp);
+  if (ws_bytes < need) return fail(DSTILL_EWORKSPACE, "verify needs %zu workspace bytes", need);
+  VerifyArgs a;
+  a.mode = mode; a.bs = bs; a.gamma = gamma; a.vocab = vocab; a.tdtype = target_dtype;
+  a.temperature = mode == DSTILL_VERIFY_RS ? temperature : 1.0f;
+  a.seed = seed; a.cycle = cycle;
+  a.draft_ids = draft_ids; a.draft_lse = draft_lse; a.draft_logits = draft_logits;
+  a.target = target_logits;
+  a.tokens = out_tokens; a.tau = out_tau; a.flags = out_flags;
+  a.ws = ws; a.nsplit = nsplit; a.nsamp = nsamp;
+  launch_verify(a, (hipStream_t)stream);
+  return hip_check("verify launch");
+}
+
+int api_fail(int code, const char *msg) { return fail(code, "%s", msg); }
+
+}  // namespace dstill
+
 extern "C" {
 
 int dstill_version(void) { return 100; }
@@ -494,41 +536,16 @@ int dstill_verify_workspace_bytes(int32_t bs, int32_t gamma, int32_t vocab, size
   return DSTILL_OK;
 }
 
+
 int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float temperature,
                   uint64_t seed, uint64_t cycle, const int32_t *draft_ids,
                   const float *draft_lse, const float *draft_logits,
                   const void *target_logits, int32_t target_dtype, int32_t *out_tokens,
                   int32_t *out_tau, uint32_t *out_flags, void *ws, size_t ws_bytes,
                   void *stream) {
-  if (mode != DSTILL_VERIFY_GREEDY && mode != DSTILL_VERIFY_RS)
-    return fail(DSTILL_EINVAL, "unknown verify mode %d", mode);
-  if (bs < 0 || gamma < 1 || gamma > 63 || vocab < 2)
-    return fail(DSTILL_ESHAPE, "need bs >= 0, 1 <= gamma <= 63, vocab >= 2");
-  if (target_dtype != DSTILL_F32 && target_dtype != DSTILL_BF16)
-    return fail(DSTILL_EUNSUPPORTED, "target_dtype %d", target_dtype);
-  if (bs == 0) return DSTILL_OK;
-  if (!draft_ids || !target_logits || !out_tokens || !out_tau || !out_flags || !ws)
-    return fail(DSTILL_EINVAL, "null tensor argument");
-  if (mode == DSTILL_VERIFY_RS) {
-    if (!draft_lse || !draft_logits)
-      return fail(DSTILL_EINVAL, "rejection sampling needs draft_lse and draft_logits");
-    if (!(temperature > 0.f)) return fail(DSTILL_EINVAL, "temperature must be > 0");
-  }
-  if (cycle >> 56) return fail(DSTILL_EINVAL, "cycle must be < 2^56");
-  const int nsplit = verify_plan_splits(bs * (gamma + 1), vocab);
-  const int nsamp = verify_plan_splits(bs, vocab);
-  const size_t need = verify_ws_bytes(bs, gamma, nsplit, nsamp);
-  if (ws_bytes < need) return fail(DSTILL_EWORKSPACE, "verify needs %zu workspace bytes", need);
-  VerifyArgs a;
-  a.mode = mode; a.bs = bs; a.gamma = gamma; a.vocab = vocab; a.tdtype = target_dtype;
-  a.temperature = mode == DSTILL_VERIFY_RS ? temperature : 1.0f;
-  a.seed = seed; a.cycle = cycle;
-  a.draft_ids = draft_ids; a.draft_lse = draft_lse; a.draft_logits = draft_logits;
-  a.target = target_logits;
-  a.tokens = out_tokens; a.tau = out_tau; a.flags = out_flags;
-  a.ws = ws; a.nsplit = nsplit; a.nsamp = nsamp;
-  launch_verify(a, (hipStream_t)stream);
-  return hip_check("verify launch");
+  return verify_call(mode, bs, gamma, vocab, temperature, seed, cycle, draft_ids, draft_lse,
+                     draft_logits, target_logits, target_dtype, out_tokens, out_tau, out_flags,
+                     ws, ws_bytes, stream);
 }
 
 int dstill_dloop_branches(int32_t bs, int32_t gamma, int32_t K, const int32_t *anchor,

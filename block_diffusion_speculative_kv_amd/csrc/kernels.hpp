@@ -141,6 +141,16 @@ int verify_plan_splits(int rows, int vocab);
 size_t verify_ws_bytes(int bs, int gamma, int nsplit, int nsamp);
 void launch_verify(const VerifyArgs &a, hipStream_t st);
 
+// Argument checks, workspace sizing and launch of one verification call
+// (api.cpp); the workspace is the caller's or the library's fixed scratch.
+int verify_call(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float temperature,
+                uint64_t seed, uint64_t cycle, const int32_t *draft_ids, const float *draft_lse,
+                const float *draft_logits, const void *target_logits, int32_t target_dtype,
+                int32_t *out_tokens, int32_t *out_tau, uint32_t *out_flags, void *ws,
+                size_t ws_bytes, void *stream);
+// Records msg as the thread's last error and returns code.
+int api_fail(int code, const char *msg);
+
 // ---- D-Loop second pass (dloop.hip) -----------------------------------------
 struct DloopArgs {
   int bs, gamma, K, mask_id;

@@ -268,6 +268,26 @@ int dstill_verify(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab, float 
                   int32_t *out_tau, uint32_t *out_flags, void *ws, size_t ws_bytes,
                   void *stream);
 
+/* ---- verification without a caller workspace ------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as dstill_verify, minus ws / ws_bytes: the
+ * workspace is a fixed array of DSTILL_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per device, held until the process ends.  The call allocates
+ * nothing (no hipMalloc / hipFree); its first call on a device looks up that
+ * device's array address.  Shapes whose dstill_verify_workspace_bytes exceeds
+ * the array are refused with EWORKSPACE before anything is enqueued (4 MiB
+ * covers bs up to 6060 at gamma 15, 31772 at gamma 1, at any vocabulary).  Every call
+ * on a device shares its array: calls that overlap on one device race, so
+ * order them (one stream, or events between streams). */
+#define DSTILL_NOALLOC_SCRATCH_BYTES (4u << 20)
+int dstill_verify_noalloc(int32_t mode, int32_t bs, int32_t gamma, int32_t vocab,
+                          float temperature, uint64_t seed, uint64_t cycle,
+                          const int32_t *draft_ids, const float *draft_lse,
+                          const float *draft_logits, const void *target_logits,
+                          int32_t target_dtype, int32_t *out_tokens, int32_t *out_tau,
+                          uint32_t *out_flags, void *stream);
+
 /* ---- D-Loop: looped second draft pass and joint K-branch verification ----
  * D-Loop page, section 3.1 (the prefix score after Eq. (4), Eq. (5)) and
  * section 3.3 (inference: joint verification of K branches).
