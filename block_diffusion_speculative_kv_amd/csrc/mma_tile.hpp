@@ -140,6 +140,7 @@ struct TileEngine {
   __device__ __forceinline__ static void mainloop(Smem &sm, const Loader &ld, int nst,
                                                   f32x4 (&acc)[NW][MW]) {
     constexpr int NKK = KT / 32;
+    static_assert(NKK == 2, "two 32-deep k-steps per stage");
     static_assert(!PERM || NW % 2 == 0, "permuted rows pair the tiles");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
@@ -158,73 +159,83 @@ struct TileEngine {
       for (int j = 0; j < MW; ++j)
         boff[j][kk] = tile_frag_off<KT>(wm * 16 * MW + 16 * j + r16, kk, g);
     }
-    // Fragments of both k-steps of a stage live in separate registers: the
-    // first k-step's reads are issued together, the second k-step's reads are
-    // interleaved with the first k-step's multiplies, and the second k-step's
-    // multiplies follow, so the matrix pipe waits for LDS once per stage
-    // rather than before every few products.
-    auto compute = [&](int s) {
+    // Fragments of one k-step: the second k-step of stage s is read while the
+    // first k-step's products run, and the first k-step of stage s + 1 is
+    // read (after the barrier that publishes its copies) while the second
+    // k-step's products run, so the matrix pipe never waits for LDS after a
+    // barrier.  Once every wave has read both k-steps of stage s, its
+    // buffers are free: the barrier in the middle of stage s lets the copies
+    // of stage s + NSW (weight) and s + 2 (activations) refill them.
+    bf16x8 fa[2][NW], fb[2][MW];
+    auto read = [&](int s, int kk, int set) {
       const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
       const char *xs = reinterpret_cast<const char *>(&sm.x[s % NSX][0]);
-      bf16x8 a[NKK][NW], b[NKK][MW];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+      for (int i = 0; i < NW; ++i) fa[set][i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
 #pragma unroll
-        for (int i = 0; i < NW; ++i) a[kk][i] = *reinterpret_cast<const bf16x8 *>(ws + aoff[i][kk]);
-#pragma unroll
-        for (int j = 0; j < MW; ++j) b[kk][j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-#pragma unroll
-          for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(a[kk][i], b[kk][j], acc[i][j]);
-      // schedule: reads of k-step 0, then (one read of k-step 1, RATIO
-      // products of k-step 0) while both last, then the remaining products
-      constexpr int NF = NW + MW, NP = NW * MW;
-      if constexpr (NKK == 2) {
-        constexpr int RATIO = NP / NF > 0 ? NP / NF : 1;
-        constexpr int INTER = NF * RATIO <= NP ? NF : NP / RATIO;
-        __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
-        static_for<INTER>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, RATIO, 0);
-        });
-        if constexpr (NF > INTER) __builtin_amdgcn_sched_group_barrier(0x100, NF - INTER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NP - INTER * RATIO, 0);
-      }
+      for (int j = 0; j < MW; ++j) fb[set][j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
     };
-    // Issue order: W0, X0, W1 .. W(NSW - 2); then per stage s, after its
-    // wait: X(s + 1), W(s + NSW - 1).  When stage s is waited for, the copies
-    // issued after X(s) are W(1 .. NSW - 2) at s = 0, and W(s + NSW - 2)
-    // later (those that exist); W(s) itself was issued before X(s), except
-    // with NSW = 2, where it follows X(s) and nothing may stay outstanding.
+    auto mma = [&](int set) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+#pragma unroll
+        for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(fa[set][i], fb[set][j], acc[i][j]);
+    };
+    // interleave: the NW + MW reads with the NW * MW products they overlap
+    auto interleave = [&]() {
+      constexpr int NF = NW + MW, NP = NW * MW;
+      constexpr int RATIO = NP / NF > 0 ? NP / NF : 1;
+      constexpr int INTER = NF * RATIO <= NP ? NF : NP / RATIO;
+      static_for<INTER>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, RATIO, 0);
+      });
+      if constexpr (NF > INTER) __builtin_amdgcn_sched_group_barrier(0x100, NF - INTER, 0);
+      if constexpr (NP > INTER * RATIO)
+        __builtin_amdgcn_sched_group_barrier(0x008, NP - INTER * RATIO, 0);
+    };
+    // Issue order: W0, X0, W1 .. W(NSW - 2) before stage 0; after the
+    // barrier that publishes stage s (s >= 0): X(s + 1), W(s + NSW - 1).  The
+    // wait for stage s + 1 then leaves in flight only the copies issued
+    // after X(s + 1), i.e. W(s + NSW - 1) if it exists (W(s + 1) was issued
+    // before X(s + 1) for NSW >= 2).
     ld.issue_w(sm, 0);
     ld.issue_x(sm, 0);
 #pragma unroll
     for (int p = 1; p <= NSW - 2; ++p)
       if (p < nst) ld.issue_w(sm, p);
-    for (int s = 0; s < nst; ++s) {
-      int later = 0;  // W stages allowed to stay in flight
-      if (NSW > 2) later = s == 0 ? min(NSW - 2, nst - 1) : (s + NSW - 2 < nst ? 1 : 0);
+    {
+      const int later = NSW > 2 ? min(NSW - 2, nst - 1) : 0;
       if (later == 0) {
         wait_vmcnt<0>();
       } else if (later == 1) {
         wait_vmcnt<NCW>();
       } else {
-        // only at s = 0, with stages 1 .. later issued behind X(0)
         static_for<(NSW > 3 ? NSW - 3 : 0)>([&](auto L) {
           constexpr int n = decltype(L)::value + 2;
           if (later == n) wait_vmcnt<n * NCW>();
         });
       }
-      // every wave's copies of stage s are visible after the barrier, and the
-      // buffers refilled next (last read at stage s - 1) are free
-      __syncthreads();
-      if (s + 1 < nst) ld.issue_x(sm, s + 1);
-      if (s + NSW - 1 < nst) ld.issue_w(sm, s + NSW - 1);
-      compute(s);
+    }
+    __syncthreads();
+    if (1 < nst) ld.issue_x(sm, 1);
+    if (NSW - 1 < nst) ld.issue_w(sm, NSW - 1);
+    read(0, 0, 0);
+    for (int s = 0; s < nst; ++s) {
+      read(s, 1, 1);
+      mma(0);
+      interleave();
+      if (s + 1 < nst) {
+        if (NSW > 2 && s + NSW - 1 < nst) wait_vmcnt<NCW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (s + 2 < nst) ld.issue_x(sm, s + 2);
+        if (s + NSW < nst) ld.issue_w(sm, s + NSW);
+      }
+      // (the last stage re-reads its own first k-step: unused, harmless)
+      read(min(s + 1, nst - 1), 0, 0);
+      mma(1);
+      interleave();
     }
     __syncthreads();  // every wave is done with the rings: the caller may reuse them
   }
