@@ -348,14 +348,15 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
     const double zd = (double)a.draft_logits[((long)b * G + k) * V + y];
     const double T = (double)a.temperature;
     const double lp = zt / T - lse;
-    const double lq = zd / T - (double)a.draft_lse[(long)b * G + k];
+    const float dl = a.draft_lse[(long)b * G + k];
+    const double lq = zd / T - (double)dl;
     const double ratio = exp(lp - lq);
     uint32_t raw[8];
     philox_block8(a.seed, 1u, (uint64_t)b, (uint64_t)k, a.cycle, 0, raw);
     const double u = (double)u24(raw[0]);
     ok = u < ratio;
     near = fabs(ratio - u) < (double)NEAR_BAND;
-    if (!isfinite(zd)) bad = 1;
+    if (!isfinite(zd) || !isfinite(dl)) bad = 1;
   }
   // first failing slot (gamma if all pass)
   const unsigned long long fail = __ballot(k < G && !ok);
@@ -383,9 +384,36 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
 }
 
 // ---- residual / bonus draw ---------------------------------------------------
+// Per (sequence, vocabulary split): the bonus / fallback draw argmax (lp + g)
+// over every id (lp = z_t / T - lse_t, g the Gumbel noise), and the residual
+// draw argmax (log max(0, p - q) + g).  Since max(0, p - q) <= p, the
+// residual score of an id is at most its lp + g, so the fp64 residual (two
+// exponentials and a logarithm) is evaluated only where it can matter: the
+// split is taken in windows of VS_GPT groups of 8 ids per thread, kept in
+// registers; with U the window's largest lp + g, the ids with lp + g >= U - 4
+// are evaluated first, then those down to U - 16, then all the rest, and the
+// walk stops as soon as the best residual score found lies a near-tie band
+// (plus a rounding margin) above the current threshold: no id left out can
+// then win, nor come within the band of the winner (which is all the
+// runner-up score is used for).  A block whose residual is empty (p <= q
+// everywhere) evaluates every id, as before.
+constexpr int VS_GPT = 3;
+constexpr int VS_THREADS = 256;
+
+__device__ __forceinline__ double block_max_d(double v, double *sh) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, WAVE));
+  __syncthreads();  // sh is free (earlier readers are done)
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = sh[0];
+  for (int i = 1; i < VS_THREADS / 64; ++i) r = fmax(r, sh[i]);
+  return r;
+}
+
 template <typename TT>
-__global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) {
-  __shared__ VSampPart red[4];
+__global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, VerifyWs w) {
+  __shared__ VSampPart red[VS_THREADS / 64];
+  __shared__ double shd[VS_THREADS / 64];
   const int b = blockIdx.x, sp = blockIdx.y;
   const int G = a.gamma, V = a.vocab;
   const int ks = w.kstar[b];
@@ -403,38 +431,92 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
   // vector loads need rows of whole 8-id groups on 16-byte boundaries
   const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
                    (bonus || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
-  for (int vb = v0 + 8 * threadIdx.x; vb < v1; vb += 8 * blockDim.x) {
-    // the 8 target and draft logits are loaded before the noise is drawn, as
-    // vectors where the row allows (one round trip instead of one per id)
-    float xt[8], xd[8];
-    if (vec && vb + 8 <= v1) {
-      ld8(zt + vb, xt);
-      if (!bonus) ld8(zd + vb, xd);
-    } else {
+  constexpr int WIN = 8 * VS_GPT * VS_THREADS;  // ids per window
+  for (int wb = v0; wb < v1; wb += WIN) {
+    double lpv[VS_GPT][8];
+    float gv[VS_GPT][8], xdv[VS_GPT][8];
+    double ub = -INFINITY;  // this thread's largest lp + g in the window
+#pragma unroll
+    for (int gi = 0; gi < VS_GPT; ++gi) {
+      const int vb = wb + 8 * (threadIdx.x + gi * VS_THREADS);
+      // the 8 target and draft logits are loaded before the noise is drawn,
+      // as vectors where the row allows
+      float xt[8], xd[8];
+      if (vec && vb + 8 <= v1) {
+        ld8(zt + vb, xt);
+        if (!bonus) ld8(zd + vb, xd);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xt[e] = vb + e < v1 ? ld(zt, vb + e) : 0.f;
+          xd[e] = !bonus && vb + e < v1 ? zd[vb + e] : 0.f;
+        }
+      }
+      uint32_t raw[8];
+      if (vb < v1)
+        philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xt[e] = vb + e < v1 ? ld(zt, vb + e) : 0.f;
-        xd[e] = !bonus && vb + e < v1 ? zd[vb + e] : 0.f;
+        const int v = vb + e;
+        lpv[gi][e] = -INFINITY;
+        gv[gi][e] = 0.f;
+        xdv[gi][e] = xd[e];
+        if (v >= v1) continue;
+        const float g = gumbel_of(raw[e]);
+        const double lp = (double)xt[e] / T - lse_t;
+        lpv[gi][e] = lp;
+        gv[gi][e] = g;
+        d2_push(pp, lp + (double)g, v);
+        ub = fmax(ub, lp + (double)g);
+        if (!bonus && !isfinite((double)xd[e])) bad = 1;
       }
     }
-    uint32_t raw[8];
-    philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
+    if (bonus) continue;
+    const double U = block_max_d(ub, shd);
+    if (U == -INFINITY) continue;  // nothing finite in this window
+    // thresholds, highest first; ids in [t, t_prev) are evaluated in a round
+    double tprev = INFINITY;
+#pragma unroll 1
+    for (int round = 0; round < 3; ++round) {
+      const double t = round == 0 ? U - 4.0 : round == 1 ? U - 16.0 : -INFINITY;
+      // candidates of this round as a bit mask over the thread's ids, then
+      // one fp64 evaluation per candidate (the values picked by a select
+      // chain, so the evaluation code exists once)
+      uint32_t cand = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int v = vb + e;
-      if (v >= v1) break;
-      const double g = (double)gumbel_of(raw[e]);
-      const double lp = (double)xt[e] / T - lse_t;
-      d2_push(pp, lp + g, v);
-      if (!bonus) {
-        const double zdv = (double)xd[e];
-        if (!isfinite(zdv)) bad = 1;
+      for (int gi = 0; gi < VS_GPT; ++gi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double u = lpv[gi][e] + (double)gv[gi][e];
+          // (a margin above the exact bound: log(exp(lp)) may round above lp)
+          if (lpv[gi][e] > -INFINITY && u + 1e-9 >= t && u + 1e-9 < tprev)
+            cand |= 1u << (8 * gi + e);
+        }
+      while (cand) {
+        const int i = __builtin_ctz(cand);
+        cand &= cand - 1;
+        double lp = 0.0;
+        float g = 0.f, xdf = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < VS_GPT; ++gi)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (i == 8 * gi + e) {
+              lp = lpv[gi][e];
+              g = gv[gi][e];
+              xdf = xdv[gi][e];
+            }
+        const int v = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS) + (i & 7);
+        const double zdv = (double)xdf;
         const double r = exp(lp) - exp(zdv / T - lse_d);
         if (r > 0.0) {
           any_r = 1;
-          d2_push(rr, log(r) + g, v);
+          d2_push(rr, log(r) + (double)g, v);
         }
       }
+      tprev = t;
+      const double best = block_max_d(rr.best, shd);
+      if (best >= t + (double)NEAR_BAND + 1e-9) break;
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -456,7 +538,7 @@ __global__ __launch_bounds__(256) void vsample_kernel(VerifyArgs a, VerifyWs w) 
   __syncthreads();
   if (threadIdx.x == 0) {
     VSampPart t = red[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+    for (int i = 1; i < VS_THREADS / 64; ++i) {
       const VSampPart u = red[i];
       D2 x{t.best_r, t.second_r, t.idx_r}, y{u.best_r, u.second_r, u.idx_r};
       x = d2_merge(x, y);
@@ -520,7 +602,7 @@ static void launch_typed(const VerifyArgs &a, hipStream_t st) {
   const int dw = a.gamma + 1 < 16 ? a.gamma + 1 : 16;  // one wave per target row, up to 16
   hipLaunchKernelGGL(vdecide_kernel<TT>, dim3(a.bs), dim3(64 * dw), 0, st, a, w);
   if (a.mode == 1) {
-    hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsamp), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(vsample_kernel<TT>, dim3(a.bs, a.nsamp), dim3(VS_THREADS), 0, st, a, w);
     hipLaunchKernelGGL(vfinish_kernel, dim3(a.bs), dim3(64), 0, st, a, w);
   }
 }

@@ -34,7 +34,9 @@ FLAG_NEAR_TIE_TARGET = 1      # target argmax top-2 gap below NEAR
 FLAG_NEAR_THRESHOLD = 2       # |p/q - u| below NEAR at a deciding test
 FLAG_NEAR_TIE_SAMPLE = 4      # residual / bonus Gumbel-max top-2 gap below NEAR
 FLAG_ZERO_RESIDUAL = 8        # max(0, p - q) summed to zero: drew from p
-FLAG_BAD_INPUT = 16           # draft id out of range or non-finite logits
+FLAG_BAD_INPUT = 16           # draft id out of range or a non-finite logit read
+# (tokens, tau and the other flags of a sequence flagged BAD_INPUT follow from
+# the clamped ids and the non-finite values as they fall: unspecified)
 
 
 def _argmax_gap(score):
@@ -78,18 +80,29 @@ def verify_rs(zt, zd, y, temperature, u, gumbel_at):
     y = np.asarray(y)
     gamma = y.shape[0]
     flags = 0
-    if np.any((y < 0) | (y >= zt.shape[1])) or not (
-            np.all(np.isfinite(zt)) and np.all(np.isfinite(zd))):
-        flags |= FLAG_BAD_INPUT
+    # Data faults: a draft id out of range, or a non-finite value among the
+    # inputs the accept tests read -- any target logit (each row's
+    # log-sum-exp needs all of it), and for every slot k the draft logit of
+    # y_k and the draft row's log-sum-exp -- or in the draft row of the first
+    # rejection (the residual reads all of it).
+    bad = np.any((y < 0) | (y >= zt.shape[1])) or not np.all(np.isfinite(zt))
     lt = logsumexp(zt, axis=-1)
-    ld = logsumexp(zd, axis=-1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ld = logsumexp(zd, axis=-1)
+    yc = np.clip(y, 0, zt.shape[1] - 1)
+    if not (np.all(np.isfinite(zd[np.arange(gamma), yc])) and np.all(np.isfinite(ld))):
+        bad = True
+    if bad:
+        flags |= FLAG_BAD_INPUT
     for k in range(gamma):
-        yk = int(y[k])
+        yk = int(yc[k])
         ratio = np.exp((zt[k, yk] - lt[k]) - (zd[k, yk] - ld[k]))
         if abs(ratio - u[k]) < NEAR:
             flags |= FLAG_NEAR_THRESHOLD
         if u[k] < ratio:
             continue
+        if not np.all(np.isfinite(zd[k])):
+            flags |= FLAG_BAD_INPUT
         p = np.exp(zt[k] - lt[k])
         q = np.exp(zd[k] - ld[k])
         r = np.maximum(p - q, 0.0)
@@ -103,12 +116,12 @@ def verify_rs(zt, zd, y, temperature, u, gumbel_at):
         v, gap = _argmax_gap(score)
         if gap < NEAR:
             flags |= FLAG_NEAR_TIE_SAMPLE
-        return [int(t) for t in y[:k]] + [v], k + 1, flags
+        return [int(t) for t in yc[:k]] + [v], k + 1, flags
     score = zt[gamma] - lt[gamma] + gumbel_at(gamma)
     v, gap = _argmax_gap(score)
     if gap < NEAR:
         flags |= FLAG_NEAR_TIE_SAMPLE
-    return [int(t) for t in y] + [v], gamma + 1, flags
+    return [int(t) for t in yc] + [v], gamma + 1, flags
 
 
 def accept_uniforms(seed, seq, cycle, gamma):

@@ -154,3 +154,56 @@ def test_rs_replays_with_same_counter_and_changes_with_cycle():
     for x, z in zip(a, b):
         assert np.array_equal(x, z)
     assert not all(np.array_equal(x, z) for x, z in zip(a, c))
+
+
+@pytest.mark.parametrize("mode", ["greedy", "rs"])
+def test_non_finite_inputs_flag_like_the_oracle(mode):
+    """BAD_INPUT marks a non-finite value among the inputs the decisions read:
+    any target logit; in rejection sampling also the draft logit of each
+    slot's id, each draft row's log-sum-exp, and the whole draft row of the
+    first rejection.  The flag must agree bit for bit; a flagged sequence's
+    tokens are unspecified but tau stays in range; unflagged sequences agree
+    as usual."""
+    dev = device()
+    bs, gamma, V = 10, 7, 5003
+    tdt = "f32" if mode == "greedy" else "bf16"
+    zt, zt_np, zd, zd_np = _rs_inputs(bs, gamma, V, tdt, "correlated", seed=41)
+    zt_np = zt_np.copy()
+    zd_np = zd_np.copy()
+    rng = np.random.default_rng(3)
+    y_np = np.argmax(zd_np + rng.gumbel(size=zd_np.shape), -1)
+    if mode == "greedy":
+        y_np[:, :3] = np.argmax(zt_np[:, :3], -1)   # a few accepted slots
+    nan, inf = np.nan, np.inf
+    zt_np[0, gamma, 17] = nan                        # target bonus row
+    zt_np[1, 0, 4000] = inf                          # target row 0
+    zt_np[2, 3, 5] = -inf                            # target row 3
+    if mode == "rs":
+        zd_np[3, 1, y_np[3, 1]] = inf                 # draft logit at y
+        zd_np[4, 2, (y_np[4, 2] + 1) % V] = nan       # draft row 2's log-sum-exp
+        zt_np[5, 0, y_np[5, 0]] = -60.0               # slot 0 rejected ...
+        zd_np[5, 0, (y_np[5, 0] + 9) % V] = -inf      # ... its row holds -inf
+        zd_np[7, 0, (y_np[7, 0] + 1) % V] = -inf      # away from y in an accepted row:
+        zt_np[7, 0, y_np[7, 0]] = zd_np[7, 0, y_np[7, 0]] + 8.0   # unread, no flag
+    zt_t = torch.from_numpy(zt_np).to(zt.dtype).to(dev)
+    zt_np = to_np(zt_t)                              # what the kernel sees (bf16 rounding)
+    y = torch.from_numpy(y_np.astype(np.int32)).to(dev)
+    if mode == "greedy":
+        gpu = _gpu_verify(bd.VERIFY_GREEDY, zt_t, y)
+        ref = ov.verify_batch("greedy", zt_np, y_np)
+    else:
+        with np.errstate(invalid="ignore", over="ignore"):
+            lse_np = logsumexp(zd_np, axis=-1)
+        zd_t = torch.from_numpy(zd_np.astype(np.float32)).to(dev)
+        lse = torch.from_numpy(lse_np.astype(np.float32)).to(dev)
+        gpu = _gpu_verify(bd.VERIFY_RS, zt_t, y, zd=zd_t, lse=lse, seed=5, cycle=2)
+        ref = ov.verify_batch("rs", zt_np, y_np, zd=zd_np.astype(np.float32).astype(np.float64),
+                              seed=5, cycle=2)
+    gbad = (gpu[2] & bd.FLAG_BAD_INPUT) != 0
+    rbad = (ref[2] & bd.FLAG_BAD_INPUT) != 0
+    assert np.array_equal(gbad, rbad), f"{mode}: BAD_INPUT {gbad.astype(int)} vs {rbad.astype(int)}"
+    want_bad = [0, 1, 2] + ([3, 4, 5] if mode == "rs" else [])
+    assert sorted(np.nonzero(gbad)[0].tolist()) == want_bad
+    assert np.all((gpu[1] >= 1) & (gpu[1] <= gamma + 1))
+    ok = ~gbad
+    _check(tuple(x[ok] for x in gpu), tuple(x[ok] for x in ref), f"{mode} unflagged rows")

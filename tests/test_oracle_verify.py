@@ -268,3 +268,56 @@ def test_shared_gumbel_coupling_bound():
         assert agree >= (1 - d) / (1 + d) - 4 * np.sqrt(0.25 / n)
         # marginals are still exact draws from P and Q
         assert stats.chisquare(np.bincount(x, minlength=V), P * n).pvalue > 1e-4
+
+
+# -- data faults: BAD_INPUT covers exactly the values the decisions read ------
+
+def _rs_case(seed=3, gamma=4, V=12):
+    rng = np.random.default_rng(seed)
+    zt = rng.normal(0, 2, (gamma + 1, V))
+    zd = rng.normal(0, 2, (gamma, V))
+    y = rng.integers(0, V, gamma)
+    u = np.full(gamma, 1e-3)          # every finite test accepts unless p/q tiny
+    g = lambda k: philox.gumbel_row(0, philox.PURPOSE_RESIDUAL, 0, k, 0, V)
+    return zt, zd, y, u, g
+
+
+@pytest.mark.parametrize("where", ["target_bonus_row", "draft_at_y", "draft_lse", "rejected_row"])
+def test_rs_bad_input_on_values_read(where):
+    from oracle.verify import FLAG_BAD_INPUT
+    zt, zd, y, u, g = _rs_case()
+    if where == "target_bonus_row":
+        zt[-1, 5] = np.nan                  # read by the last row's log-sum-exp
+    elif where == "draft_at_y":
+        zd[1, y[1]] = np.inf                # the accept test of slot 1 reads it
+    elif where == "draft_lse":
+        zd[2, (y[2] + 1) % 12] = np.nan     # not at y, but in the row's log-sum-exp
+    else:
+        zt[0, y[0]] = -30.0                 # slot 0 is rejected ...
+        zd[0, (y[0] + 1) % 12] = -np.inf    # ... and the residual reads its whole row
+    _, tau, f = verify_rs(zt, zd, y, 1.0, u, g)
+    assert f & FLAG_BAD_INPUT and 1 <= tau <= 5
+
+
+def test_rs_unread_infinite_draft_value_is_not_a_fault():
+    """-inf in an accepted draft row away from y changes no value the
+    decisions read (its row's log-sum-exp stays finite): no flag, and the
+    same outcome as a very negative finite logit."""
+    from oracle.verify import FLAG_BAD_INPUT
+    zt, zd, y, u, g = _rs_case()
+    zd2 = zd.copy()
+    zd2[0, (y[0] + 1) % 12] = -np.inf
+    zd3 = zd.copy()
+    zd3[0, (y[0] + 1) % 12] = -1e300
+    a = verify_rs(zt, zd2, y, 1.0, u, g)
+    b = verify_rs(zt, zd3, y, 1.0, u, g)
+    assert a[2] & FLAG_BAD_INPUT == 0 and a == b and a[1] >= 2
+
+
+def test_rs_out_of_range_id_flagged_and_clamped():
+    from oracle.verify import FLAG_BAD_INPUT
+    zt, zd, y, u, g = _rs_case()
+    y = y.copy()
+    y[2] = 12                                # == V
+    toks, tau, f = verify_rs(zt, zd, y, 1.0, u, g)
+    assert f & FLAG_BAD_INPUT and all(0 <= t < 12 for t in toks) and 1 <= tau <= 5
