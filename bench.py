@@ -295,11 +295,19 @@ def main():
     if cfg["dtype"] != "bf16":
         head_kernel = "lm_head_kernel<float>"
     else:
-        r = cyc.rows
-        head_kernel = ("lm_head_stream_kernel" if r <= 16 else
-                       "lm_head_lds_kernel (%d ids x %d rows tile)" % (
-                           (64, 32) if r <= 32 else (64, 64) if r <= 64
-                           else (128, 160) if r <= 160 else (256, 256)))
+        # mirrors launch_lm_head: the weight-streaming kernel up to 160 rows
+        # (128-deep stages up to 64 rows, 64-deep beyond, when they divide the
+        # depth), the tile engine otherwise
+        r, d = cyc.rows, cfg["hidden"]
+        rt = (r + 15) // 16
+        ks = 128 if rt <= 4 else 64
+        if r <= 160 and d % ks == 0:
+            head_kernel = "lm_head_stream_kernel (%d row tiles, %d-deep stages)" % (
+                rt if rt <= 4 else rt + (rt & 1), ks)
+        else:
+            head_kernel = "lm_head_lds_kernel (%d ids x %d rows tile)" % (
+                (64, 32) if r <= 32 else (64, 64) if r <= 64
+                else (128, 160) if r <= 160 else (256, 256))
     head_kernel += " (+lm_combine_kernel)"
     traffic = None
     if args.workload == "q8b_bs32_rs":

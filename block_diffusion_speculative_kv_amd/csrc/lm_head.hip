@@ -90,11 +90,13 @@ __device__ __forceinline__ RowStat rowstat_shfl_xor(const RowStat &a, int o) {
 
 // Reduction of one row's logits held by a lane: NP pairs of 8 consecutive ids
 // starting at vw + 32p + 8g.  Writes the logits if asked, draws the Gumbel
-// noise (one Philox block per 8 ids), and returns the lane's statistics
-// merged over the wave's four lane groups.
+// noise (one Philox block per 8 ids; or takes gpre, the same stream's noise
+// drawn once for several rows), and returns the lane's statistics merged over
+// the wave's four lane groups.
 template <int NP, bool STORE = true>
 __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw, int g,
-                                                float (&zz)[NP][8]) {
+                                                float (&zz)[NP][8],
+                                                const float (*gpre)[8] = nullptr) {
   const int V = a.vocab;
   const float invT = 1.0f / a.temperature;
   const bool gumbel = a.mode != 0;
@@ -112,7 +114,11 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
   for (int p = 0; p < NP; ++p) {
     const int v0 = vw + 32 * p + 8 * g;
     float gn[8];
-    if (gumbel && rvalid && v0 < V) {
+    if (gpre != nullptr) {
+      // noise drawn once for rows that share their stream (shared mode)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gn[e] = gpre[p][e];
+    } else if (gumbel && rvalid && v0 < V) {
       uint32_t raw[8];
       if (a.mode == 2)
         philox_block8(a.seed, 3u, 0, (uint64_t)slot, a.cycle, (uint64_t)(v0 >> 3), raw);
@@ -344,40 +350,67 @@ constexpr int head_stage_wave_rows() {
   return w;
 }
 
-// Weight-streaming variant for up to 64 rows (bf16): the weight tile of 128
-// vocabulary rows streams through a ring of LDS stages of k = 128 (256
-// contiguous bytes of every row, 32 KB), filled by direct global->LDS copies
-// NS - 1 stages ahead (four stages, so ~96 KB per compute unit in flight, for
-// up to 32 rows; three for 33..64 rows, whose larger hidden slices leave room
-// for three).  The slice of the 16 RT hidden rows (4 RT KB) rides in the same
-// ring.  The kernel also takes several row blocks, those of one vocabulary
-// block placed on one XCD next to each other (workgroup i runs on XCD i mod
-// 8); measured on the 8B-shaped head that was slower than the 128 x 160 tile
-// from 100 rows on (144 rows: 473 against 377 us), so the launch uses one row
-// block.  LDS rows are unpadded and XOR-swizzled per 16-byte chunk, so the 16
-// rows one fragment read touches (in the permuted vocabulary order) fall on
-// distinct banks.
-constexpr int HS_K = 128;       // k per stage
-constexpr int HS_ROWS = 128;    // vocabulary rows per workgroup (32 per wave)
-constexpr int HS_WC = HS_ROWS * HS_K * 2 / 1024 / 4;  // weight copies per wave per stage
-constexpr int HS_MAX_RT = 4;    // row tiles of 16 per workgroup
+// Weight-streaming variant for up to 160 rows (bf16): the weight tile of 128
+// vocabulary rows streams through a ring of LDS stages (the 2 KS contiguous
+// bytes of every row), filled by direct global->LDS copies NS - 1 stages
+// ahead; the slice of the 16 RT hidden rows rides in the same ring.  Up to
+// 64 rows the stages are 128 deep (four stages up to 32 rows, three beyond);
+// from 65 rows 64 deep, four stages (measured on the 8B-shaped head at 144
+// rows: 397 us for the 128 x 160 tile of the tile engine, 371 us here in
+// argmax mode; two vocabulary tile pairs per wave, 256 ids per workgroup,
+// took 403 us: 594 workgroups round to three passes over 256 compute units).
+// The kernel also takes several row blocks, those of one vocabulary block
+// placed on one XCD next to each other (workgroup i runs on XCD i mod 8); the
+// launch uses one.  LDS rows are unpadded and XOR-swizzled per 16-byte chunk,
+// so the 16 rows one fragment read touches (in the permuted vocabulary order)
+// fall on distinct banks.
+constexpr int HS_MAX_RT = 10;   // row tiles of 16 per workgroup
 
-template <int RT>
+// Stage geometry: TPW pairs of 16-id vocabulary tiles per wave (HS rows =
+// 128 TPW per workgroup of 4 waves), KS = k per stage: 128 with one pair (up
+// to 4 row tiles), 64 with two pairs (5 to 10 row tiles: each hidden
+// fragment read from LDS feeds four products instead of two, and the 80-160
+// hidden rows of a stage still leave room for a three-deep ring).  A stage
+// row is 2 KS bytes; one copy (64 lanes x 16 bytes) fills 512 / KS rows.
+template <int RT, int KS, int TPW>
 struct HsStage {
-  bf16 w[HS_ROWS * HS_K];
-  bf16 x[16 * RT * HS_K];
+  bf16 w[128 * TPW * KS];
+  bf16 x[16 * RT * KS];
 };
-template <int RT>
-constexpr int hs_stages() { return RT <= 2 ? 4 : 3; }
-static_assert(sizeof(HsStage<2>) * hs_stages<2>() <= 160 * 1024, "ring fits LDS");
-static_assert(sizeof(HsStage<4>) * hs_stages<4>() <= 160 * 1024, "ring fits LDS");
+template <int RT, int KS, int TPW>
+constexpr int hs_stages() {
+  constexpr int n = (int)((160 * 1024) / sizeof(HsStage<RT, KS, TPW>));
+  return n < 4 ? n : 4;
+}
+static_assert(hs_stages<2, 128, 1>() == 4 && hs_stages<4, 128, 1>() == 3, "ring depths");
+static_assert(hs_stages<10, 64, 1>() == 4, "ring depth of the 160-row slices");
 
-__device__ __forceinline__ int hs_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
+// 16-byte chunk swizzles.  KS = 128 (16 chunks per row): weight rows on
+// bits {0, 1, 3, 4}, the bits that vary over the 16 (permuted) rows of one
+// fragment read; hidden rows on bits 0..3.  KS = 64 (8 chunks, two rows per
+// 256-byte bank window): weight rows on bits {1, 3, 4}, hidden rows on bits
+// {1, 2, 3} (bit 0 picks the half of the bank window).
+template <int KS>
+__device__ __forceinline__ int hs_wswz(int row) {
+  if (KS == 128) return (row & 3) | ((row >> 1) & 12);
+  return ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+template <int KS>
+__device__ __forceinline__ int hs_xswz(int row) {
+  if (KS == 128) return row & 15;
+  return (row >> 1) & 7;
+}
 
-template <int RT>
+template <int RT, int KS, int TPW>
 __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb) {
-  constexpr int NS = hs_stages<RT>(), OPS = HS_WC + RT;  // copies per wave per stage
-  __shared__ HsStage<RT> ring[NS];
+  constexpr int ROWS = 128 * TPW;                               // vocabulary rows per workgroup
+  constexpr int CPR = KS / 8, CROWS = 64 / CPR;                 // chunks per row, rows per copy
+  constexpr int WC = ROWS * KS * 2 / 1024 / 4;                  // weight copies per wave per stage
+  constexpr int XC = 16 * RT * KS * 2 / 1024 / 4;               // hidden copies per wave per stage
+  static_assert(16 * RT * KS * 2 % 4096 == 0, "hidden copies split evenly over the 4 waves");
+  constexpr int NS = hs_stages<RT, KS, TPW>(), OPS = WC + XC;   // copies per wave per stage
+  static_assert(NS >= 2, "ring");
+  __shared__ HsStage<RT, KS, TPW> ring[NS];
   // XCD-aware mapping of the linear workgroup id to (vocab block, row block)
   const int L = blockIdx.x;
   const int xcd = L % NXCD, slot = L / NXCD;
@@ -386,37 +419,39 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int V = a.vocab, d = a.d;
-  const int v0 = vb * HS_ROWS, r0 = rb * 16 * RT;
+  const int v0 = vb * ROWS, r0 = rb * 16 * RT;
   auto hrow = [&](int r) { return (long)(r / a.rows_per_seq) * a.seq_stride + r % a.rows_per_seq; };
   const long h0 = hrow(r0);
   const char *wblk = reinterpret_cast<const char *>((const bf16 *)a.w + (long)v0 * d);
   const char *xblk = reinterpret_cast<const char *>((const bf16 *)a.hidden + h0 * d);
-  // weight copy j of wave w fills LDS vectors 64 (4 j + w) + lane: tile row
-  // 4 (4 j + w) + lane / 16, physical chunk lane % 16; hidden copy j of wave
-  // w fills rows 4 (4 j + w) + lane / 16 of the stage's 16 RT x 128 slice
-  uint32_t goff[HS_WC];
+  // copy j of wave w fills LDS vectors 64 (4 j + w) + lane: stage row
+  // CROWS (4 j + w) + lane / CPR, physical chunk lane % CPR (weight and
+  // hidden alike, each in its own part of the stage)
+  uint32_t goff[WC];
 #pragma unroll
-  for (int j = 0; j < HS_WC; ++j) {
-    const int row = 4 * (4 * j + wave) + (lane >> 4), pc = lane & 15;
-    goff[j] = (uint32_t)((min(v0 + row, V - 1) - v0) * d * 2 + 16 * (pc ^ hs_swz(row)));
+  for (int j = 0; j < WC; ++j) {
+    const int row = CROWS * (4 * j + wave) + lane / CPR, pc = lane % CPR;
+    goff[j] = (uint32_t)((min(v0 + row, V - 1) - v0) * d * 2 + 16 * (pc ^ hs_wswz<KS>(row)));
   }
-  uint32_t xoff[RT];
+  uint32_t xoff[XC];
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    const int row = 4 * (4 * j + wave) + (lane >> 4), pc = lane & 15;
+  for (int j = 0; j < XC; ++j) {
+    const int row = CROWS * (4 * j + wave) + lane / CPR, pc = lane % CPR;
     const int r = min(r0 + row, a.rows - 1);
-    xoff[j] = (uint32_t)((hrow(r) - h0) * d * 2 + 16 * (pc ^ (row & 15)));
+    xoff[j] = (uint32_t)((hrow(r) - h0) * d * 2 + 16 * (pc ^ hs_xswz<KS>(row)));
   }
-  // A-operand rows of this wave's tile pair (permuted vocabulary order)
-  int arow[2];
+  // A-operand rows of this wave's tiles (permuted vocabulary order: tile
+  // 2q + t row 4 i + e is id 32 q + 8 i + 4 t + e of the wave's band)
+  int arow[2 * TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) arow[t] = 32 * wave + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-  f32x4 acc[2][RT];
+  for (int t = 0; t < 2 * TPW; ++t)
+    arow[t] = 32 * (TPW * wave + (t >> 1)) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3);
+  f32x4 acc[2 * TPW][RT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2 * TPW; ++t)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = d / HS_K;
+  const int nst = d / KS;
   // each block starts its k walk at a different stage, so concurrent blocks
   // do not sweep the same column offset of their rows at the same time (the
   // row blocks of one vocabulary block share the start, so they read the
@@ -424,33 +459,14 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb
   const int rot = (vb * 5) % nst;
   auto kst = [&](int s) { return s + rot < nst ? s + rot : s + rot - nst; };
   auto issue = [&](int s) {
-    const long k0 = (long)kst(s) * HS_K * 2;
-    HsStage<RT> &st = ring[s % NS];
+    const long k0 = (long)kst(s) * KS * 2;
+    HsStage<RT, KS, TPW> &st = ring[s % NS];
     const uint32_t wl = lds_u32(&st.w[0]) + wave * 1024;
 #pragma unroll
-    for (int j = 0; j < HS_WC; ++j) dma16(wblk + k0, goff[j], wl + j * 4096);
+    for (int j = 0; j < WC; ++j) dma16(wblk + k0, goff[j], wl + j * 4096);
     const uint32_t xl = lds_u32(&st.x[0]) + wave * 1024;
 #pragma unroll
-    for (int j = 0; j < RT; ++j) dma16(xblk + k0, xoff[j], xl + j * 4096);
-  };
-  auto compute = [&](const HsStage<RT> &st) {
-    const char *ws = reinterpret_cast<const char *>(&st.w[0]);
-    const char *xs = reinterpret_cast<const char *>(&st.x[0]);
-#pragma unroll
-    for (int kk = 0; kk < HS_K / 32; ++kk) {
-      bf16x8 xf[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        xf[rt] = *reinterpret_cast<const bf16x8 *>(xs + (16 * rt + r16) * HS_K * 2 +
-                                                   16 * ((kk * 4 + g) ^ r16));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
-            ws + arow[t] * HS_K * 2 + 16 * ((kk * 4 + g) ^ hs_swz(arow[t])));
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[t][rt] = Mma<bf16>::run(fa, xf[rt], acc[t][rt]);
-      }
-    }
+    for (int j = 0; j < XC; ++j) dma16(xblk + k0, xoff[j], xl + j * 4096);
   };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
@@ -466,20 +482,59 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb
     // next (read at stage s - 1) is free
     __syncthreads();
     if (s + NS - 1 < nst) issue(s + NS - 1);
-    compute(ring[s % NS]);
+    // (written out here rather than in a lambda over acc: with many row
+    // tiles the compiler would keep a captured accumulator array in memory)
+    const char *ws = reinterpret_cast<const char *>(&ring[s % NS].w[0]);
+    const char *xs = reinterpret_cast<const char *>(&ring[s % NS].x[0]);
+#pragma unroll
+    for (int kk = 0; kk < KS / 32; ++kk) {
+      bf16x8 xf[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        xf[rt] = *reinterpret_cast<const bf16x8 *>(
+            xs + (16 * rt + r16) * KS * 2 + 16 * ((kk * 4 + g) ^ hs_xswz<KS>(16 * rt + r16)));
+#pragma unroll
+      for (int t = 0; t < 2 * TPW; ++t) {
+        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
+            ws + arow[t] * KS * 2 + 16 * ((kk * 4 + g) ^ hs_wswz<KS>(arow[t])));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[t][rt] = Mma<bf16>::run(fa, xf[rt], acc[t][rt]);
+      }
+    }
   }
   __syncthreads();
-  // epilogue: per row, the wave's 32 ids, then the four waves in LDS
+  // epilogue: per row, the wave's 32 TPW ids, then the four waves in LDS
   RowStat(*red)[16 * RT] = reinterpret_cast<RowStat(*)[16 * RT]>(&ring[0]);
-  const int vw = v0 + 32 * wave;
+  static_assert(4 * 16 * RT * sizeof(RowStat) <= sizeof(ring), "row records fit the ring");
+  const int vw = v0 + 32 * TPW * wave;
+  // Shared-noise mode draws one stream per block slot: when the slots of
+  // this lane's rows 16 rt + r16 are all r16 % rows_per_seq (rows_per_seq
+  // divides 16), the lane draws that stream's noise once for all its rows.
+  float gsh[TPW][8];
+  const bool share = a.mode == 2 && 16 % a.rows_per_seq == 0;
+  if (share) {
+    const int sl = r16 % a.rows_per_seq;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float zz[1][8];
+    for (int p = 0; p < TPW; ++p) {
+      const int gv0 = vw + 32 * p + 8 * g;
+      uint32_t raw[8];
+      philox_block8(a.seed, 3u, 0, (uint64_t)sl, a.cycle, (uint64_t)(gv0 >> 3), raw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zz[0][e] = acc[e >> 2][rt][e & 3];
-    RowStat st2 = lane_rowstat<1>(a, r0 + 16 * rt + r16, vw, g, zz);
-    if (g == 0) red[wave][16 * rt + r16] = st2;
+      for (int e = 0; e < 8; ++e) gsh[p][e] = gv0 < V ? gumbel_of(raw[e]) : 0.f;
+    }
   }
+  // (a compile-time loop: a rolled one would index acc at run time and put
+  // it in memory)
+  static_for<RT>([&](auto RTI) {
+    constexpr int rt = decltype(RTI)::value;
+    float zz[TPW][8];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zz[p][e] = acc[2 * p + (e >> 2)][rt][e & 3];
+    RowStat st2 = lane_rowstat<TPW>(a, r0 + 16 * rt + r16, vw, g, zz, share ? gsh : nullptr);
+    if (g == 0) red[wave][16 * rt + r16] = st2;
+  });
   __syncthreads();
   if (threadIdx.x < 16 * RT && r0 + (int)threadIdx.x < a.rows) {
     const int i = threadIdx.x;
@@ -490,10 +545,10 @@ __global__ __launch_bounds__(256) void lm_head_stream_kernel(HeadArgs a, int nrb
   }
 }
 
-template <int RT>
+template <int RT, int KS, int TPW>
 static void launch_stream(const HeadArgs &a, int nrb, hipStream_t st) {
   const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nrb);
-  hipLaunchKernelGGL((lm_head_stream_kernel<RT>), grid, dim3(256), 0, st, a, nrb);
+  hipLaunchKernelGGL((lm_head_stream_kernel<RT, KS, TPW>), grid, dim3(256), 0, st, a, nrb);
 }
 
 // One workgroup per row merges the row's vocabulary-block records in two
@@ -600,25 +655,30 @@ static void launch_head_tile(const HeadArgs &a, dim3 grid, int nmb, hipStream_t 
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
-  // up to 64 rows stream the weight through an LDS ring; more rows go
-  // through the tile engine, with a tile fitted to the row count (both
-  // address a block's hidden rows with 32-bit byte offsets)
+  // up to 160 rows stream the weight through an LDS ring; more rows (and
+  // depths the streaming stages do not divide) go through the tile engine,
+  // with a tile fitted to the row count (both address a block's hidden rows
+  // with 32-bit byte offsets)
   int BN = HeadMidTile::BN, BM = HeadMidTile::BM;
   if (a.rows <= 32) BN = 64, BM = 32;
   else if (a.rows <= 64) BN = 64, BM = 64;
   else if (a.rows > 160) BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
-  // streaming path: up to 64 rows, one row block of 16 RT rows (measured on
+  // streaming path: up to 160 rows, one row block of 16 RT rows (measured on
   // the 8B-shaped head: 30 rows 306 -> 248 us, 60 rows 298 -> 273 us against
-  // the 64 x 32 / 64 x 64 tiles)
+  // the 64 x 32 / 64 x 64 tiles; 144 rows 397 -> 371 us against 128 x 160)
   const int snrb = 1, srt = (a.rows + 15) / 16;
   const long sspan = ((long)(16 * srt - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
-  if (a.dtype == 1 && a.rows <= 16 * HS_MAX_RT && a.d % HS_K == 0 && sspan < (1L << 31)) {
-    a.nvb = (a.vocab + HS_ROWS - 1) / HS_ROWS;
-    if (srt == 1) launch_stream<1>(a, snrb, st);
-    else if (srt == 2) launch_stream<2>(a, snrb, st);
-    else if (srt == 3) launch_stream<3>(a, snrb, st);
-    else launch_stream<4>(a, snrb, st);
+  const int sks = srt <= 4 ? 128 : 64;
+  if (a.dtype == 1 && a.rows <= 16 * HS_MAX_RT && a.d % sks == 0 && sspan < (1L << 31)) {
+    a.nvb = (a.vocab + 127) / 128;
+    if (srt == 1) launch_stream<1, 128, 1>(a, snrb, st);
+    else if (srt == 2) launch_stream<2, 128, 1>(a, snrb, st);
+    else if (srt == 3) launch_stream<3, 128, 1>(a, snrb, st);
+    else if (srt == 4) launch_stream<4, 128, 1>(a, snrb, st);
+    else if (srt <= 6) launch_stream<6, 64, 1>(a, snrb, st);
+    else if (srt <= 8) launch_stream<8, 64, 1>(a, snrb, st);
+    else launch_stream<10, 64, 1>(a, snrb, st);
   } else if (a.dtype == 1 && a.d % HEAD_KT == 0 && span < (1L << 31)) {
     a.nvb = (a.vocab + BN - 1) / BN;
     const int nmb = (a.rows + BM - 1) / BM;

@@ -150,9 +150,11 @@ def test_ragged_bf16_tiles_off_the_streaming_depth(rows, mode):
     _run_case(5003, 576, "bf16", rows, 15, 16, mode, keep_logits=True)
 
 
-def test_ragged_bf16_gumbel_up_to_160_rows():
-    # 65..160 rows: the 128 x 160 tile, partial last vocabulary block
-    _run_case(5003, 512, "bf16", 100, 15, 16, bd.HEAD_GUMBEL, T=0.9, keep_logits=True)
+@pytest.mark.parametrize("rows", [80, 100, 150])
+def test_ragged_bf16_gumbel_up_to_160_rows(rows):
+    # 65..160 rows: the streaming kernel with 64-deep stages and 6, 8 or 10
+    # row tiles (the last one ragged), partial last vocabulary block
+    _run_case(5003, 512, "bf16", rows, 15, 16, bd.HEAD_GUMBEL, T=0.9, keep_logits=True)
 
 
 def test_ragged_bf16_argmax_two_row_blocks():
