@@ -74,12 +74,13 @@ def _algorithmic(cfg, rows, n_inj):
     )
 
 
-def _profiled_traffic(kernel, files):
+def _profiled_traffic(workload, kernel, files):
     """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size),
-    or None when the kernel's sources changed since the counters were taken."""
+    summary of `workload` (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size), or None when there is none or the kernel's sources changed
+    since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "q8b_bs32_rs_hbm_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -310,8 +311,8 @@ def main():
                 else (128, 160) if r <= 160 else (256, 256))
     head_kernel += " (+lm_combine_kernel)"
     traffic = None
-    if args.workload == "q8b_bs32_rs":
-        traffic = _profiled_traffic("lm_head_lds_kernel",
+    if cfg["dtype"] == "bf16":
+        traffic = _profiled_traffic(args.workload, head_kernel.split(" ")[0],
                                     ["lm_head.hip", "mma_tile.hpp", "dma.hpp", "common.hpp",
                                      "kernels.hpp"])
     if head_bound == "mfma":
