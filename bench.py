@@ -98,7 +98,8 @@ def _profiled_traffic(workload, kernel, files):
 
 def _cpu_baseline(cfg, cyc, budget_s):
     """Time the CPU oracle on a bounded sample of the same workload: whole
-    cycles for as many sequences as fit in ~budget_s, scaled to the batch."""
+    cycles for as many sequences as fit in ~budget_s, scaled to the batch,
+    then again with BLAS held to one thread for a per-core figure."""
     import numpy as np
 
     from block_diffusion_speculative_kv_amd import KVCache
@@ -117,8 +118,8 @@ def _cpu_baseline(cfg, cyc, budget_s):
     target = host(cyc.target) if cyc.verify_mode is not None else None
     n_new, g, V = cyc.n_new, cfg["gamma"], cfg["vocab"]
     T = float(cfg.get("temperature", 1.0))
-    done, t_total = 0, 0.0
-    for b, S in enumerate(cfg["ctx_lens"]):
+    def one_cycle(b, S):
+        """one sequence's full cycle on the oracle; returns its seconds"""
         ck = [host(k[b]) for k in cyc.kv.k]
         cv = [host(KVCache.untile_v(v[b:b + 1])[0]) for v in cyc.kv.v]   # -> [h, pos, dh]
         t0 = time.perf_counter()
@@ -136,16 +137,47 @@ def _cpu_baseline(cfg, cyc, budget_s):
             mode = "rs" if cfg["verify"] == "rs" else "greedy"
             verify_batch(mode, target[b:b + 1], out["ids"][None, :],
                          zd=out["logits"][None, :], temperature=T, seed=cyc.seed, cycle=0)
-        t_total += time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    done, t_total = 0, 0.0
+    for b, S in enumerate(cfg["ctx_lens"]):
+        t_total += one_cycle(b, S)
         done += 1
         if t_total >= budget_s:
             break
     per_seq = t_total / done
     cycles_per_s = 1.0 / (per_seq * cfg["bs"])
+    # the same oracle with its BLAS held to one thread, on the first
+    # sequences (a per-core figure; about a third of the budget)
+    single = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
+        with threadpool_limits(1):
+            d1, t1 = 0, 0.0
+            for b, S in enumerate(cfg["ctx_lens"]):
+                t1 += one_cycle(b, S)
+                d1 += 1
+                if t1 >= budget_s / 3:
+                    break
+        single = dict(value=1.0 / (t1 / d1 * cfg["bs"]), unit="cycles/s", cores=1,
+                      sample=f"{d1} of {cfg['bs']} sequences ({t1:.1f} s), BLAS held to one thread")
+    except ImportError:  # pragma: no cover
+        blas = []
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=cycles_per_s, unit="cycles/s", cores=len(os.sched_getaffinity(0)),
                 kind="oracle",
                 sample=f"{done} of {cfg['bs']} sequences, one full cycle each "
-                       f"({t_total:.1f} s), scaled linearly to the batch")
+                       f"({t_total:.1f} s), scaled linearly to the batch",
+                single_thread=single, cpu_model=cpu_model, blas=blas)
 
 
 def main():
