@@ -59,6 +59,9 @@ void launch_draft_prep(const int32_t *tokens, const int32_t *ctx_len, int bs, in
 }
 
 // ---- embedding gather into the fp32 residual stream --------------------------
+// One workgroup per row.  Rows whose width is a multiple of 8 move as
+// 8-element vectors, the loads of a thread issued before its stores, so a
+// row costs about one round trip to memory instead of one per element.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T *__restrict__ embed,
                                                     const int32_t *__restrict__ tok, int d,
@@ -66,7 +69,41 @@ __global__ __launch_bounds__(256) void embed_kernel(const T *__restrict__ embed,
   const int r = blockIdx.x;
   const T *src = embed + (long)tok[r] * d;
   float *dst = h + (long)r * d;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) dst[j] = to_f32(src[j]);
+  if (d % 8 == 0) {
+    constexpr int U = 4;  // vectors in flight per thread
+    for (int j0 = 8 * threadIdx.x; j0 < d; j0 += 8 * U * blockDim.x) {
+      float x[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + 8 * u * blockDim.x;
+        if (j < d) {
+          if constexpr (sizeof(T) == 2) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src + j);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[u][e] = static_cast<float>(v[e]);
+          } else {
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src + j);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + j + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[u][e] = v0[e];
+              x[u][4 + e] = v1[e];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + 8 * u * blockDim.x;
+        if (j < d) {
+          *reinterpret_cast<f32x4 *>(dst + j) = f32x4{x[u][0], x[u][1], x[u][2], x[u][3]};
+          *reinterpret_cast<f32x4 *>(dst + j + 4) = f32x4{x[u][4], x[u][5], x[u][6], x[u][7]};
+        }
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += blockDim.x) dst[j] = to_f32(src[j]);
+  }
 }
 
 void launch_embed(int dtype, const void *embed, const int32_t *tok, int R, int d, float *h,

@@ -577,15 +577,34 @@ __global__ __launch_bounds__(COMB_T) void lm_combine_kernel(HeadArgs a) {
   arg.second = -INFINITY;
   arg.idx = 0x7fffffff;
   float zbest = 0.f, zmax = -INFINITY, m = -INFINITY;
-  for (int i = tid; i < a.nvb; i += COMB_T) {
-    const HeadPartial h = p[i];
-    ArgTop2 o;
-    o.best = h.best;
-    o.second = h.second;
-    o.idx = h.idx;
-    arg_merge(arg, zbest, o, h.zbest);
-    zmax = fmaxf(zmax, h.zmax);
-    m = fmaxf(m, h.m);
+  // records in batches of CB per thread, loaded before any is merged; the
+  // (m, s) of the first batch stay in registers for the second pass, which
+  // then needs no reload when one batch covers the row (nvb <= CB COMB_T)
+  constexpr int CB = 8;
+  float bm[CB], bs[CB];
+  for (int i0 = 0; i0 < a.nvb; i0 += CB * COMB_T) {
+    HeadPartial hb[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int i = i0 + tid + u * COMB_T;
+      if (i < a.nvb) hb[u] = p[i];
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int i = i0 + tid + u * COMB_T;
+      if (i0 == 0) {
+        bm[u] = i < a.nvb ? hb[u].m : -INFINITY;
+        bs[u] = i < a.nvb ? hb[u].s : 0.f;
+      }
+      if (i >= a.nvb) continue;
+      ArgTop2 o;
+      o.best = hb[u].best;
+      o.second = hb[u].second;
+      o.idx = hb[u].idx;
+      arg_merge(arg, zbest, o, hb[u].zbest);
+      zmax = fmaxf(zmax, hb[u].zmax);
+      m = fmaxf(m, hb[u].m);
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     ArgTop2 b;
@@ -607,11 +626,16 @@ __global__ __launch_bounds__(COMB_T) void lm_combine_kernel(HeadArgs a) {
 #pragma unroll
   for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_m[w]);
   double s = 0.0;
-  if (M != -INFINITY)
-    for (int i = tid; i < a.nvb; i += COMB_T) {
+  if (M != -INFINITY) {
+    // same order as before: record tid, tid + COMB_T, ...
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (bm[u] != -INFINITY) s += (double)bs[u] * exp((double)bm[u] - (double)M);
+    for (int i = tid + CB * COMB_T; i < a.nvb; i += COMB_T) {
       const float mi = p[i].m, si = p[i].s;
       if (mi != -INFINITY) s += (double)si * exp((double)mi - (double)M);
     }
+  }
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, WAVE);
   if (lane == 0) s_s[wave] = s;
   __syncthreads();
