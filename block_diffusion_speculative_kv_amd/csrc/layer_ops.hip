@@ -179,8 +179,18 @@ __global__ __launch_bounds__(NORM_ROW_T) void norm_row_kernel(
     x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < d) {
       if (resid) x[i] = *reinterpret_cast<const f32x4 *>(resid + (long)r * d + c);
-      for (int sp = 0; sp < nsplit; ++sp)
-        x[i] += *reinterpret_cast<const f32x4 *>(parts + ((long)sp * M + r) * d + c);
+      // the planes in batches of SB loads in flight, summed in split order
+      constexpr int SB = 8;
+      for (int sp0 = 0; sp0 < nsplit; sp0 += SB) {
+        f32x4 pv[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+          if (sp0 + k < nsplit)
+            pv[k] = *reinterpret_cast<const f32x4 *>(parts + ((long)(sp0 + k) * M + r) * d + c);
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+          if (sp0 + k < nsplit) x[i] += pv[k];
+      }
       if (resid && write_resid) *reinterpret_cast<f32x4 *>(resid + (long)r * d + c) = x[i];
       ss += x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
     }
@@ -319,14 +329,27 @@ __global__ __launch_bounds__(64 * POST_HEADS) void qkv_post_kernel(
   if (head >= hq + 2 * hkv) return;
   const bool is_q = head < hq, is_k = !is_q && head < hq + hkv;
   float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
+  // the planes in batches of SB loads in flight, summed in split order
+  constexpr int SB = 8;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
     if (p < half) {
       const float *src = parts + (long)r * ncol + head * dh + p;
-      for (int s = 0; s < nsplit; ++s) {
-        x1[i] += src[(long)s * R * ncol];
-        x2[i] += src[(long)s * R * ncol + half];
+      for (int s0 = 0; s0 < nsplit; s0 += SB) {
+        float a1[SB], a2[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+          if (s0 + k < nsplit) {
+            a1[k] = src[(long)(s0 + k) * R * ncol];
+            a2[k] = src[(long)(s0 + k) * R * ncol + half];
+          }
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+          if (s0 + k < nsplit) {
+            x1[i] += a1[k];
+            x2[i] += a2[k];
+          }
       }
     }
   }
@@ -380,9 +403,22 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float *__restrict__ p
   const long r = i / mlp, j = i % mlp;
   const long plane = (long)R * 2 * mlp;
   float g = 0.f, u = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    g += parts[s * plane + r * 2 * mlp + j];
-    u += parts[s * plane + r * 2 * mlp + mlp + j];
+  // the planes in batches of SB loads in flight, summed in split order
+  constexpr int SB = 8;
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    float gv[SB], uv[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      if (s0 + k < nsplit) {
+        gv[k] = parts[(s0 + k) * plane + r * 2 * mlp + j];
+        uv[k] = parts[(s0 + k) * plane + r * 2 * mlp + mlp + j];
+      }
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      if (s0 + k < nsplit) {
+        g += gv[k];
+        u += uv[k];
+      }
   }
   const float silu = g / (1.0f + expf(-g));
   act[i] = from_f32<T>(silu * u);
@@ -402,14 +438,15 @@ void launch_swiglu(int dtype, const float *parts, int nsplit, int R, int mlp, vo
 }
 
 // ---- injected K/V: k-norm + rotary embedding, scatter into the cache --------
-template <typename T>
+template <typename T, int RPW>
 __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     const float *__restrict__ parts, int nsplit, int n, int hkv, int dh,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
     int qk_norm, float eps, const float2 *__restrict__ rope, int max_batch, int cap,
-    int with_v, int rpw) {
+    int with_v) {
   // K heads, and the V heads too when with_v (else inject_v_kernel does them);
-  // each wave takes its head in rpw consecutive rows
+  // each wave takes its head in RPW consecutive rows, whose split-plane
+  // loads are all issued before the first row is normalised and stored
   const int head = blockIdx.y * POST_HEADS + (threadIdx.x >> 6);
   const int layer = blockIdx.z, lane = threadIdx.x & 63;
   if (head >= (with_v ? 2 : 1) * hkv) return;
@@ -417,40 +454,53 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
   const bool is_k = head < hkv;
   const int h = is_k ? head : head - hkv;
   T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
-#pragma unroll 1
-  for (int i = 0; i < rpw; ++i) {
-    const int r = blockIdx.x * rpw + i;
-    if (r >= n) break;
-    const int sq = seq[r], ps = pos[r];
-    if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
-    // all loads of the split planes first (they are independent), then the
-    // sums in split order
-    float x1[2] = {0.f, 0.f}, x2[2] = {0.f, 0.f};
+  float x1[RPW][2], x2[RPW][2];
+  int sq[RPW], ps[RPW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int p = lane + 64 * j;
-      if (p < half) {
-        const float *src = parts + (long)r * width + layer * ncol + head * dh + p;
-        for (int s = 0; s < nsplit; ++s) {
-          x1[j] += src[(long)s * n * width];
-          x2[j] += src[(long)s * n * width + half];
+  for (int i = 0; i < RPW; ++i) {
+    const int r = blockIdx.x * RPW + i;
+    sq[i] = r < n ? seq[r] : -1;
+    ps[i] = r < n ? pos[r] : -1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) x1[i][j] = x2[i][j] = 0.f;
+  }
+  // splits outermost, so every load of one split is in flight at once (sums
+  // in split order)
+  for (int s = 0; s < nsplit; ++s) {
+    const float *plane = parts + (long)s * n * width + layer * ncol + head * dh;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = blockIdx.x * RPW + i;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = lane + 64 * j;
+        if (r < n && p < half) {
+          x1[i][j] += plane[(long)r * width + p];
+          x2[i][j] += plane[(long)r * width + p + half];
         }
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = blockIdx.x * RPW + i;
+    if (r >= n) break;
+    if (sq[i] < 0 || sq[i] >= max_batch || ps[i] < 0 || ps[i] >= cap) continue;
     // K cache rows are dh-vectors [cap][dh]; the V cache is stored in tiles
     // of 64 keys, d-major inside a tile: [cap/64][dh][64]
     const long stride = is_k ? 1 : 64;
-    T *dst = is_k ? kc + (((long)sq * hkv + h) * cap + ps) * dh
-                  : vc + ((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (ps & 63);
+    T *dst = is_k ? kc + (((long)sq[i] * hkv + h) * cap + ps[i]) * dh
+                  : vc + ((long)sq[i] * hkv + h) * dh * cap + (long)(ps[i] >> 6) * dh * 64 +
+                        (ps[i] & 63);
     if (is_k)
-      head_norm_rope<T>(x1, x2, dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
+      head_norm_rope<T>(x1[i], x2[i], dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
                         rope + (long)r * half);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int p = lane + 64 * j;
       if (p < half) {
-        dst[p * stride] = from_f32<T>(x1[j]);
-        dst[(p + half) * stride] = from_f32<T>(x2[j]);
+        dst[p * stride] = from_f32<T>(x1[i][j]);
+        dst[(p + half) * stride] = from_f32<T>(x2[i][j]);
       }
     }
   }
@@ -478,13 +528,15 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
   for (int i0 = threadIdx.x; i0 < INJ_VROWS * q4; i0 += U * blockDim.x) {
     f32x4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * blockDim.x, row = i / q4, r = r0 + row;
-      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (i < INJ_VROWS * q4 && r < n) {
-        const float *src = parts + (long)r * width + col0 + 4 * (i % q4);
-        for (int s = 0; s < nsplit; ++s)
-          x[u] += *reinterpret_cast<const f32x4 *>(src + (long)s * n * width);
+    for (int u = 0; u < U; ++u) x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // splits outermost: the U loads of a split are in flight together
+    for (int s = 0; s < nsplit; ++s) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * blockDim.x, row = i / q4, r = r0 + row;
+        if (i < INJ_VROWS * q4 && r < n)
+          x[u] += *reinterpret_cast<const f32x4 *>(parts + (long)s * n * width + (long)r * width +
+                                                   col0 + 4 * (i % q4));
       }
     }
 #pragma unroll
@@ -496,15 +548,51 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
       for (int e = 0; e < 4; ++e) tile[row * ts + d + e] = x[u][e];
     }
   }
+  // groups of 8 rows that are 8 consecutive positions of one sequence from a
+  // multiple of 8 (the usual prefill case) fill 8 consecutive slots of a tile
+  // row: one 16-byte store; other groups are stored element by element
+  __shared__ int gsq[INJ_VROWS / 8], gps[INJ_VROWS / 8];
+  if (threadIdx.x < INJ_VROWS / 8) {
+    const int g0 = r0 + 8 * threadIdx.x;
+    int q = -1, p0 = -1;
+    if (g0 + 7 < n) {
+      q = seq[g0];
+      p0 = pos[g0];
+      bool ok = q >= 0 && q < max_batch && p0 >= 0 && p0 + 7 < cap && (p0 & 7) == 0;
+      for (int e = 1; e < 8 && ok; ++e) ok = seq[g0 + e] == q && pos[g0 + e] == p0 + e;
+      if (!ok) q = -1;
+    }
+    gsq[threadIdx.x] = q;
+    gps[threadIdx.x] = p0;
+  }
   __syncthreads();
   T *vc = (T *)il.vc[layer];
-  for (int i = threadIdx.x; i < INJ_VROWS * dh; i += blockDim.x) {
-    const int d = i / INJ_VROWS, row = i % INJ_VROWS, r = r0 + row;
-    if (r >= n) continue;
-    const int sq = seq[r], ps = pos[r];
-    if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
-    vc[((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (long)d * 64 + (ps & 63)] =
-        from_f32<T>(tile[row * ts + d]);
+  for (int i = threadIdx.x; i < (INJ_VROWS / 8) * dh; i += blockDim.x) {
+    const int d = i / (INJ_VROWS / 8), grp = i % (INJ_VROWS / 8), row0 = 8 * grp;
+    const int q = gsq[grp];
+    if (q >= 0) {
+      const int p0 = gps[grp];
+      T v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(tile[(row0 + e) * ts + d]);
+      T *dst = vc + ((long)q * hkv + h) * dh * cap + (long)(p0 >> 6) * dh * 64 + (long)d * 64 +
+               (p0 & 63);
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = v[e];
+      }
+      continue;
+    }
+    for (int e = 0; e < 8; ++e) {
+      const int row = row0 + e, r = r0 + row;
+      if (r >= n) break;
+      const int sq = seq[r], ps = pos[r];
+      if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
+      vc[((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (long)d * 64 + (ps & 63)] =
+          from_f32<T>(tile[row * ts + d]);
+    }
   }
 }
 
@@ -520,12 +608,22 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
   const int rpw = post_rows(n);
   dim3 grid((n + rpw - 1) / rpw, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
             il.layers);
-  if (dtype == 1)
-    hipLaunchKernelGGL(inject_post_kernel<bf16>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v, rpw);
-  else
-    hipLaunchKernelGGL(inject_post_kernel<float>, grid, dim3(64 * POST_HEADS), 0, st, parts, nsplit, n, hkv, dh,
-                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap, with_v, rpw);
+  const float2 *cs = (const float2 *)rope;
+  if (dtype == 1) {
+    if (rpw == 4)
+      hipLaunchKernelGGL((inject_post_kernel<bf16, 4>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+    else
+      hipLaunchKernelGGL((inject_post_kernel<bf16, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+  } else {
+    if (rpw == 4)
+      hipLaunchKernelGGL((inject_post_kernel<float, 4>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+    else
+      hipLaunchKernelGGL((inject_post_kernel<float, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+  }
   if (with_v) return;
   // V heads: staged and written along rows
   const dim3 vgrid((n + INJ_VROWS - 1) / INJ_VROWS, hkv, il.layers);

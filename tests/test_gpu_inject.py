@@ -136,6 +136,56 @@ def test_many_rows_transposed_v_path():
                                    f"{what} layer {l}: one call vs chunks")
 
 
+def test_prefill_rows_vector_v_stores():
+    # 2100 consecutive-position rows, as a prefill chunk gives them: from 2048
+    # rows the V rows go through the row-tiled pass, which stores 8 keys at
+    # once where 8 rows are 8 aligned consecutive positions of one sequence.
+    # Sequence 0 takes rows 0..1002 (positions 0..1002), sequence 1 rows
+    # 1003..2099 (positions 3..1099): the group of rows 1000..1007 straddles
+    # the two, row 1500 is invalid (its group is stored element by element),
+    # the other groups take the vector stores.  Against the oracle, the
+    # untouched cache rows, and the same rows injected in chunks below 2048
+    # rows (the per-row pass).
+    cfg = configs.small_bf16()
+    n, cap = 2100, 1152
+    dev = device()
+    w = gen.weights(cfg, device=dev)
+    dr = bd.Drafter(cfg, w)
+    feats = gen.feats(cfg, n, device=dev)
+    seq = np.where(np.arange(n) < 1003, 0, 1)
+    pos = np.where(seq == 0, np.arange(n), np.arange(n) - 1000)
+    seq[1500] = -1
+    seq_t = torch.from_numpy(seq.astype(np.int32)).to(dev)
+    pos_t = torch.from_numpy(pos.astype(np.int32)).to(dev)
+    ws = dr.workspace(max_inject_rows=n)
+    kv = dr.kv_cache(2, cap)
+    dr.inject_kv(feats, seq_t, pos_t, kv, ws)
+    torch.cuda.synchronize()
+    ok = seq >= 0
+    rows = np.nonzero(ok)[0]
+    _check(cfg, w, kv, feats, seq, pos, np.unique(np.concatenate(
+        [rows[::9], rows[(rows >= 990) & (rows < 1020)], rows[(rows >= 1490) & (rows < 1512)],
+         rows[-12:]])))
+    # the slot of the invalid row (sequence 1, position 500) and the slots no
+    # row names stay zero
+    for l in range(cfg["n_layers"]):
+        v = bd.KVCache.untile_v(kv.v[l]).float().cpu().numpy()
+        assert not v[1, :, 500].any() and not v[0, :, 1003:].any() and not v[1, :, :3].any()
+    kv2 = dr.kv_cache(2, cap)
+    for a, b in ((0, 700), (700, 1400), (1400, n)):
+        dr.inject_kv(feats[a:b].contiguous(), seq_t[a:b].contiguous(), pos_t[a:b].contiguous(),
+                     kv2, ws)
+    torch.cuda.synchronize()
+    for l in range(cfg["n_layers"]):
+        for c1, c2, what in ((kv.k[l], kv2.k[l], "K"), (kv.v[l], kv2.v[l], "V")):
+            a = c1.float().cpu().numpy() if what == "K" else \
+                bd.KVCache.untile_v(c1).float().cpu().numpy()
+            b = c2.float().cpu().numpy() if what == "K" else \
+                bd.KVCache.untile_v(c2).float().cpu().numpy()
+            assert_bf16_rows_close(a[seq[rows], :, pos[rows]], b[seq[rows], :, pos[rows]],
+                                   f"{what} layer {l}: one call vs chunks")
+
+
 def test_q8b_three_layers_grouped_kv_off_the_192_tile():
     # 1001 rows, three 8B-shaped layers: the grouped K/V product (N = 3 x
     # 2048 = 6144, K = 4096) has the shape that takes 192-wide weight tiles,
