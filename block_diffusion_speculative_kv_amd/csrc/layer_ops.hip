@@ -284,10 +284,11 @@ __device__ __forceinline__ void rope_pair(float &x1, float &x2, float2 cs) {
   x2 = y2;
 }
 
-template <typename T>
-__device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh, bool norm,
-                                               const T *g, float eps,
-                                               const float2 *__restrict__ cs) {
+// The same with the gains and the rotary table already in registers (g1[i],
+// g2[i], c[i] for p = lane + 64 i), so a caller can request them ahead.
+__device__ __forceinline__ void head_norm_rope_regs(float x1[2], float x2[2], int dh, bool norm,
+                                                    const float g1[2], const float g2[2],
+                                                    float eps, const float2 c[2]) {
   const int lane = threadIdx.x & 63, half = dh / 2;
   if (norm) {
     float ss = 0.f;
@@ -299,16 +300,37 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
     for (int i = 0; i < 2; ++i) {
       const int p = lane + 64 * i;
       if (p < half) {
-        x1[i] = x1[i] * rs * to_f32(g[p]);
-        x2[i] = x2[i] * rs * to_f32(g[p + half]);
+        x1[i] = x1[i] * rs * g1[i];
+        x2[i] = x2[i] * rs * g2[i];
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = lane + 64 * i;
-    if (p < half) rope_pair(x1[i], x2[i], cs[p]);
+    if (p < half) rope_pair(x1[i], x2[i], c[i]);
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh, bool norm,
+                                               const T *g, float eps,
+                                               const float2 *__restrict__ cs) {
+  const int lane = threadIdx.x & 63, half = dh / 2;
+  float g1[2] = {0.f, 0.f}, g2[2] = {0.f, 0.f};
+  float2 c[2] = {float2{1.f, 0.f}, float2{1.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    if (p < half) {
+      if (norm) {
+        g1[i] = to_f32(g[p]);
+        g2[i] = to_f32(g[p + half]);
+      }
+      c[i] = cs[p];
+    }
+  }
+  head_norm_rope_regs(x1, x2, dh, norm, g1, g2, eps, c);
 }
 
 constexpr int POST_HEADS = 4;  // heads per workgroup, one wave each
@@ -456,13 +478,30 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
   T *kc = (T *)il.kc[layer], *vc = (T *)il.vc[layer];
   float x1[RPW][2], x2[RPW][2];
   int sq[RPW], ps[RPW];
+  // the rows' ids, rotary tables and (K) the norm gains are requested
+  // together with the planes
+  const bool norm = is_k && qk_norm != 0;
+  float g1[2] = {0.f, 0.f}, g2[2] = {0.f, 0.f};
+  float2 cs[RPW][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = lane + 64 * j;
+    if (norm && p < half) {
+      g1[j] = to_f32(((const T *)il.k_norm[layer])[p]);
+      g2[j] = to_f32(((const T *)il.k_norm[layer])[p + half]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = blockIdx.x * RPW + i;
     sq[i] = r < n ? seq[r] : -1;
     ps[i] = r < n ? pos[r] : -1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) x1[i][j] = x2[i][j] = 0.f;
+    for (int j = 0; j < 2; ++j) {
+      x1[i][j] = x2[i][j] = 0.f;
+      const int p = lane + 64 * j;
+      cs[i][j] = is_k && r < n && p < half ? rope[(long)r * half + p] : float2{1.f, 0.f};
+    }
   }
   // splits outermost, so every load of one split is in flight at once (sums
   // in split order)
@@ -492,9 +531,7 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
     T *dst = is_k ? kc + (((long)sq[i] * hkv + h) * cap + ps[i]) * dh
                   : vc + ((long)sq[i] * hkv + h) * dh * cap + (long)(ps[i] >> 6) * dh * 64 +
                         (ps[i] & 63);
-    if (is_k)
-      head_norm_rope<T>(x1[i], x2[i], dh, qk_norm != 0, (const T *)il.k_norm[layer], eps,
-                        rope + (long)r * half);
+    if (is_k) head_norm_rope_regs(x1[i], x2[i], dh, norm, g1, g2, eps, cs[i]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int p = lane + 64 * j;
@@ -519,7 +556,15 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, InjectLayers il,
     int max_batch, int cap) {
   extern __shared__ float tile[];  // [INJ_VROWS][dh + 1]
+  __shared__ int rsq[INJ_VROWS], rps[INJ_VROWS], gsq[INJ_VROWS / 8], gps[INJ_VROWS / 8];
   const int r0 = blockIdx.x * INJ_VROWS, h = blockIdx.y, layer = blockIdx.z;
+  // the rows' sequence ids and positions are requested first and staged in
+  // LDS with the tile
+  int my_sq = -1, my_ps = -1;
+  if (threadIdx.x < INJ_VROWS && r0 + (int)threadIdx.x < n) {
+    my_sq = seq[r0 + threadIdx.x];
+    my_ps = pos[r0 + threadIdx.x];
+  }
   const int ncol = 2 * hkv * dh, width = il.layers * ncol, ts = dh + 1;
   const long col0 = (long)layer * ncol + (long)hkv * dh + (long)h * dh;
   // 16-byte loads, eight per thread issued together (dh is 64 or 128)
@@ -551,18 +596,20 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
   // groups of 8 rows that are 8 consecutive positions of one sequence from a
   // multiple of 8 (the usual prefill case) fill 8 consecutive slots of a tile
   // row: one 16-byte store; other groups are stored element by element
-  __shared__ int gsq[INJ_VROWS / 8], gps[INJ_VROWS / 8];
+  if (threadIdx.x < INJ_VROWS) {
+    rsq[threadIdx.x] = my_sq;
+    rps[threadIdx.x] = my_ps;
+  }
+  __syncthreads();
   if (threadIdx.x < INJ_VROWS / 8) {
-    const int g0 = r0 + 8 * threadIdx.x;
-    int q = -1, p0 = -1;
-    if (g0 + 7 < n) {
-      q = seq[g0];
-      p0 = pos[g0];
-      bool ok = q >= 0 && q < max_batch && p0 >= 0 && p0 + 7 < cap && (p0 & 7) == 0;
-      for (int e = 1; e < 8 && ok; ++e) ok = seq[g0 + e] == q && pos[g0 + e] == p0 + e;
-      if (!ok) q = -1;
-    }
-    gsq[threadIdx.x] = q;
+    const int g = 8 * threadIdx.x;
+    int q = rsq[g];
+    const int p0 = rps[g];
+    bool ok = r0 + g + 7 < n && q >= 0 && q < max_batch && p0 >= 0 && p0 + 7 < cap &&
+              (p0 & 7) == 0;
+#pragma unroll
+    for (int e = 1; e < 8; ++e) ok = ok && rsq[g + e] == q && rps[g + e] == p0 + e;
+    gsq[threadIdx.x] = ok ? q : -1;
     gps[threadIdx.x] = p0;
   }
   __syncthreads();
@@ -588,7 +635,7 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
     for (int e = 0; e < 8; ++e) {
       const int row = row0 + e, r = r0 + row;
       if (r >= n) break;
-      const int sq = seq[r], ps = pos[r];
+      const int sq = rsq[row], ps = rps[row];
       if (sq < 0 || sq >= max_batch || ps < 0 || ps >= cap) continue;
       vc[((long)sq * hkv + h) * dh * cap + (long)(ps >> 6) * dh * 64 + (long)d * 64 + (ps & 63)] =
           from_f32<T>(tile[row * ts + d]);
