@@ -543,6 +543,92 @@ __global__ __launch_bounds__(64 * POST_HEADS) void inject_post_kernel(
   }
 }
 
+// K heads of many rows with dh = 128 (bf16): 16 lanes per (row, head), each
+// lane holding 4 consecutive dims of each half (the rotary pairs (e, e + 64)
+// in one lane), so loads are 16 bytes and a wave has 4 rows of its head in
+// flight per batch, KW_BATCH batches issued before any is finished.  The
+// head norm reduces over the 16 lanes of a row.
+constexpr int KW_BATCH = 2;
+constexpr int KW_ROWS = 4 * 4 * KW_BATCH;  // rows per workgroup (4 waves)
+template <typename T>
+__global__ __launch_bounds__(256) void inject_k_wide_kernel(
+    const float *__restrict__ parts, int nsplit, int n, int hkv, const int32_t *__restrict__ seq,
+    const int32_t *__restrict__ pos, InjectLayers il, int qk_norm, float eps,
+    const float2 *__restrict__ rope, int max_batch, int cap) {
+  constexpr int DH = 128, HALF = 64;
+  const int h = blockIdx.y, layer = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane >> 4, l = lane & 15;
+  const int ncol = 2 * hkv * DH, width = il.layers * ncol;
+  const bool norm = qk_norm != 0;
+  float g1[4], g2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    g1[e] = norm ? to_f32(((const T *)il.k_norm[layer])[4 * l + e]) : 1.f;
+    g2[e] = norm ? to_f32(((const T *)il.k_norm[layer])[HALF + 4 * l + e]) : 1.f;
+  }
+  f32x4 x1[KW_BATCH], x2[KW_BATCH], c01[KW_BATCH], c23[KW_BATCH];
+  int rr[KW_BATCH], sq[KW_BATCH], ps[KW_BATCH];
+#pragma unroll
+  for (int b = 0; b < KW_BATCH; ++b) {
+    const int r = blockIdx.x * KW_ROWS + wave * 4 * KW_BATCH + 4 * b + sub;
+    rr[b] = r;
+    sq[b] = r < n ? seq[r] : -1;
+    ps[b] = r < n ? pos[r] : -1;
+    x1[b] = x2[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the row's rotary table: (cos, sin) of dims 4l .. 4l + 3
+    const f32x4 *cr = reinterpret_cast<const f32x4 *>(rope + (long)min(r, n - 1) * HALF + 4 * l);
+    c01[b] = cr[0];
+    c23[b] = cr[1];
+  }
+  for (int s = 0; s < nsplit; ++s) {
+    const float *plane = parts + (long)s * n * width + layer * ncol + h * DH + 4 * l;
+#pragma unroll
+    for (int b = 0; b < KW_BATCH; ++b) {
+      if (rr[b] < n) {
+        x1[b] += *reinterpret_cast<const f32x4 *>(plane + (long)rr[b] * width);
+        x2[b] += *reinterpret_cast<const f32x4 *>(plane + (long)rr[b] * width + HALF);
+      }
+    }
+  }
+  T *kc = (T *)il.kc[layer];
+#pragma unroll
+  for (int b = 0; b < KW_BATCH; ++b) {
+    float a[4], c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = x1[b][e];
+      c[e] = x2[b][e];
+    }
+    if (norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + c[e] * c[e];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = a[e] * rs * g1[e];
+        c[e] = c[e] * rs * g2[e];
+      }
+    }
+    const float cs[8] = {c01[b][0], c01[b][1], c01[b][2], c01[b][3],
+                         c23[b][0], c23[b][1], c23[b][2], c23[b][3]};
+    T o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y1 = a[e], y2 = c[e];
+      rope_pair(y1, y2, float2{cs[2 * e], cs[2 * e + 1]});
+      o1[e] = from_f32<T>(y1);
+      o2[e] = from_f32<T>(y2);
+    }
+    if (rr[b] >= n || sq[b] < 0 || sq[b] >= max_batch || ps[b] < 0 || ps[b] >= cap) continue;
+    T *dst = kc + (((long)sq[b] * hkv + h) * cap + ps[b]) * DH + 4 * l;
+    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(o1);
+    *reinterpret_cast<uint2 *>(dst + HALF) = *reinterpret_cast<const uint2 *>(o2);
+  }
+}
+
 // V rows of the injected layers, 64 rows x dh per workgroup: the split sums
 // are staged in LDS as [row][d] (loads along d) and written out along rows,
 // so the rows of consecutive positions of one sequence, which share a 64-key
@@ -653,6 +739,12 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
   // INJ_V_MIN_ROWS rows the row-tiled transposing pass (contiguous stores)
   const int with_v = n < INJ_V_MIN_ROWS;
   const int rpw = post_rows(n);
+  if (dtype == 1 && !with_v && dh == 128) {
+    // K heads on the wide pass (16-byte loads, 4 rows per wave at a time)
+    const dim3 kgrid((n + KW_ROWS - 1) / KW_ROWS, hkv, il.layers);
+    hipLaunchKernelGGL(inject_k_wide_kernel<bf16>, kgrid, dim3(256), 0, st, parts, nsplit, n, hkv,
+                       seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
+  } else {
   dim3 grid((n + rpw - 1) / rpw, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
             il.layers);
   const float2 *cs = (const float2 *)rope;
@@ -670,6 +762,7 @@ void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hk
     else
       hipLaunchKernelGGL((inject_post_kernel<float, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
                          nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+  }
   }
   if (with_v) return;
   // V heads: staged and written along rows
