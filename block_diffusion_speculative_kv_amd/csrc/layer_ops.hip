@@ -333,6 +333,32 @@ __device__ __forceinline__ void head_norm_rope(float x1[2], float x2[2], int dh,
   head_norm_rope_regs(x1, x2, dh, norm, g1, g2, eps, c);
 }
 
+// Wide head layout for 128-dim heads: 16 lanes per (row, head), lane l
+// holding dims 4l .. 4l + 3 (a) and 64 + 4l .. 64 + 4l + 3 (c), so each
+// rotary pair (e, e + 64) sits in one lane.  Optional RMSNorm over the 128
+// dims (a reduction over the 16 lanes) with gains g1 / g2, then the rotary
+// embedding with the row's (cos, sin) of dims 4l .. 4l + 3 (c01, c23).
+__device__ __forceinline__ void wide_norm_rope(float a[4], float c[4], bool norm, const float g1[4],
+                                               const float g2[4], float eps, f32x4 c01,
+                                               f32x4 c23) {
+  if (norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + c[e] * c[e];
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+    const float rs = 1.0f / sqrtf(ss / 128.0f + eps);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = a[e] * rs * g1[e];
+      c[e] = c[e] * rs * g2[e];
+    }
+  }
+  const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) rope_pair(a[e], c[e], float2{cs[2 * e], cs[2 * e + 1]});
+}
+
 constexpr int POST_HEADS = 4;  // heads per workgroup, one wave each
 // Rows per workgroup of the injection's head pass: per-row work is small, so
 // with many rows each wave takes its head in a few consecutive rows (fewer,
@@ -599,28 +625,12 @@ __global__ __launch_bounds__(256) void inject_k_wide_kernel(
       a[e] = x1[b][e];
       c[e] = x2[b][e];
     }
-    if (norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + c[e] * c[e];
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
-      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = a[e] * rs * g1[e];
-        c[e] = c[e] * rs * g2[e];
-      }
-    }
-    const float cs[8] = {c01[b][0], c01[b][1], c01[b][2], c01[b][3],
-                         c23[b][0], c23[b][1], c23[b][2], c23[b][3]};
+    wide_norm_rope(a, c, norm, g1, g2, eps, c01[b], c23[b]);
     T o1[4], o2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float y1 = a[e], y2 = c[e];
-      rope_pair(y1, y2, float2{cs[2 * e], cs[2 * e + 1]});
-      o1[e] = from_f32<T>(y1);
-      o2[e] = from_f32<T>(y2);
+      o1[e] = from_f32<T>(a[e]);
+      o2[e] = from_f32<T>(c[e]);
     }
     if (rr[b] >= n || sq[b] < 0 || sq[b] >= max_batch || ps[b] < 0 || ps[b] >= cap) continue;
     T *dst = kc + (((long)sq[b] * hkv + h) * cap + ps[b]) * DH + 4 * l;
