@@ -165,17 +165,17 @@ __global__ __launch_bounds__(256) void norm_apply_kernel(const float *__restrict
 // output in a single pass, with no scratch row.  Partial planes are summed in
 // split order, as in the two-pass form.
 constexpr int NORM_ROW_T = 1024;
-template <typename T, int CPT>
-__global__ __launch_bounds__(NORM_ROW_T) void norm_row_kernel(
+template <typename T, int CPT, int NT = NORM_ROW_T>
+__global__ __launch_bounds__(NT) void norm_row_kernel(
     const float *__restrict__ parts, int nsplit, int M, int d, float *resid, int write_resid,
     const T *__restrict__ gain, float eps, T *__restrict__ out, long out_stride) {
-  __shared__ float red[NORM_ROW_T / WAVE];
+  __shared__ float red[NT / WAVE];
   const int r = blockIdx.x;
   f32x4 x[CPT];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = (i * NORM_ROW_T + threadIdx.x) * 4;
+    const int c = (i * NT + threadIdx.x) * 4;
     x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < d) {
       if (resid) x[i] = *reinterpret_cast<const f32x4 *>(resid + (long)r * d + c);
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NORM_ROW_T) void norm_row_kernel(
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = (i * NORM_ROW_T + threadIdx.x) * 4;
+    const int c = (i * NT + threadIdx.x) * 4;
     if (c >= d) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -212,13 +212,19 @@ static bool launch_norm_row(const float *parts, int nsplit, int M, int d, float 
                             int write_resid, const void *gain, float eps, void *out,
                             long out_stride, hipStream_t st) {
   const int cpt = (d + 4 * NORM_ROW_T - 1) / (4 * NORM_ROW_T);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(M), dim3(NORM_ROW_T), 0, st, parts, nsplit, M, d, resid,
-                       write_resid, (const T *)gain, eps, (T *)out, out_stride);
+  auto go = [&](auto kern, int nt) {
+    hipLaunchKernelGGL(kern, dim3(M), dim3(nt), 0, st, parts, nsplit, M, d, resid, write_resid,
+                       (const T *)gain, eps, (T *)out, out_stride);
   };
-  if (cpt == 1) go(norm_row_kernel<T, 1>);
-  else if (cpt == 2) go(norm_row_kernel<T, 2>);
-  else if (cpt <= 4) go(norm_row_kernel<T, 4>);
+  // many rows (prefill chunks): 256 threads with 4x the columns each, so a
+  // compute unit keeps 4x the bytes in flight
+  if (M >= 2048 && d <= 4096) {
+    go(norm_row_kernel<T, 4, 256>, 256);
+    return true;
+  }
+  if (cpt == 1) go(norm_row_kernel<T, 1>, NORM_ROW_T);
+  else if (cpt == 2) go(norm_row_kernel<T, 2>, NORM_ROW_T);
+  else if (cpt <= 4) go(norm_row_kernel<T, 4>, NORM_ROW_T);
   else return false;
   return true;
 }
