@@ -745,40 +745,45 @@ __global__ __launch_bounds__(256) void inject_v_kernel(
   }
 }
 
+// The per-row head pass: K heads (norm + rotary), and V heads when with_v.
+template <typename T>
+static void launch_post_rows(const float *parts, int nsplit, int n, int hkv, int dh,
+                             const int32_t *seq, const int32_t *pos, const InjectLayers &il,
+                             int qk_norm, float eps, const float *rope, int max_batch, int cap,
+                             int with_v, hipStream_t st) {
+  const int rpw = post_rows(n);
+  const dim3 grid((n + rpw - 1) / rpw, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
+                  il.layers);
+  const float2 *cs = (const float2 *)rope;
+  if (rpw == 4)
+    hipLaunchKernelGGL((inject_post_kernel<T, 4>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                       nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+  else
+    hipLaunchKernelGGL((inject_post_kernel<T, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
+                       nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
+}
+
 void launch_inject_post(int dtype, const float *parts, int nsplit, int n, int hkv, int dh,
                         const int32_t *seq, const int32_t *pos, const InjectLayers &il,
                         int qk_norm, float eps, const float *rope, int max_batch, int cap,
                         hipStream_t st) {
   if (n == 0 || il.layers == 0) return;
-  // K heads: per-head norm + rotary embedding, one wave per (row, head).  V
-  // heads: with few rows the same per-row pass (enough workgroups), from
-  // INJ_V_MIN_ROWS rows the row-tiled transposing pass (contiguous stores)
+  // K heads: per-head norm + rotary embedding, one wave per (row, head), or
+  // (bf16, dh 128, from INJ_V_MIN_ROWS rows) the wide pass with 16 lanes per
+  // (row, head).  V heads: with few rows the same per-row pass (enough
+  // workgroups), from INJ_V_MIN_ROWS rows the row-tiled transposing pass
+  // (contiguous stores).
   const int with_v = n < INJ_V_MIN_ROWS;
-  const int rpw = post_rows(n);
   if (dtype == 1 && !with_v && dh == 128) {
-    // K heads on the wide pass (16-byte loads, 4 rows per wave at a time)
     const dim3 kgrid((n + KW_ROWS - 1) / KW_ROWS, hkv, il.layers);
     hipLaunchKernelGGL(inject_k_wide_kernel<bf16>, kgrid, dim3(256), 0, st, parts, nsplit, n, hkv,
                        seq, pos, il, qk_norm, eps, (const float2 *)rope, max_batch, cap);
+  } else if (dtype == 1) {
+    launch_post_rows<bf16>(parts, nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, rope, max_batch,
+                           cap, with_v, st);
   } else {
-  dim3 grid((n + rpw - 1) / rpw, ((with_v ? 2 : 1) * hkv + POST_HEADS - 1) / POST_HEADS,
-            il.layers);
-  const float2 *cs = (const float2 *)rope;
-  if (dtype == 1) {
-    if (rpw == 4)
-      hipLaunchKernelGGL((inject_post_kernel<bf16, 4>), grid, dim3(64 * POST_HEADS), 0, st, parts,
-                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
-    else
-      hipLaunchKernelGGL((inject_post_kernel<bf16, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
-                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
-  } else {
-    if (rpw == 4)
-      hipLaunchKernelGGL((inject_post_kernel<float, 4>), grid, dim3(64 * POST_HEADS), 0, st, parts,
-                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
-    else
-      hipLaunchKernelGGL((inject_post_kernel<float, 1>), grid, dim3(64 * POST_HEADS), 0, st, parts,
-                         nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, cs, max_batch, cap, with_v);
-  }
+    launch_post_rows<float>(parts, nsplit, n, hkv, dh, seq, pos, il, qk_norm, eps, rope,
+                            max_batch, cap, with_v, st);
   }
   if (with_v) return;
   // V heads: staged and written along rows
