@@ -117,6 +117,18 @@ struct TileEngine {
 #pragma unroll
       for (int i = 0; i < NCW; ++i) dma16(wb, woff[i], wl + i * 1024 * NWAVES);
     }
+    // Copy i (compile-time) of this wave for one stage.
+    __device__ __forceinline__ void issue_w_one(Smem &sm, int stage, int i) const {
+      const char *wb = wbase + (long)stage * KT * 2;
+      const uint32_t wl = lds_u32(&sm.w[stage % NSW][0]) + (threadIdx.x >> 6) * 1024;
+      dma16(wb, woff[i], wl + i * 1024 * NWAVES);
+    }
+    __device__ __forceinline__ void issue_x_one(Smem &sm, int stage, int i) const {
+      const char *xb = xbase + (long)stage * KT * 2;
+      const uint32_t xl = lds_u32(&sm.x[stage % NSX][0]) + (threadIdx.x >> 6) * 1024;
+      if (TX % NWAVES == 0 || NWAVES * i + (int)(threadIdx.x >> 6) < TX)
+        dma16(xb, xoff[i], xl + i * 1024 * NWAVES);
+    }
     __device__ __forceinline__ void issue_x(Smem &sm, int stage) const {
       const char *xb = xbase + (long)stage * KT * 2;
       const uint32_t xl = lds_u32(&sm.x[stage % NSX][0]) + (threadIdx.x >> 6) * 1024;
@@ -165,7 +177,18 @@ struct TileEngine {
     // k-step's products run, so the matrix pipe never waits for LDS after a
     // barrier.  Once every wave has read both k-steps of stage s, its
     // buffers are free: the barrier in the middle of stage s lets the copies
-    // of stage s + NSW (weight) and s + 2 (activations) refill them.
+    // of stage s + 2 (activations) and, for a two-deep weight ring, s + 2
+    // (weight) refill them; with a deeper weight ring the weight copies of
+    // stage s + NSW - 1 go into the buffer freed by the previous barrier,
+    // during the first half of stage s.
+    //
+    // Copies are spread between groups of products instead of being issued
+    // in one burst: a wave stalls on a vector-memory instruction the memory
+    // pipeline cannot take yet, and with every wave issuing all its copies
+    // after the same barrier the matrix pipe idles while the queue drains.
+    // Each half stage is cut into as many groups as it has copies (a copy,
+    // then its share of the fragment reads and of the products), fenced by
+    // scheduling barriers so the compiler keeps that order.
     bf16x8 fa[2][NW], fb[2][MW];
     auto read = [&](int s, int kk, int set) {
       const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
@@ -175,30 +198,53 @@ struct TileEngine {
 #pragma unroll
       for (int j = 0; j < MW; ++j) fb[set][j] = *reinterpret_cast<const bf16x8 *>(xs + boff[j][kk]);
     };
-    auto mma = [&](int set) {
-#pragma unroll
-      for (int i = 0; i < NW; ++i)
-#pragma unroll
-        for (int j = 0; j < MW; ++j) acc[i][j] = Mma<bf16>::run(fa[set][i], fb[set][j], acc[i][j]);
-    };
-    // interleave: the NW + MW reads with the NW * MW products they overlap
-    auto interleave = [&]() {
-      constexpr int NF = NW + MW, NP = NW * MW;
-      constexpr int RATIO = NP / NF > 0 ? NP / NF : 1;
-      constexpr int INTER = NF * RATIO <= NP ? NF : NP / RATIO;
-      static_for<INTER>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, RATIO, 0);
+    // Half stage: products of fragment set `set`; reads of the other set from
+    // stage rs, k-step rkk; copies copy(c) for c < NC.
+    auto half = [&](auto set_c, int rs, auto rkk_c, auto nc_c, auto copy) {
+      constexpr int set = decltype(set_c)::value, oset = set ^ 1, rkk = decltype(rkk_c)::value;
+      constexpr int NC = decltype(nc_c)::value, NG = NC > 0 ? NC : 1;
+      constexpr int NP = NW * MW, NF = NW + MW;
+      const char *ws = reinterpret_cast<const char *>(&sm.w[rs % NSW][0]);
+      const char *xs = reinterpret_cast<const char *>(&sm.x[rs % NSX][0]);
+      static_for<NG>([&](auto G) {
+        constexpr int q = decltype(G)::value;
+        constexpr int f0 = q * NF / NG, f1 = (q + 1) * NF / NG;
+        constexpr int p0 = q * NP / NG, p1 = (q + 1) * NP / NG;
+        if constexpr (NC > 0) copy(G);
+        static_for<f1 - f0>([&](auto F) {
+          constexpr int f = f0 + decltype(F)::value;
+          if constexpr (f < NW)
+            fa[oset][f] = *reinterpret_cast<const bf16x8 *>(ws + aoff[f][rkk]);
+          else
+            fb[oset][f - NW] = *reinterpret_cast<const bf16x8 *>(xs + boff[f - NW][rkk]);
+        });
+        static_for<p1 - p0>([&](auto P) {
+          constexpr int p = p0 + decltype(P)::value, i = p / MW, j = p % MW;
+          acc[i][j] = Mma<bf16>::run(fa[set][i], fb[set][j], acc[i][j]);
+        });
+        // reads and products alternate inside the group
+        constexpr int nf = f1 - f0, np = p1 - p0;
+        constexpr int ratio = nf > 0 && np / nf > 0 ? np / nf : 1;
+        constexpr int inter = nf * ratio <= np ? nf : np / ratio;
+        static_for<inter>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, ratio, 0);
+        });
+        if constexpr (nf > inter) __builtin_amdgcn_sched_group_barrier(0x100, nf - inter, 0);
+        if constexpr (np > inter * ratio)
+          __builtin_amdgcn_sched_group_barrier(0x008, np - inter * ratio, 0);
+        __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (NF > INTER) __builtin_amdgcn_sched_group_barrier(0x100, NF - INTER, 0);
-      if constexpr (NP > INTER * RATIO)
-        __builtin_amdgcn_sched_group_barrier(0x008, NP - INTER * RATIO, 0);
     };
-    // Issue order: W0, X0, W1 .. W(NSW - 2) before stage 0; after the
-    // barrier that publishes stage s (s >= 0): X(s + 1), W(s + NSW - 1).  The
-    // wait for stage s + 1 then leaves in flight only the copies issued
-    // after X(s + 1), i.e. W(s + NSW - 1) if it exists (W(s + 1) was issued
-    // before X(s + 1) for NSW >= 2).
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto no_copy = [&](auto) {};
+    // Issue order: W0, X0, W1 .. W(NSW - 2) before stage 0, then X1 (and W1
+    // for a two-deep weight ring) after the barrier that publishes stage 0.
+    // In stage s: W(s + NSW - 1) in the first half (NSW > 2); after the
+    // barrier that publishes stage s + 1, X(s + 2) (and W(s + 2) for NSW =
+    // 2).  The wait for stage s + 1 then leaves in flight only W(s + NSW - 1)
+    // if it exists (W(s + 1) was issued before X(s + 1) for NSW > 2).
     ld.issue_w(sm, 0);
     ld.issue_x(sm, 0);
 #pragma unroll
@@ -219,23 +265,38 @@ struct TileEngine {
     }
     __syncthreads();
     if (1 < nst) ld.issue_x(sm, 1);
-    if (NSW - 1 < nst) ld.issue_w(sm, NSW - 1);
+    if (NSW == 2 && 1 < nst) ld.issue_w(sm, 1);
     read(0, 0, 0);
     for (int s = 0; s < nst; ++s) {
-      read(s, 1, 1);
-      mma(0);
-      interleave();
+      // first half: products of k-step 0, reads of k-step 1, weight copies
+      if constexpr (NSW > 2) {
+        const int ws_ = s + NSW - 1;
+        const bool cw = ws_ < nst;
+        half(I0{}, s, I1{}, std::integral_constant<int, NCW>{}, [&](auto C) {
+          if (cw) ld.issue_w_one(sm, ws_, decltype(C)::value);
+        });
+      } else {
+        half(I0{}, s, I1{}, I0{}, no_copy);
+      }
       if (s + 1 < nst) {
         if (NSW > 2 && s + NSW - 1 < nst) wait_vmcnt<NCW>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (s + 2 < nst) ld.issue_x(sm, s + 2);
-        if (s + NSW < nst) ld.issue_w(sm, s + NSW);
       }
-      // (the last stage re-reads its own first k-step: unused, harmless)
-      read(min(s + 1, nst - 1), 0, 0);
-      mma(1);
-      interleave();
+      // second half: products of k-step 1, reads of stage s + 1's k-step 0
+      // (the last stage re-reads its own: unused, harmless), activation
+      // copies (and weight copies for a two-deep ring)
+      const bool cx = s + 2 < nst;
+      const int xs_ = s + 2;
+      half(I1{}, min(s + 1, nst - 1), I0{},
+           std::integral_constant<int, NCX + (NSW == 2 ? NCW : 0)>{}, [&](auto C) {
+             constexpr int c = decltype(C)::value;
+             if constexpr (c < NCX) {
+               if (cx) ld.issue_x_one(sm, xs_, c);
+             } else {
+               if (cx) ld.issue_w_one(sm, xs_, c - NCX);
+             }
+           });
     }
     __syncthreads();  // every wave is done with the rings: the caller may reuse them
   }
