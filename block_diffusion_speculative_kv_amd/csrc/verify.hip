@@ -125,6 +125,10 @@ __device__ __forceinline__ float ld(const float *p, long i) { return p[i]; }
 __device__ __forceinline__ float ld(const bf16 *p, long i) { return static_cast<float>(p[i]); }
 
 // ---- per-row statistics --------------------------------------------------
+// Headroom of the lazy softmax reference in the row pass: terms are at most
+// e^16, so a split's sums stay far inside fp32 (per group) and fp64 range.
+constexpr float VROW_LAZY = 16.f;
+
 template <typename TT>
 __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
   __shared__ VRowPart red[4];
@@ -154,9 +158,10 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
   };
   if ((V & 7) == 0) {
     // 8 consecutive ids per thread per step (v0 and v1 are multiples of 8):
-    // the running max moves once per group (one fp64 rescale), the 8 terms
-    // exp(y - m) <= 1 are summed in fp32 with the hardware exp2 and folded
-    // into the fp64 sum once
+    // the softmax reference moves at most once per group (one fp64
+    // rescale, and only past the lazy headroom), the 8 terms exp(y - m) <=
+    // e^VROW_LAZY are summed in fp32 with the hardware exp2 and folded into
+    // the fp64 sum once
     // U groups per thread are loaded before any is reduced (more loads in
     // flight); each thread still takes its groups in increasing order.  One
     // top-2 per group position (8 independent chains instead of one); the
@@ -183,7 +188,12 @@ __global__ __launch_bounds__(256) void vrow_kernel(VerifyArgs a, VerifyWs w) {
         y[e] = x[e] * invT;
         gm = fmaxf(gm, y[e]);
       }
-      if (gm > m) {
+      // Lazy reference: s holds sum exp(y - m) for a reference m that is
+      // moved (with an fp64 rescale) only when a group's maximum exceeds it
+      // by more than VROW_LAZY, so every term stays at most e^VROW_LAZY.
+      // Moving it at every new maximum would run the fp64 exponential for
+      // nearly every group of a wave (some lane almost always sees one).
+      if (gm > m + VROW_LAZY) {
         s = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)gm);
         m = gm;
       }
@@ -432,93 +442,97 @@ __global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, Verif
   const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
                    (bonus || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
   constexpr int WIN = 8 * VS_GPT * VS_THREADS;  // ids per window
-  for (int wb = v0; wb < v1; wb += WIN) {
-    double lpv[VS_GPT][8];
-    float gv[VS_GPT][8], xdv[VS_GPT][8];
-    double ub = -INFINITY;  // this thread's largest lp + g in the window
+  // z / T in fp64; at T = 1 the division is exact and skipped (the walk is
+  // instantiated once per case, so the choice is not made per element)
+  auto walk = [&](auto unit_c) {
+    constexpr bool unit = decltype(unit_c)::value;
+    auto over_t = [&](double z) { return unit ? z : z / T; };
+    for (int wb = v0; wb < v1; wb += WIN) {
+      // per id only its bound lp + g, rounded to fp32 (-inf: no id); the
+      // candidates' exact values are recomputed from the logits and the
+      // noise stream, so the window costs 24 registers, not 96
+      float uf[VS_GPT][8];
+      double ub = -INFINITY;  // this thread's largest lp + g in the window
 #pragma unroll
-    for (int gi = 0; gi < VS_GPT; ++gi) {
-      const int vb = wb + 8 * (threadIdx.x + gi * VS_THREADS);
-      // the 8 target and draft logits are loaded before the noise is drawn,
-      // as vectors where the row allows
-      float xt[8], xd[8];
-      if (vec && vb + 8 <= v1) {
-        ld8(zt + vb, xt);
-        if (!bonus) ld8(zd + vb, xd);
-      } else {
+      for (int gi = 0; gi < VS_GPT; ++gi) {
+        const int vb = wb + 8 * (threadIdx.x + gi * VS_THREADS);
+        // the 8 target and draft logits are loaded before the noise is drawn,
+        // as vectors where the row allows
+        float xt[8], xd[8];
+        if (vec && vb + 8 <= v1) {
+          ld8(zt + vb, xt);
+          if (!bonus) ld8(zd + vb, xd);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xt[e] = vb + e < v1 ? ld(zt, vb + e) : 0.f;
+            xd[e] = !bonus && vb + e < v1 ? zd[vb + e] : 0.f;
+          }
+        }
+        uint32_t raw[8];
+        if (vb < v1)
+          philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xt[e] = vb + e < v1 ? ld(zt, vb + e) : 0.f;
-          xd[e] = !bonus && vb + e < v1 ? zd[vb + e] : 0.f;
+          const int v = vb + e;
+          uf[gi][e] = -INFINITY;
+          if (v >= v1) continue;
+          const double lp = over_t((double)xt[e]) - lse_t;
+          const double u = lp + (double)gumbel_of(raw[e]);
+          if (lp > -INFINITY) uf[gi][e] = (float)u;
+          d2_push(pp, u, v);
+          ub = fmax(ub, u);
+          if (!bonus && !isfinite((double)xd[e])) bad = 1;
         }
       }
-      uint32_t raw[8];
-      if (vb < v1)
-        philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = vb + e;
-        lpv[gi][e] = -INFINITY;
-        gv[gi][e] = 0.f;
-        xdv[gi][e] = xd[e];
-        if (v >= v1) continue;
-        const float g = gumbel_of(raw[e]);
-        const double lp = (double)xt[e] / T - lse_t;
-        lpv[gi][e] = lp;
-        gv[gi][e] = g;
-        d2_push(pp, lp + (double)g, v);
-        ub = fmax(ub, lp + (double)g);
-        if (!bonus && !isfinite((double)xd[e])) bad = 1;
-      }
-    }
-    if (bonus) continue;
-    const double U = block_max_d(ub, shd);
-    if (U == -INFINITY) continue;  // nothing finite in this window
-    // thresholds, highest first; ids in [t, t_prev) are evaluated in a round
-    double tprev = INFINITY;
+      if (bonus) continue;
+      const double U = block_max_d(ub, shd);
+      if (U == -INFINITY) continue;  // nothing finite in this window
+      // thresholds, highest first; an id is evaluated in the first round
+      // whose threshold its bound reaches (done: already evaluated)
+      uint32_t done = 0;
 #pragma unroll 1
-    for (int round = 0; round < 3; ++round) {
-      const double t = round == 0 ? U - 4.0 : round == 1 ? U - 16.0 : -INFINITY;
-      // candidates of this round as a bit mask over the thread's ids, then
-      // one fp64 evaluation per candidate (the values picked by a select
-      // chain, so the evaluation code exists once)
-      uint32_t cand = 0;
-#pragma unroll
-      for (int gi = 0; gi < VS_GPT; ++gi)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double u = lpv[gi][e] + (double)gv[gi][e];
-          // (a margin above the exact bound: log(exp(lp)) may round above lp)
-          if (lpv[gi][e] > -INFINITY && u + 1e-9 >= t && u + 1e-9 < tprev)
-            cand |= 1u << (8 * gi + e);
-        }
-      while (cand) {
-        const int i = __builtin_ctz(cand);
-        cand &= cand - 1;
-        double lp = 0.0;
-        float g = 0.f, xdf = 0.f;
+      for (int round = 0; round < 3; ++round) {
+        const double t = round == 0 ? U - 4.0 : round == 1 ? U - 16.0 : -INFINITY;
+        // the fp32 bound is within |u| 2^-24 of lp + g, and log(exp(lp)) may
+        // round above lp: a slack of 1e-6 absolute plus 1e-6 relative keeps
+        // every id whose exact bound reaches t
+        const float tf = round == 2 ? -INFINITY : (float)(t - 1e-6 - fabs(t) * 1e-6);
+        uint32_t cand = 0;
 #pragma unroll
         for (int gi = 0; gi < VS_GPT; ++gi)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (i == 8 * gi + e) {
-              lp = lpv[gi][e];
-              g = gv[gi][e];
-              xdf = xdv[gi][e];
-            }
-        const int v = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS) + (i & 7);
-        const double zdv = (double)xdf;
-        const double r = exp(lp) - exp(zdv / T - lse_d);
-        if (r > 0.0) {
-          any_r = 1;
-          d2_push(rr, log(r) + (double)g, v);
+            if (uf[gi][e] > -INFINITY && uf[gi][e] >= tf) cand |= 1u << (8 * gi + e);
+        cand &= ~done;
+        done |= cand;
+        // one fp64 evaluation per candidate, its logits reloaded and its
+        // noise redrawn (the same expressions as above: the same values)
+        while (cand) {
+          const int i = __builtin_ctz(cand);
+          cand &= cand - 1;
+          const int vb = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS), e = i & 7;
+          const int v = vb + e;
+          uint32_t raw[8];
+          philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
+          uint32_t re = raw[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) re = e == k ? raw[k] : re;
+          const double lp = over_t((double)ld(zt, v)) - lse_t;
+          const double zdv = (double)zd[v];
+          const double r = exp(lp) - exp(over_t(zdv) - lse_d);
+          if (r > 0.0) {
+            any_r = 1;
+            d2_push(rr, log(r) + (double)gumbel_of(re), v);
+          }
         }
+        const double best = block_max_d(rr.best, shd);
+        if (best >= t + (double)NEAR_BAND + 1e-9) break;
       }
-      tprev = t;
-      const double best = block_max_d(rr.best, shd);
-      if (best >= t + (double)NEAR_BAND + 1e-9) break;
     }
-  }
+  };
+  if (T == 1.0) walk(std::true_type{});
+  else walk(std::false_type{});
   for (int o = 32; o > 0; o >>= 1) {
     D2 x{__shfl_xor(rr.best, o, WAVE), __shfl_xor(rr.second, o, WAVE), __shfl_xor(rr.idx, o, WAVE)};
     rr = d2_merge(rr, x);
