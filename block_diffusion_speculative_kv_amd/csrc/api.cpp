@@ -318,10 +318,11 @@ int dstill_workspace_bytes(const dstill_handle *h, const dstill_limits *lim, siz
       for (int b2 = 1; b2 < B; ++b2)
         best = std::max(best, draft_ws(c, bs, C, b2, bound, ncu, nullptr, nullptr));
     }
-  for (int n = 1; n <= lim->max_inject_rows; n += (n < 4096 ? 1 : 64))
+  // every row count: a product's k-split plan can move either way with the
+  // row count, so skipping any could under-report (each size costs a few
+  // split-plan evaluations: ~50 ms of host time at 65536 rows)
+  for (int n = 1; n <= lim->max_inject_rows; ++n)
     best = std::max(best, inject_ws(c, n, ncu, nullptr, nullptr));
-  if (lim->max_inject_rows > 0)
-    best = std::max(best, inject_ws(c, lim->max_inject_rows, ncu, nullptr, nullptr));
   best = std::max(best, head_ws(c, lim->max_head_rows));
   *bytes = best;
   return DSTILL_OK;
