@@ -58,11 +58,13 @@ struct RowStat {
   float zbest, zmax, m, s;
 };
 
+// Branch-free: a side with m = -inf (no ids) has s = 0 and weight 0, the
+// other keeps its s exactly (expf(0) = 1), as a branch on -inf would.
 __device__ __forceinline__ void ms_merge(float &m, float &s, float m2, float s2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) { m = m2; s = s2; return; }
   const float M = fmaxf(m, m2);
-  s = s * expf(m - M) + s2 * expf(m2 - M);
+  const float w1 = m == -INFINITY ? 0.f : expf(m - M);
+  const float w2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
+  s = s * w1 + s2 * w2;
   m = M;
 }
 
@@ -102,6 +104,7 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
   const bool gumbel = a.mode != 0;
   const bool rvalid = r < a.rows;
   const int seq = r / a.rows_per_seq, slot = r % a.rows_per_seq;
+  const bool full = vw + 32 * NP <= V;  // wave-uniform: vw is the wave's first id
   RowStat st;
   st.arg.best = -INFINITY;
   st.arg.second = -INFINITY;
@@ -130,18 +133,25 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
 #pragma unroll
       for (int e = 0; e < 8; ++e) gn[e] = 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    // (full: every id of the wave's band lies in the vocabulary, the common
+    // case, taken by the whole wave without per-id guards)
+    auto push = [&](int e) {
       const int v = v0 + e;
-      if (v < V) {
-        const float z = zz[p][e];
-        const float sc = gumbel ? z * invT + gn[e] : z;
-        const bool win = sc > st.arg.best || (sc == st.arg.best && v < st.arg.idx);
-        if (win) st.zbest = z;
-        top2_push(st.arg, sc, v);
-        st.zmax = fmaxf(st.zmax, z);
-        st.m = fmaxf(st.m, z * invT);
-      }
+      const float z = zz[p][e];
+      const float sc = gumbel ? z * invT + gn[e] : z;
+      const bool win = sc > st.arg.best || (sc == st.arg.best && v < st.arg.idx);
+      st.zbest = win ? z : st.zbest;
+      top2_push(st.arg, sc, v);
+      st.zmax = fmaxf(st.zmax, z);
+      st.m = fmaxf(st.m, z * invT);
+    };
+    if (full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) push(e);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v0 + e < V) push(e);
     }
     if (STORE && a.logits && rvalid) {
       float *lp = a.logits + (long)r * V + v0;
@@ -150,7 +160,13 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
         if (v0 + e < V) lp[e] = zz[p][e];
     }
   }
-  if (st.m != -INFINITY) {
+  if (full && st.m != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        st.s += __builtin_amdgcn_exp2f((zz[p][e] * invT - st.m) * 1.4426950408889634f);
+  } else if (st.m != -INFINITY) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
