@@ -143,7 +143,6 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
       st.zbest = win ? z : st.zbest;
       top2_push(st.arg, sc, v);
       st.zmax = fmaxf(st.zmax, z);
-      st.m = fmaxf(st.m, z * invT);
     };
     if (full) {
 #pragma unroll
@@ -160,19 +159,24 @@ __device__ __forceinline__ RowStat lane_rowstat(const HeadArgs &a, int r, int vw
         if (v0 + e < V) lp[e] = zz[p][e];
     }
   }
+  // the largest z / T is the largest z times 1 / T (T > 0; rounding is
+  // monotone, so this is exactly the maximum of the rounded products)
+  st.m = st.zmax * invT;
+  // exp(z / T - m) = exp2(z (log2 e / T) - m log2 e), one FMA per term
+  const float kz = invT * 1.4426950408889634f, km = st.m * 1.4426950408889634f;
   if (full && st.m != -INFINITY) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        st.s += __builtin_amdgcn_exp2f((zz[p][e] * invT - st.m) * 1.4426950408889634f);
+        st.s += __builtin_amdgcn_exp2f(fmaf(zz[p][e], kz, -km));
   } else if (st.m != -INFINITY) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (vw + 32 * p + 8 * g + e < V)
-          st.s += __builtin_amdgcn_exp2f((zz[p][e] * invT - st.m) * 1.4426950408889634f);
+          st.s += __builtin_amdgcn_exp2f(fmaf(zz[p][e], kz, -km));
   }
   st = rowstat_shfl_xor(st, 16);
   st = rowstat_shfl_xor(st, 32);
