@@ -182,13 +182,13 @@ struct TileEngine {
     // stage s + NSW - 1 go into the buffer freed by the previous barrier,
     // during the first half of stage s.
     //
-    // Copies are spread between groups of products instead of being issued
-    // in one burst: a wave stalls on a vector-memory instruction the memory
-    // pipeline cannot take yet, and with every wave issuing all its copies
-    // after the same barrier the matrix pipe idles while the queue drains.
-    // Each half stage is cut into as many groups as it has copies (a copy,
-    // then its share of the fragment reads and of the products), fenced by
-    // scheduling barriers so the compiler keeps that order.
+    // Copies are spread between groups of products rather than issued in one
+    // burst after the barrier, so no wave holds its products back behind a
+    // run of copy instructions (faster on the short per-cycle products, no
+    // slower on the long ones).  Each half stage is cut into as many groups
+    // as it has copies (a copy, then its share of the fragment reads and of
+    // the products), fenced by scheduling barriers so the compiler keeps that
+    // order.
     bf16x8 fa[2][NW], fb[2][MW];
     auto read = [&](int s, int kk, int set) {
       const char *ws = reinterpret_cast<const char *>(&sm.w[s % NSW][0]);
