@@ -46,7 +46,6 @@ constexpr int HEAD_KT = 64;   // LDS path: k per stage
 // copies half the bytes into LDS per product term.
 template <int NW, int MW>
 using HeadTile = TileEngine<2, 2, NW, MW, HEAD_KT, 3, 2>;
-using HeadMidTile = TileEngine<2, 2, 4, 5, HEAD_KT, 2, 2>;
 using HeadBigTile = TileEngine<2, 4, 8, 4, HEAD_KT, 3, 2>;
 constexpr int NXCD = 8;
 
@@ -699,14 +698,15 @@ static void launch_head_tile(const HeadArgs &a, dim3 grid, int nmb, hipStream_t 
 void launch_lm_head(const HeadArgs &args, hipStream_t st) {
   if (args.rows == 0) return;
   HeadArgs a = args;
-  // up to 160 rows stream the weight through an LDS ring; more rows (and
-  // depths the streaming stages do not divide) go through the tile engine,
-  // with a tile fitted to the row count (both address a block's hidden rows
-  // with 32-bit byte offsets)
-  int BN = HeadMidTile::BN, BM = HeadMidTile::BM;
+  // up to 160 rows stream the weight through an LDS ring; more rows (and,
+  // up to 64 rows, depths the 128-deep streaming stages do not divide) go
+  // through the tile engine, with a tile fitted to the row count (both
+  // address a block's hidden rows with 32-bit byte offsets).  From 65 to 160
+  // rows the streaming conditions hold whenever the tile's do (64-deep
+  // stages, a span no larger than the tile's), so no tile serves them.
+  int BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   if (a.rows <= 32) BN = 64, BM = 32;
   else if (a.rows <= 64) BN = 64, BM = 64;
-  else if (a.rows > 160) BN = HeadBigTile::BN, BM = HeadBigTile::BM;
   const long span = ((long)(BM - 1) / a.rows_per_seq + 1) * a.seq_stride * a.d * 2;
   // streaming path: up to 160 rows, one row block of 16 RT rows (measured on
   // the 8B-shaped head: 30 rows 306 -> 248 us, 60 rows 298 -> 273 us against
@@ -729,7 +729,6 @@ void launch_lm_head(const HeadArgs &args, hipStream_t st) {
     const dim3 grid((a.nvb + NXCD - 1) / NXCD * NXCD * nmb);
     if (BM == 32) launch_head_tile<HeadTile<2, 1>>(a, grid, nmb, st);
     else if (BM == 64) launch_head_tile<HeadTile<2, 2>>(a, grid, nmb, st);
-    else if (BM == 160) launch_head_tile<HeadMidTile>(a, grid, nmb, st);
     else launch_head_tile<HeadBigTile>(a, grid, nmb, st);
   } else {
     a.nvb = (a.vocab + HEAD_VB - 1) / HEAD_VB;

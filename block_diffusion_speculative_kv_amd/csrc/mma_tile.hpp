@@ -71,8 +71,8 @@ struct TileEngine {
   static constexpr int TW = BN / RPI, TX = BM / RPI;
   static constexpr int NCW = TW / NWAVES, NCX = (TX + NWAVES - 1) / NWAVES;
   static_assert(KT == 64 || KT == 32, "stage depth");
-  static_assert(NSX == 2 && NSW >= 2 && NSW <= 8, "ring depths");
-  static_assert(NCW * (NSW > 2 ? NSW - 2 : 0) < 64, "vmcnt holds the copies left in flight");
+  static_assert(NSX == 2 && NSW >= 3 && NSW <= 8, "ring depths");
+  static_assert(NCW * (NSW - 2) < 64, "vmcnt holds the copies left in flight");
   static_assert(TW * RPI == BN && TX * RPI == BM && NCW * NWAVES == TW, "whole copies");
 
   struct Smem {
@@ -177,8 +177,7 @@ struct TileEngine {
     // k-step's products run, so the matrix pipe never waits for LDS after a
     // barrier.  Once every wave has read both k-steps of stage s, its
     // buffers are free: the barrier in the middle of stage s lets the copies
-    // of stage s + 2 (activations) and, for a two-deep weight ring, s + 2
-    // (weight) refill them; with a deeper weight ring the weight copies of
+    // of stage s + 2 (activations) refill them, and the weight copies of
     // stage s + NSW - 1 go into the buffer freed by the previous barrier,
     // during the first half of stage s.
     //
@@ -238,20 +237,18 @@ struct TileEngine {
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    auto no_copy = [&](auto) {};
-    // Issue order: W0, X0, W1 .. W(NSW - 2) before stage 0, then X1 (and W1
-    // for a two-deep weight ring) after the barrier that publishes stage 0.
-    // In stage s: W(s + NSW - 1) in the first half (NSW > 2); after the
-    // barrier that publishes stage s + 1, X(s + 2) (and W(s + 2) for NSW =
-    // 2).  The wait for stage s + 1 then leaves in flight only W(s + NSW - 1)
-    // if it exists (W(s + 1) was issued before X(s + 1) for NSW > 2).
+    // Issue order: W0, X0, W1 .. W(NSW - 2) before stage 0, then X1 after
+    // the barrier that publishes stage 0.  In stage s: W(s + NSW - 1) in the
+    // first half; after the barrier that publishes stage s + 1, X(s + 2).
+    // The wait for stage s + 1 then leaves in flight only W(s + NSW - 1) if
+    // it exists (W(s + 1) was issued before X(s + 1)).
     ld.issue_w(sm, 0);
     ld.issue_x(sm, 0);
 #pragma unroll
     for (int p = 1; p <= NSW - 2; ++p)
       if (p < nst) ld.issue_w(sm, p);
     {
-      const int later = NSW > 2 ? min(NSW - 2, nst - 1) : 0;
+      const int later = min(NSW - 2, nst - 1);
       if (later == 0) {
         wait_vmcnt<0>();
       } else if (later == 1) {
@@ -265,38 +262,29 @@ struct TileEngine {
     }
     __syncthreads();
     if (1 < nst) ld.issue_x(sm, 1);
-    if (NSW == 2 && 1 < nst) ld.issue_w(sm, 1);
     read(0, 0, 0);
     for (int s = 0; s < nst; ++s) {
       // first half: products of k-step 0, reads of k-step 1, weight copies
-      if constexpr (NSW > 2) {
+      {
         const int ws_ = s + NSW - 1;
         const bool cw = ws_ < nst;
         half(I0{}, s, I1{}, std::integral_constant<int, NCW>{}, [&](auto C) {
           if (cw) ld.issue_w_one(sm, ws_, decltype(C)::value);
         });
-      } else {
-        half(I0{}, s, I1{}, I0{}, no_copy);
       }
       if (s + 1 < nst) {
-        if (NSW > 2 && s + NSW - 1 < nst) wait_vmcnt<NCW>();
+        if (s + NSW - 1 < nst) wait_vmcnt<NCW>();
         else wait_vmcnt<0>();
         __syncthreads();
       }
       // second half: products of k-step 1, reads of stage s + 1's k-step 0
       // (the last stage re-reads its own: unused, harmless), activation
-      // copies (and weight copies for a two-deep ring)
+      // copies
       const bool cx = s + 2 < nst;
       const int xs_ = s + 2;
-      half(I1{}, min(s + 1, nst - 1), I0{},
-           std::integral_constant<int, NCX + (NSW == 2 ? NCW : 0)>{}, [&](auto C) {
-             constexpr int c = decltype(C)::value;
-             if constexpr (c < NCX) {
-               if (cx) ld.issue_x_one(sm, xs_, c);
-             } else {
-               if (cx) ld.issue_w_one(sm, xs_, c - NCX);
-             }
-           });
+      half(I1{}, min(s + 1, nst - 1), I0{}, std::integral_constant<int, NCX>{}, [&](auto C) {
+        if (cx) ld.issue_x_one(sm, xs_, decltype(C)::value);
+      });
     }
     __syncthreads();  // every wave is done with the rings: the caller may reuse them
   }
