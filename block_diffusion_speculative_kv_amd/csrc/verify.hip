@@ -292,6 +292,22 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
   __shared__ RowRes res[64];
   const int b = blockIdx.x, G = a.gamma, V = a.vocab;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  // Wave 0's per-slot inputs (lane k: the draft id, and for rejection
+  // sampling the target and draft logits at it and the draft's log-sum-exp)
+  // do not depend on the row merge: their loads are issued first.
+  const int k = lane;
+  int y = 0, yraw = 0;
+  double zt_y = 0.0, zd_y = 0.0;
+  float dl = 0.f;
+  if (wave == 0 && k < G) {
+    yraw = a.draft_ids[(long)b * G + k];
+    y = yraw < 0 ? 0 : (yraw >= V ? V - 1 : yraw);
+    if (a.mode != 0) {
+      zt_y = (double)ld((const TT *)a.target, ((long)b * (G + 1) + k) * V + y);
+      zd_y = (double)a.draft_logits[((long)b * G + k) * V + y];
+      dl = a.draft_lse[(long)b * G + k];
+    }
+  }
   // Row merge, one wave per target row, lanes over the row's vocabulary
   // splits: top-2 and flags by wave reduction, then the log-sum-exp as
   // M + log(sum_j s_j exp(m_j - M)) with M the largest split maximum.
@@ -330,7 +346,6 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
   }
   __syncthreads();
   if (wave != 0) return;
-  const int k = lane;
   const bool rowlane = k <= G;
   ArgTop2 arg{-INFINITY, -INFINITY, 0x7fffffff};
   int bad = 0;
@@ -340,12 +355,7 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
     bad = res[k].bad;
     lse = res[k].lse;
   }
-  int y = 0, yraw = 0;
-  if (k < G) {
-    yraw = a.draft_ids[(long)b * G + k];
-    y = yraw < 0 ? 0 : (yraw >= V ? V - 1 : yraw);
-    if (y != yraw) bad = 1;
-  }
+  if (k < G && y != yraw) bad = 1;
   uint32_t flags = 0;
   bool ok = false;  // slot k passes its test
   bool near = false;
@@ -353,20 +363,16 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
     ok = k < G && yraw == arg.idx;
     near = rowlane && (arg.best - arg.second) < NEAR_BAND;
   } else if (k < G) {
-    const long row = (long)b * (G + 1) + k;
-    const double zt = (double)ld((const TT *)a.target, row * V + y);
-    const double zd = (double)a.draft_logits[((long)b * G + k) * V + y];
     const double T = (double)a.temperature;
-    const double lp = zt / T - lse;
-    const float dl = a.draft_lse[(long)b * G + k];
-    const double lq = zd / T - (double)dl;
+    const double lp = zt_y / T - lse;
+    const double lq = zd_y / T - (double)dl;
     const double ratio = exp(lp - lq);
     uint32_t raw[8];
     philox_block8(a.seed, 1u, (uint64_t)b, (uint64_t)k, a.cycle, 0, raw);
     const double u = (double)u24(raw[0]);
     ok = u < ratio;
     near = fabs(ratio - u) < (double)NEAR_BAND;
-    if (!isfinite(zd) || !isfinite(dl)) bad = 1;
+    if (!isfinite(zd_y) || !isfinite(dl)) bad = 1;
   }
   // first failing slot (gamma if all pass)
   const unsigned long long fail = __ballot(k < G && !ok);
@@ -397,16 +403,20 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
 // Per (sequence, vocabulary split): the bonus / fallback draw argmax (lp + g)
 // over every id (lp = z_t / T - lse_t, g the Gumbel noise), and the residual
 // draw argmax (log max(0, p - q) + g).  Since max(0, p - q) <= p, the
-// residual score of an id is at most its lp + g, so the fp64 residual (two
-// exponentials and a logarithm) is evaluated only where it can matter: the
-// split is taken in windows of VS_GPT groups of 8 ids per thread, kept in
-// registers; with U the window's largest lp + g, the ids with lp + g >= U - 4
-// are evaluated first, then those down to U - 16, then all the rest, and the
-// walk stops as soon as the best residual score found lies a near-tie band
-// (plus a rounding margin) above the current threshold: no id left out can
-// then win, nor come within the band of the winner (which is all the
-// runner-up score is used for).  A block whose residual is empty (p <= q
-// everywhere) evaluates every id, as before.
+// residual score of an id is at most its bound lp + g.  The split is taken
+// in windows of VS_GPT groups of 8 ids per thread; a first pass draws every
+// id's noise and keeps, in registers, its fp32 bound and its fp32 noise
+// (exact: the noise is an fp32 value).  With U the window's largest bound,
+// ids are then evaluated exactly in fp64 (bound and, for a rejected row, the
+// residual: two exponentials and a logarithm) in rounds: those with bound
+// >= U - 4 first, then down to U - 16, then all the rest.  The first round
+// holds the largest lp + g and every id within the near-tie band of it, so
+// the bonus / fallback top-2 taken over the evaluated ids decides exactly
+// what the full one does (the runner-up is used only against the band).
+// The residual walk stops as soon as its best score lies the band (plus a
+// rounding margin) above the current threshold: no id left out can then
+// win, nor come within the band of the winner.  A block whose residual is
+// empty (p <= q everywhere) evaluates every id.
 constexpr int VS_GPT = 3;
 constexpr int VS_THREADS = 256;
 
@@ -442,17 +452,20 @@ __global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, Verif
   const bool vec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
                    (bonus || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
   constexpr int WIN = 8 * VS_GPT * VS_THREADS;  // ids per window
-  // z / T in fp64; at T = 1 the division is exact and skipped (the walk is
-  // instantiated once per case, so the choice is not made per element)
+  // The fp32 bound is formed from the fp32 logit and lse_t rounded to fp32
+  // while |lse_t| < 1e30 (then no z / T of the row can overflow fp32, as
+  // lse_t >= max z / T), else from the fp64 lp; either way it lies within
+  // 2^-21 (|z / T| + |lse_t| + |g| + |bound|) of the exact lp + g.
+  const bool f32b = fabs(lse_t) < 1e30;
+  const float lse_f = (float)lse_t, invT_f = (float)(1.0 / T);
+  // exact values: z / T in fp64; at T = 1 the division is exact and skipped
+  // (the walk is instantiated once per case, not chosen per element)
   auto walk = [&](auto unit_c) {
     constexpr bool unit = decltype(unit_c)::value;
     auto over_t = [&](double z) { return unit ? z : z / T; };
     for (int wb = v0; wb < v1; wb += WIN) {
-      // per id only its bound lp + g, rounded to fp32 (-inf: no id); the
-      // candidates' exact values are recomputed from the logits and the
-      // noise stream, so the window costs 24 registers, not 96
-      float uf[VS_GPT][8];
-      double ub = -INFINITY;  // this thread's largest lp + g in the window
+      float uf[VS_GPT][8], gf[VS_GPT][8];
+      float ub = -INFINITY;  // this thread's largest bound in the window
 #pragma unroll
       for (int gi = 0; gi < VS_GPT; ++gi) {
         const int vb = wb + 8 * (threadIdx.x + gi * VS_THREADS);
@@ -476,28 +489,30 @@ __global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, Verif
         for (int e = 0; e < 8; ++e) {
           const int v = vb + e;
           uf[gi][e] = -INFINITY;
+          gf[gi][e] = 0.f;
           if (v >= v1) continue;
-          const double lp = over_t((double)xt[e]) - lse_t;
-          const double u = lp + (double)gumbel_of(raw[e]);
-          if (lp > -INFINITY) uf[gi][e] = (float)u;
-          d2_push(pp, u, v);
-          ub = fmax(ub, u);
-          if (!bonus && !isfinite((double)xd[e])) bad = 1;
+          const float g = gumbel_of(raw[e]);
+          float bnd;
+          if (f32b) bnd = (unit ? xt[e] - lse_f : fmaf(xt[e], invT_f, -lse_f)) + g;
+          else bnd = (float)(over_t((double)xt[e]) - lse_t + (double)g);
+          uf[gi][e] = bnd;  // -inf where z = -inf; NaN is never a candidate
+          gf[gi][e] = g;
+          ub = fmaxf(ub, bnd);
+          if (!bonus && !isfinite(xd[e])) bad = 1;
         }
       }
-      if (bonus) continue;
-      const double U = block_max_d(ub, shd);
+      const double U = block_max_d((double)ub, shd);
       if (U == -INFINITY) continue;  // nothing finite in this window
+      // covers the fp32 bound's error (above) with a wide margin for every
+      // id whose bound is within 16 + |g| of U, and the rounding of tf
+      const double slack = 1e-4 + 1e-5 * (fabs(U) + fabs(lse_t));
       // thresholds, highest first; an id is evaluated in the first round
       // whose threshold its bound reaches (done: already evaluated)
       uint32_t done = 0;
 #pragma unroll 1
       for (int round = 0; round < 3; ++round) {
         const double t = round == 0 ? U - 4.0 : round == 1 ? U - 16.0 : -INFINITY;
-        // the fp32 bound is within |u| 2^-24 of lp + g, and log(exp(lp)) may
-        // round above lp: a slack of 1e-6 absolute plus 1e-6 relative keeps
-        // every id whose exact bound reaches t
-        const float tf = round == 2 ? -INFINITY : (float)(t - 1e-6 - fabs(t) * 1e-6);
+        const float tf = round == 2 ? -INFINITY : (float)(t - slack);
         uint32_t cand = 0;
 #pragma unroll
         for (int gi = 0; gi < VS_GPT; ++gi)
@@ -507,25 +522,26 @@ __global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, Verif
         cand &= ~done;
         done |= cand;
         // one fp64 evaluation per candidate, its logits reloaded and its
-        // noise redrawn (the same expressions as above: the same values)
+        // noise taken from the window's registers
         while (cand) {
           const int i = __builtin_ctz(cand);
           cand &= cand - 1;
-          const int vb = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS), e = i & 7;
-          const int v = vb + e;
-          uint32_t raw[8];
-          philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)(vb >> 3), raw);
-          uint32_t re = raw[0];
+          const int v = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS) + (i & 7);
+          float gs = 0.f;
 #pragma unroll
-          for (int k = 1; k < 8; ++k) re = e == k ? raw[k] : re;
+          for (int j = 0; j < VS_GPT * 8; ++j) gs = i == j ? gf[j >> 3][j & 7] : gs;
+          const double g = (double)gs;
           const double lp = over_t((double)ld(zt, v)) - lse_t;
-          const double zdv = (double)zd[v];
-          const double r = exp(lp) - exp(over_t(zdv) - lse_d);
-          if (r > 0.0) {
-            any_r = 1;
-            d2_push(rr, log(r) + (double)gumbel_of(re), v);
+          d2_push(pp, lp + g, v);
+          if (!bonus) {
+            const double r = exp(lp) - exp(over_t((double)zd[v]) - lse_d);
+            if (r > 0.0) {
+              any_r = 1;
+              d2_push(rr, log(r) + g, v);
+            }
           }
         }
+        if (bonus) break;  // the first round decides the bonus draw
         const double best = block_max_d(rr.best, shd);
         if (best >= t + (double)NEAR_BAND + 1e-9) break;
       }
