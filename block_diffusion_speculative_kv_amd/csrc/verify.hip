@@ -405,12 +405,12 @@ __global__ __launch_bounds__(1024) void vdecide_kernel(VerifyArgs a, VerifyWs w)
 // draw argmax (log max(0, p - q) + g).  Since max(0, p - q) <= p, the
 // residual score of an id is at most its bound lp + g.  The split is taken
 // in windows of VS_GPT groups of 8 ids per thread; a first pass draws every
-// id's noise and keeps only its fp32 bound in registers.  With U the
-// window's largest bound, ids are then evaluated exactly in fp64 (bound and,
-// for a rejected row, the residual: two exponentials and a logarithm) in
-// rounds: those with bound >= U - 4 first, then down to U - 16, then all the
-// rest.  The first round holds the largest lp + g and every id within the
-// near-tie band of it, so
+// id's noise and keeps, in registers, its fp32 bound and its fp32 noise
+// (exact: the noise is an fp32 value).  With U the window's largest bound,
+// ids are then evaluated exactly in fp64 (bound and, for a rejected row, the
+// residual: two exponentials and a logarithm) in rounds: those with bound
+// >= U - 4 first, then down to U - 16, then all the rest.  The first round
+// holds the largest lp + g and every id within the near-tie band of it, so
 // the bonus / fallback top-2 taken over the evaluated ids decides exactly
 // what the full one does (the runner-up is used only against the band).
 // The residual walk stops as soon as its best score lies the band (plus a
@@ -431,7 +431,7 @@ __device__ __forceinline__ double block_max_d(double v, double *sh) {
 }
 
 template <typename TT>
-__global__ __launch_bounds__(VS_THREADS, 4) void vsample_kernel(VerifyArgs a, VerifyWs w) {
+__global__ __launch_bounds__(VS_THREADS) void vsample_kernel(VerifyArgs a, VerifyWs w) {
   __shared__ VSampPart red[VS_THREADS / 64];
   __shared__ double shd[VS_THREADS / 64];
   const int b = blockIdx.x, sp = blockIdx.y;
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(VS_THREADS, 4) void vsample_kernel(VerifyArgs a, Ve
     constexpr bool unit = decltype(unit_c)::value;
     auto over_t = [&](double z) { return unit ? z : z / T; };
     for (int wb = v0; wb < v1; wb += WIN) {
-      float uf[VS_GPT][8];
+      float uf[VS_GPT][8], gf[VS_GPT][8];
       float ub = -INFINITY;  // this thread's largest bound in the window
 #pragma unroll
       for (int gi = 0; gi < VS_GPT; ++gi) {
@@ -489,12 +489,14 @@ __global__ __launch_bounds__(VS_THREADS, 4) void vsample_kernel(VerifyArgs a, Ve
         for (int e = 0; e < 8; ++e) {
           const int v = vb + e;
           uf[gi][e] = -INFINITY;
+          gf[gi][e] = 0.f;
           if (v >= v1) continue;
           const float g = gumbel_of(raw[e]);
           float bnd;
           if (f32b) bnd = (unit ? xt[e] - lse_f : fmaf(xt[e], invT_f, -lse_f)) + g;
           else bnd = (float)(over_t((double)xt[e]) - lse_t + (double)g);
           uf[gi][e] = bnd;  // -inf where z = -inf; NaN is never a candidate
+          gf[gi][e] = g;
           ub = fmaxf(ub, bnd);
           if (!bonus && !isfinite(xd[e])) bad = 1;
         }
@@ -520,20 +522,15 @@ __global__ __launch_bounds__(VS_THREADS, 4) void vsample_kernel(VerifyArgs a, Ve
         cand &= ~done;
         done |= cand;
         // one fp64 evaluation per candidate, its logits reloaded and its
-        // noise redrawn (the same stream element: the same fp32 value); at
-        // 128 VGPRs the ~1024 workgroups the split plan aims for run in one
-        // round of four per compute unit, which gains more than keeping each
-        // id's noise in registers would
+        // noise taken from the window's registers
         while (cand) {
           const int i = __builtin_ctz(cand);
           cand &= cand - 1;
           const int v = wb + 8 * (threadIdx.x + (i >> 3) * VS_THREADS) + (i & 7);
-          uint32_t rw[8];
-          philox_block8(a.seed, 2u, (uint64_t)b, (uint64_t)ks, a.cycle, (uint64_t)((v & ~7) >> 3), rw);
-          uint32_t re = rw[0];
+          float gs = 0.f;
 #pragma unroll
-          for (int k = 1; k < 8; ++k) re = (i & 7) == k ? rw[k] : re;
-          const double g = (double)gumbel_of(re);
+          for (int j = 0; j < VS_GPT * 8; ++j) gs = i == j ? gf[j >> 3][j & 7] : gs;
+          const double g = (double)gs;
           const double lp = over_t((double)ld(zt, v)) - lse_t;
           d2_push(pp, lp + g, v);
           if (!bonus) {
