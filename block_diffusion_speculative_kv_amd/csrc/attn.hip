@@ -735,6 +735,76 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e] * inv);
 }
 
+// The same merge for plans of more than 8 splits, in the same split order:
+// the row's threads first load the (m, l) of different splits at once and
+// take M by shuffles, the weights go through LDS, and the O vectors are then
+// loaded 16 splits at a time: three dependent rounds of loads at 32 splits
+// instead of eight.  (Up to 8 splits the kernel above needs two rounds and
+// no barrier.)
+constexpr int ATT_MAX_SPLITS = 128;  // the split plan's cap
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_wide_kernel(AttnArgs a) {
+  constexpr int MAXR = 128 / 16;  // rows per workgroup at dh = 64
+  __shared__ float sw[MAXR][ATT_MAX_SPLITS], sl[MAXR][ATT_MAX_SPLITS];
+  const int bc = blockIdx.x, head = blockIdx.y;
+  const int dh = a.dh, per_row = dh / 4, rows_per_wg = 128 / per_row;
+  const int rw = threadIdx.x / per_row, j = threadIdx.x % per_row;
+  const int s = blockIdx.z * rows_per_wg + rw;
+  const int d = j * 4;
+  const bool live = s < a.B;
+  const int b = bc / a.C;
+  const int S = a.eff_ctx[b] - ctx_lo(a.eff_ctx[b], a.window);  // keys from the first split
+  const int nvalid = max(1, (S + a.split - 1) / a.split);
+  const long rec0 = ((long)bc * a.hq + head) * a.nsplit * a.B + (live ? s : 0);  // + sp*B
+  // lane j of a row takes splits j, j + per_row, ... (per_row >= 16 lanes)
+  constexpr int SPL = ATT_MAX_SPLITS / 16;
+  float mv[SPL], lv[SPL];
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int sp = j + i * per_row;
+    const bool ok = live && sp < nvalid;
+    const long r = rec0 + (long)sp * a.B;
+    mv[i] = ok ? a.mlpart[r * 2] : -INFINITY;
+    lv[i] = ok ? a.mlpart[r * 2 + 1] : 0.f;
+    M = fmaxf(M, mv[i]);
+  }
+  // the row's lanes are an aligned group of per_row lanes of one wave
+  for (int o = per_row / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, WAVE));
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int sp = j + i * per_row;
+    if (live && sp < nvalid) {
+      sw[rw][sp] = exp2f(mv[i] - M);
+      sl[rw][sp] = lv[i];
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  constexpr int G = 16;
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < nvalid; sp0 += G) {
+    f32x4 ov[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      ov[i] = sp0 + i < nvalid
+                  ? *reinterpret_cast<const f32x4 *>(a.opart + (rec0 + (long)(sp0 + i) * a.B) * dh + d)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (sp0 + i >= nvalid) break;
+      const float w = sw[rw][sp0 + i];
+      L += w * sl[rw][sp0 + i];
+      o += w * ov[i];
+    }
+  }
+  const float inv = 1.0f / L;
+  T *dst = (T *)a.out + ((long)bc * a.B + s) * a.hq * dh + (long)head * dh + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[e] * inv);
+}
+
 template <typename T, int DH, int NTHR>
 static void launch_nthr(const AttnArgs &a, hipStream_t st) {
   const dim3 grid(a.nsplit * a.hkv * a.bs * a.C);
@@ -779,9 +849,9 @@ static void launch_typed(const AttnArgs &a, hipStream_t st) {
     else launch_nthr<T, DH, 1024>(a, st);
   }
   const int rows_per_wg = 128 / (a.dh / 4);
-  hipLaunchKernelGGL(attn_combine_kernel<T>,
-                     dim3(a.bs * a.C, a.hq, (a.B + rows_per_wg - 1) / rows_per_wg), dim3(128), 0,
-                     st, a);
+  const dim3 cgrid(a.bs * a.C, a.hq, (a.B + rows_per_wg - 1) / rows_per_wg);
+  if (a.nsplit > 8) hipLaunchKernelGGL(attn_combine_wide_kernel<T>, cgrid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(attn_combine_kernel<T>, cgrid, dim3(128), 0, st, a);
 }
 
 void launch_attention_worklist(const AttnArgs &a, int *list, hipStream_t st) {
